@@ -1,0 +1,254 @@
+"""Seeded input generators for paged and sparse MLA decode.
+
+Shapes follow the decode contract the pages describe: a query tensor
+``[batch, s_q, h_q, 576]`` in bf16, a paged latent cache of 64-token pages
+``[num_pages, 64, 1, 576]`` in bf16 addressed by a per-sequence
+``block_table`` and ``cache_seqlens`` ("Qu'est-ce que FlashMLA ?", section
+"Installation et utilisation de FlashMLA", steps 2-3; "DeepSeek, FlashMLA
+오픈소스 공개", summary: BF16, 64-token pages), and for the sparse variant an
+fp8-e4m3 cache with one scale per token plus a ``[batch, s_q, topk]`` index
+tensor where -1 marks an unused entry ("deepseek-ai/FlashMLA" project
+summary, section "기술적 세부 사항").
+
+Everything here is input preparation: random draws, page permutations, index
+lists, rounding drawn fp32 values to bf16 and quantising the sparse cache to
+fp8.  No attention arithmetic lives here.
+
+Draw order for one input set (one ``numpy.random.Generator(PCG64(seed))``):
+sequence lengths, block-table permutation, Q, KV, sparse indices, -1 mask.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence, Union
+
+import numpy as np
+
+D_QK = 576          # latent (512) + RoPE (64) dims of one cached row
+D_V = 512           # value dims: the first 512 dims of the same row
+PAGE = 64           # tokens per page
+REC_BYTES = 640     # sparse fp8 record: 576 e4m3 codes, fp32 scale, zero pad
+SCALE_OFF = 576     # byte offset of the fp32 scale inside a record
+BF16_NAN = 0x7FC0
+
+_KV_CHUNK_ROWS = 65536
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding (input preparation only)
+# --------------------------------------------------------------------------
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); return raw bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = (rounded >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bits to fp32 (exact)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) fp32 draws rounded to bf16 bits, drawn in row chunks of the leading dims."""
+    shape = tuple(int(s) for s in shape)
+    n_rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    width = shape[-1]
+    out = np.empty((n_rows, width), dtype=np.uint16)
+    for r0 in range(0, n_rows, _KV_CHUNK_ROWS):
+        r1 = min(n_rows, r0 + _KV_CHUNK_ROWS)
+        out[r0:r1] = bf16_bits_from_f32(rng.standard_normal((r1 - r0, width), dtype=np.float32))
+    return out.reshape(shape)
+
+
+# --------------------------------------------------------------------------
+# Paged inputs
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class PagedInputs:
+    q: np.ndarray               # uint16 bf16 bits [batch, s_q, h_q, 576]
+    kcache: np.ndarray          # uint16 bf16 bits [num_pages, 64, 1, 576]
+    block_table: np.ndarray     # int32 [batch, max_blocks]
+    seqlens: np.ndarray         # int32 [batch]
+    s_q: int
+    h_q: int
+    causal: bool
+    softmax_scale: float        # an fp32 value, stored as a Python float
+    poison_page: int            # index of the all-NaN page, or -1
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kcache.shape[0])
+
+
+def _fp32(x: float) -> float:
+    return float(np.float32(x))
+
+
+def make_paged(batch: int, s_q: int, h_q: int,
+               seqlens: Union[Sequence[int], tuple],
+               causal: bool, seed: int, poison: bool = True,
+               softmax_scale: Optional[float] = None) -> PagedInputs:
+    """Draw one paged decode input set.
+
+    ``seqlens`` is either an explicit list of ``batch`` lengths or
+    ``("uniform", lo, hi)`` for integer lengths drawn uniformly in [lo, hi].
+    The page pool is the exact fit sum(ceil(L/64)); its pages are handed out
+    in a random permutation, in order per sequence.  With ``poison`` an extra
+    all-NaN page is appended, every unused block-table slot points at it, and
+    the rows past each sequence's end inside its last page are set to NaN, so
+    any read outside the visible tokens shows up in the result.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if isinstance(seqlens, tuple) and len(seqlens) == 3 and seqlens[0] == "uniform":
+        L = rng.integers(int(seqlens[1]), int(seqlens[2]) + 1, size=batch).astype(np.int32)
+    else:
+        L = np.asarray(seqlens, dtype=np.int32)
+        if L.shape != (batch,):
+            raise ValueError("seqlens must have one entry per sequence")
+    if (L < 0).any():
+        raise ValueError("sequence lengths must be >= 0")
+    nblk = (L.astype(np.int64) + PAGE - 1) // PAGE
+    total = int(nblk.sum())
+    max_blocks = max(1, int(nblk.max()) if batch else 1)
+    perm = rng.permutation(total).astype(np.int32)
+    fill = total if poison else 0
+    bt = np.full((batch, max_blocks), fill, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        n = int(nblk[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = _normal_bf16(rng, (batch, s_q, h_q, D_QK))
+    kc = _normal_bf16(rng, (total, PAGE, 1, D_QK))
+    poison_page = -1
+    if poison:
+        kc = np.concatenate([kc, np.full((1, PAGE, 1, D_QK), BF16_NAN, dtype=np.uint16)], axis=0)
+        poison_page = total
+        for b in range(batch):
+            if L[b] % PAGE:
+                kc[bt[b, L[b] // PAGE], L[b] % PAGE:, 0, :] = BF16_NAN
+    scale = _fp32(D_QK ** -0.5 if softmax_scale is None else softmax_scale)
+    return PagedInputs(q=q, kcache=kc, block_table=bt, seqlens=L, s_q=s_q, h_q=h_q,
+                       causal=bool(causal), softmax_scale=scale, poison_page=poison_page)
+
+
+# --------------------------------------------------------------------------
+# Sparse fp8 inputs
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class SparseInputs:
+    q: np.ndarray               # uint16 bf16 bits [batch, s_q, h_q, 576]
+    kv: np.ndarray              # uint8 [num_tokens, 640] records
+    indices: np.ndarray         # int32 [batch, s_q, topk], -1 = unused entry
+    h_q: int
+    softmax_scale: float
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def s_q(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[2])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.kv.shape[0])
+
+
+def quantize_rows_e4m3(x: np.ndarray) -> np.ndarray:
+    """Per-row fp8-e4m3 quantisation into 640-byte records.
+
+    scale = max(amax|row|, 2^-126) / 448 in fp32; codes are x / scale rounded
+    to nearest-even e4m3 (OCP E4M3FN, the torch ``float8_e4m3fn`` cast) after
+    clamping to +-448.  Record bytes: [0, 576) codes, [576, 580) scale as
+    little-endian fp32, [580, 640) zero.
+    """
+    import torch  # local import: only the sparse generator needs torch's fp8 cast
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[0]
+    amax = np.abs(x).max(axis=1)
+    scale = (np.maximum(amax, np.float32(2.0 ** -126)) / np.float32(448.0)).astype(np.float32)
+    y = np.clip(x / scale[:, None], np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    rec = np.zeros((n, REC_BYTES), dtype=np.uint8)
+    rec[:, :D_QK] = codes
+    rec[:, SCALE_OFF:SCALE_OFF + 4] = scale.astype("<f4").view(np.uint8).reshape(n, 4)
+    return rec
+
+
+def make_sparse(batch: int, s_q: int, h_q: int, tokens_per_seq: int, topk: int,
+                p_invalid: float, seed: int,
+                softmax_scale: Optional[float] = None) -> SparseInputs:
+    """Draw one sparse fp8 decode input set.
+
+    The KV pool holds ``batch * tokens_per_seq`` tokens; sequence b owns rows
+    [b*tokens_per_seq, (b+1)*tokens_per_seq).  Query token s of sequence b
+    draws ``topk`` distinct positions from [0, tokens_per_seq - s_q + s]
+    (its causal window), in random order, mapped to global rows; then each
+    entry independently becomes -1 with probability ``p_invalid``.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _normal_bf16(rng, (batch, s_q, h_q, D_QK))
+    n_tok = batch * tokens_per_seq
+    kv = np.empty((n_tok, REC_BYTES), dtype=np.uint8)
+    for r0 in range(0, n_tok, _KV_CHUNK_ROWS):
+        r1 = min(n_tok, r0 + _KV_CHUNK_ROWS)
+        kv[r0:r1] = quantize_rows_e4m3(rng.standard_normal((r1 - r0, D_QK), dtype=np.float32))
+    idx = np.empty((batch, s_q, topk), dtype=np.int32)
+    for b in range(batch):
+        for s in range(s_q):
+            window = tokens_per_seq - s_q + s + 1
+            if topk > window:
+                raise ValueError("topk exceeds the causal window")
+            idx[b, s] = rng.choice(window, size=topk, replace=False).astype(np.int32) + b * tokens_per_seq
+    if p_invalid > 0:
+        idx[rng.random((batch, s_q, topk)) < p_invalid] = -1
+    scale = _fp32(D_QK ** -0.5 if softmax_scale is None else softmax_scale)
+    return SparseInputs(q=q, kv=kv, indices=idx, h_q=h_q, softmax_scale=scale)
+
+
+# --------------------------------------------------------------------------
+# The five named workloads
+# --------------------------------------------------------------------------
+CONFIGS = {
+    1: dict(kind="paged", name="tiny paged decode: b=2 s_q=1 h_q=16 L={37,130}",
+            batch=2, s_q=1, h_q=16, seqlens=[37, 130], causal=False),
+    2: dict(kind="paged", name="memory-bound paged decode: b=128 s_q=1 h_q=16 L=4096",
+            batch=128, s_q=1, h_q=16, seqlens=[4096] * 128, causal=False),
+    3: dict(kind="paged", name="compute-bound varlen paged decode: b=128 s_q=2 causal h_q=128 L~U[1024,8192]",
+            batch=128, s_q=2, h_q=128, seqlens=("uniform", 1024, 8192), causal=True),
+    4: dict(kind="paged", name="long-context split-KV paged decode: b=16 s_q=1 h_q=16 L=65536",
+            batch=16, s_q=1, h_q=16, seqlens=[65536] * 16, causal=False),
+    5: dict(kind="sparse", name="sparse fp8 decode: b=32 s_q=6 h_q=64 topk=2048 pool=32768/seq p(-1)=0.05",
+            batch=32, s_q=6, h_q=64, tokens_per_seq=32768, topk=2048, p_invalid=0.05),
+}
+
+
+def config_info(k: int) -> dict:
+    return dict(CONFIGS[k])
+
+
+def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
+    """Inputs for workload ``k`` (1..5) with seed 1000 + k unless given."""
+    c = CONFIGS[k]
+    seed = 1000 + k if seed is None else seed
+    if c["kind"] == "paged":
+        return make_paged(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison)
+    return make_sparse(c["batch"], c["s_q"], c["h_q"], c["tokens_per_seq"], c["topk"], c["p_invalid"], seed)

@@ -1,0 +1,10 @@
+"""CPU oracle (float64) for paged and sparse MLA decode: test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg use it.  It shares no code with the GPU library.
+"""
+
+from .mla_oracle import (  # noqa: F401
+    E4M3_TABLE, attend, bf16_to_f64, e4m3_value, gather_paged_rows,
+    lse_combine, paged_decode, sparse_decode, sparse_rows_f64, visible_count,
+)

@@ -1,0 +1,194 @@
+"""CPU oracle for paged MLA decode and sparse fp8 MLA decode.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The GPU library never calls it and
+shares no code, table or constant with it.
+
+What it computes is the plain definition, in float64, with no tiling, no
+online softmax and no splitting:
+
+* Multi-head latent attention decode is multi-query attention over one shared
+  latent row per cached token: each query head scores the 576-wide row
+  (512 latent dims + 64 RoPE dims) and takes a softmax-weighted sum of the
+  row's first 512 dims, which serve as V ("[flashinfer] FlashInfer, NVFP4를
+  활용한 DeepSeek-V4 디코딩 성능 최적화", section "코드 분석", item 2: a
+  latent row per token that is both K and V).
+* S = Q K^T, P = softmax(S), O = P V ("FlashMLA-ETAP: Efficient Transpose
+  Attention Pipeline ...", section "방법론 / 핵심 메커니즘"), with the scores
+  multiplied by ``softmax_scale`` before the softmax.
+* The log-sum-exp returned beside O is the natural log of the softmax
+  denominator of the scaled scores, in fp32 on the device ("[flashinfer] ...",
+  README tensor table: ``lse`` float32, natural log).
+* Cached rows live in 64-token pages; logical token t of sequence b is row
+  ``t % 64`` of page ``block_table[b][t // 64]`` ("Qu'est-ce que FlashMLA ?",
+  section "Installation et utilisation de FlashMLA", step 3;
+  "DeepSeek, FlashMLA 오픈소스 공개", summary: 64-token paged KV cache).
+* With ``causal`` and s_q > 1 the s_q queries are the sequence's last s_q
+  tokens, and query s sees positions <= L - s_q + s ("[flashinfer] ...",
+  README: causal mask inside the block against the request's last tokens).
+  ``cache_seqlens`` counts those query tokens.  With s_q = 1 causal changes
+  nothing.
+* Sparse decode: query token (b, s) attends exactly the rows listed in
+  ``indices[b, s, :]``; entries equal to -1 are ignored ("deepseek-ai/
+  FlashMLA" project summary, section "기술적 세부 사항", indices tensor).  Each
+  listed entry is one term (duplicates count twice).  Rows are fp8 e4m3
+  values times a per-token scale (same section, KV cache format), decoded
+  exactly in float64 from the OCP E4M3FN encoding.
+* An empty visible set gives O = 0 and LSE = -inf.
+
+The split-KV combine used by the GPU path is, mathematically, the same
+definition evaluated on a partition of the visible set; ``lse_combine`` states
+that identity (section "코드 분석", item 3 of the flashinfer page: split-KV
+combine kernel) so the tests can check it.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Tuple
+
+import numpy as np
+
+D_QK = 576
+D_V = 512
+PAGE = 64
+REC_BYTES = 640
+SCALE_OFF = 576
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 raw bits -> float64 (exact): a bf16 is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3FN byte: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    Exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there are
+    no infinities, so exponent 15 with mantissa 0..6 is an ordinary value
+    (largest 448).
+    """
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def sparse_rows_f64(kv_records: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Dequantise selected 640-byte records: e4m3(code) * per-token fp32 scale, in float64."""
+    rec = np.asarray(kv_records, dtype=np.uint8)[rows]
+    vals = E4M3_TABLE[rec[:, :D_QK]]
+    scale = np.ascontiguousarray(rec[:, SCALE_OFF:SCALE_OFF + 4]).view("<f4").reshape(-1).astype(np.float64)
+    return vals * scale[:, None]
+
+
+# --------------------------------------------------------------------------
+# The attention definition
+# --------------------------------------------------------------------------
+def attend(q: np.ndarray, rows: np.ndarray, sigma: float) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax(sigma * q rows^T) rows[:, :512] and its natural-log LSE, for every query row.
+
+    q: [H, 576] float64, rows: [T, 576] float64.  Returns O [H, 512], LSE [H].
+    """
+    H = q.shape[0]
+    if rows.shape[0] == 0:
+        return np.zeros((H, D_V)), np.full(H, -np.inf)
+    z = sigma * (rows @ q.T)                  # [T, H] scaled scores
+    m = z.max(axis=0)                         # [H]
+    e = np.exp(z - m)                         # [T, H]
+    denom = e.sum(axis=0)                     # [H]
+    o = (e.T @ rows[:, :D_V]) / denom[:, None]
+    return o, m + np.log(denom)
+
+
+def gather_paged_rows(kcache_bits: np.ndarray, block_table_row: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Rows of logical tokens 0..n_tokens-1 of one sequence, gathered through its block table."""
+    out = np.empty((n_tokens, D_QK), dtype=np.float64)
+    for t in range(0, n_tokens, PAGE):
+        page = int(block_table_row[t // PAGE])
+        n = min(PAGE, n_tokens - t)
+        out[t:t + n] = bf16_to_f64(kcache_bits[page, :n, 0, :])
+    return out
+
+
+def visible_count(L: int, s_q: int, s: int, causal: bool) -> int:
+    """Number of leading tokens query s of a length-L sequence sees."""
+    if not causal:
+        return max(0, L)
+    return max(0, min(L, L - s_q + s + 1))
+
+
+def paged_decode(q_bits: np.ndarray, kcache_bits: np.ndarray, block_table: np.ndarray,
+                 seqlens: np.ndarray, softmax_scale: float, causal: bool,
+                 batches: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Paged MLA decode.
+
+    q_bits [B, s_q, h_q, 576] bf16 bits; kcache_bits [pages, 64, 1, 576] bf16 bits;
+    block_table [B, max_blocks] int32; seqlens [B] int32; softmax_scale is an
+    fp32 value.  Returns O [B, s_q, h_q, 512] and LSE [B, s_q, h_q] in float64.
+    With ``batches`` only those sequences are computed (the rest stay NaN).
+    """
+    B, s_q, h_q, _ = q_bits.shape
+    sigma = float(np.float32(softmax_scale))
+    O = np.full((B, s_q, h_q, D_V), np.nan)
+    LSE = np.full((B, s_q, h_q), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seqlens[b])
+        rows = gather_paged_rows(kcache_bits, block_table[b], L)
+        for s in range(s_q):
+            n = visible_count(L, s_q, s, causal)
+            O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows[:n], sigma)
+    return O, LSE
+
+
+def sparse_decode(q_bits: np.ndarray, kv_records: np.ndarray, indices: np.ndarray,
+                  softmax_scale: float,
+                  sets: Optional[Iterable[Tuple[int, int]]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Sparse fp8 MLA decode.
+
+    q_bits [B, s_q, h_q, 576] bf16 bits; kv_records [N, 640] uint8;
+    indices [B, s_q, topk] int32 with -1 = ignore.  Returns O [B, s_q, h_q, 512]
+    and LSE [B, s_q, h_q] in float64.  With ``sets`` only those (b, s) are
+    computed (the rest stay NaN).
+    """
+    B, s_q, h_q, _ = q_bits.shape
+    sigma = float(np.float32(softmax_scale))
+    O = np.full((B, s_q, h_q, D_V), np.nan)
+    LSE = np.full((B, s_q, h_q), np.nan)
+    todo = [(b, s) for b in range(B) for s in range(s_q)] if sets is None else list(sets)
+    for b, s in todo:
+        entries = indices[b, s]
+        listed = entries[entries != -1].astype(np.int64)
+        rows = sparse_rows_f64(kv_records, listed)
+        O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows, sigma)
+    return O, LSE
+
+
+def lse_combine(parts_o: np.ndarray, parts_lse: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge attention results over disjoint token subsets into the result over their union.
+
+    parts_o [n, H, 512], parts_lse [n, H] (natural log, -inf for an empty part).
+    The union's denominator is the sum of the parts' denominators, so
+    LSE = log sum_i exp(LSE_i) and O = sum_i exp(LSE_i - LSE) O_i.  All parts
+    empty gives O = 0, LSE = -inf.
+    """
+    parts_o = np.asarray(parts_o, dtype=np.float64)
+    parts_lse = np.asarray(parts_lse, dtype=np.float64)
+    mu = parts_lse.max(axis=0)                                   # [H]
+    safe_mu = np.where(np.isfinite(mu), mu, 0.0)
+    w = np.where(np.isfinite(parts_lse), np.exp(parts_lse - safe_mu), 0.0)   # [n, H]
+    tot = w.sum(axis=0)
+    o = np.where(tot[:, None] > 0, (w[:, :, None] * parts_o).sum(axis=0) / np.where(tot > 0, tot, 1.0)[:, None], 0.0)
+    lse = np.where(tot > 0, safe_mu + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    return o, lse

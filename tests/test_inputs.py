@@ -1,0 +1,77 @@
+"""The seeded input generators: determinism, bf16 rounding, fp8 quantisation, layouts."""
+
+import numpy as np
+import torch
+
+from mla_inputs import (CONFIGS, bf16_bits_from_f32, bf16_bits_to_f32, make_config,
+                        make_paged, make_sparse)
+from mla_inputs.gen import quantize_rows_e4m3
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([0.0, -0.0, 1e-40, 3.0e38, 1.00390625, 1.0117188], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bf16_bits_from_f32(x), ref)
+    assert np.array_equal(bf16_bits_to_f32(ref), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_paged_generator_is_deterministic_and_well_formed():
+    a = make_paged(3, 2, 16, ("uniform", 10, 200), True, seed=9)
+    b = make_paged(3, 2, 16, ("uniform", 10, 200), True, seed=9)
+    for f in ("q", "kcache", "block_table", "seqlens"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    nblk = (a.seqlens + 63) // 64
+    used = np.concatenate([a.block_table[i, :nblk[i]] for i in range(3)])
+    assert sorted(used.tolist()) == list(range(int(nblk.sum())))       # every pool page once
+    for i in range(3):
+        assert np.all(a.block_table[i, nblk[i]:] == a.poison_page)
+        L = int(a.seqlens[i])
+        last = a.block_table[i, (L - 1) // 64]
+        if L % 64:
+            assert np.all(a.kcache[last, L % 64:] == 0x7FC0)
+        assert not np.any(a.kcache[last, :(L - 1) % 64 + 1] == 0x7FC0)
+    assert a.softmax_scale == float(np.float32(576 ** -0.5))
+
+
+def test_tiny_config_shape():
+    c = make_config(1)
+    assert c.q.shape == (2, 1, 16, 576)
+    assert c.block_table.shape == (2, 3)
+    assert c.kcache.shape == (5, 64, 1, 576)          # 4 pages + the poison page
+    assert list(c.seqlens) == [37, 130]
+    assert sorted(np.concatenate([c.block_table[0, :1], c.block_table[1]]).tolist()) == [0, 1, 2, 3]
+
+
+def test_fp8_quantisation_round_trip():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((50, 576)).astype(np.float32)
+    rec = quantize_rows_e4m3(x)
+    scale = rec[:, 576:580].copy().view("<f4").reshape(-1)
+    vals = torch.from_numpy(rec[:, :576].copy()).view(torch.float8_e4m3fn).float().numpy() * scale[:, None]
+    assert np.all(np.abs(vals - x) <= np.abs(x) * 2.0 ** -4 + scale[:, None] * 2.0 ** -9 + 1e-30)
+    assert np.all(np.abs(rec[:, :576].astype(np.int32) & 0x7F) != 0x7F)     # no NaN codes
+    assert np.all(rec[:, 580:] == 0)
+    assert np.allclose(scale, np.abs(x).max(axis=1) / 448, rtol=1e-6)
+
+
+def test_sparse_generator_indices():
+    inp = make_sparse(2, 3, 16, 200, 50, 0.2, seed=3)
+    assert inp.indices.shape == (2, 3, 50)
+    for b in range(2):
+        for s in range(3):
+            row = inp.indices[b, s]
+            valid = row[row >= 0]
+            assert len(set(valid.tolist())) == valid.size                     # distinct
+            assert np.all(valid >= b * 200) and np.all(valid <= b * 200 + 200 - 3 + s)
+    frac = np.mean(inp.indices == -1)
+    assert 0.05 < frac < 0.4
+    again = make_sparse(2, 3, 16, 200, 50, 0.2, seed=3)
+    assert np.array_equal(inp.indices, again.indices) and np.array_equal(inp.kv, again.kv)
+
+
+def test_config_table():
+    assert set(CONFIGS) == {1, 2, 3, 4, 5}
+    assert CONFIGS[2]["batch"] == 128 and CONFIGS[4]["seqlens"][0] == 65536
+    assert CONFIGS[5]["topk"] == 2048

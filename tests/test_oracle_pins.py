@@ -1,0 +1,319 @@
+"""Pins for the CPU oracle: closed forms, invariants, library special cases.
+
+Each test ties the oracle to something other than itself, so that a dropped
+term, a wrong sign, index or base, or a transposed operand in it fails here.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import bf16_bits_from_f32, make_paged, make_sparse
+from oracle import (E4M3_TABLE, attend, bf16_to_f64, lse_combine, paged_decode,
+                    sparse_decode, sparse_rows_f64, visible_count)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SIGMA = float(np.float32(576 ** -0.5))
+
+
+def _bf16(x):
+    return bf16_bits_from_f32(np.asarray(x, dtype=np.float32))
+
+
+def _one_seq_cache(rows_f32, page_order=None):
+    """Pack rows [T, 576] into a paged cache with a given page order; returns (kcache bits, block_table row)."""
+    T = rows_f32.shape[0]
+    nblk = max(1, -(-T // 64))
+    order = np.arange(nblk) if page_order is None else np.asarray(page_order)
+    kc = np.zeros((nblk, 64, 1, 576), dtype=np.uint16)
+    bits = _bf16(rows_f32)
+    for j in range(nblk):
+        n = min(64, T - 64 * j)
+        if n > 0:
+            kc[order[j], :n, 0, :] = bits[64 * j:64 * j + n]
+    return kc, order.astype(np.int32)
+
+
+# ----------------------------------------------------------------- fp8 format
+def test_e4m3_table_matches_torch_for_all_codes():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(E4M3_TABLE), nan)
+    assert np.array_equal(E4M3_TABLE[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(E4M3_TABLE[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_golden_values_from_ocp_spec():
+    n = 0
+    with open(os.path.join(GOLDEN, "e4m3_ocp.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            code_s, val_s = line.split()
+            code, val = int(code_s, 16), float(val_s)
+            got = E4M3_TABLE[code]
+            if math.isnan(val):
+                assert math.isnan(got)
+            else:
+                assert got == val and math.copysign(1, got) == math.copysign(1, val), (code, got, val)
+            n += 1
+    assert n >= 10
+
+
+def test_every_finite_e4m3_value_is_a_bf16_value():
+    finite = E4M3_TABLE[np.isfinite(E4M3_TABLE)]
+    back = bf16_to_f64(_bf16(finite.astype(np.float32)))
+    assert np.array_equal(back, finite)
+
+
+def test_sparse_record_dequant_is_code_times_scale():
+    rec = np.zeros((2, 640), dtype=np.uint8)
+    rec[0, :576] = 0x38            # 1.0
+    rec[0, 576:580] = np.array([0.25], dtype="<f4").view(np.uint8)
+    rec[1, :576] = np.arange(576) % 0x7e
+    rec[1, 576:580] = np.array([3.0], dtype="<f4").view(np.uint8)
+    rows = sparse_rows_f64(rec, np.array([1, 0]))
+    assert np.all(rows[1] == 0.25)
+    assert np.array_equal(rows[0], E4M3_TABLE[np.arange(576) % 0x7e] * 3.0)
+
+
+# ----------------------------------------------------------------- closed forms
+def test_two_token_golden():
+    vals = {}
+    with open(os.path.join(GOLDEN, "two_token_closed_form.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            k, v = line.split()
+            vals[k] = float(v)
+    q = np.zeros((1, 576)); q[0, 0] = 1.0
+    rows = np.zeros((2, 576)); rows[1, 0] = 1.0; rows[1, 1] = 1.0
+    o, lse = attend(q, rows, 1.0)
+    assert abs(o[0, 0] - vals["O0"]) < 1e-15 and abs(o[0, 1] - vals["O1"]) < 1e-15
+    assert np.all(o[0, 2:] == 0)
+    assert abs(lse[0] - vals["LSE"]) < 1e-15
+
+
+def test_single_cached_token_returns_its_value_row():
+    rng = np.random.default_rng(0)
+    for sigma in (SIGMA, 1.0, 0.5):
+        q = bf16_to_f64(_bf16(rng.standard_normal((16, 576))))
+        row = bf16_to_f64(_bf16(rng.standard_normal((1, 576))))
+        o, lse = attend(q, row, sigma)
+        assert np.array_equal(o, np.broadcast_to(row[0, :512], (16, 512)))
+        z = np.array([math.fsum(q[h] * row[0]) * sigma for h in range(16)])
+        assert np.allclose(lse, z, rtol=0, atol=1e-12)
+
+
+def test_single_token_uses_first_512_dims_as_value_and_all_576_for_scores():
+    q = np.zeros((1, 576)); q[0, 575] = 2.0          # only a RoPE dim scores
+    row = np.zeros((1, 576)); row[0, 575] = 3.0; row[0, 0] = 7.0
+    o, lse = attend(q, row, 0.5)
+    assert o[0, 0] == 7.0 and np.all(o[0, 1:] == 0)
+    assert lse[0] == 3.0                                # 0.5 * 2 * 3
+
+
+def test_two_tokens_closed_form_random():
+    rng = np.random.default_rng(1)
+    q = bf16_to_f64(_bf16(rng.standard_normal((8, 576))))
+    rows = bf16_to_f64(_bf16(rng.standard_normal((2, 576))))
+    o, lse = attend(q, rows, SIGMA)
+    for h in range(8):
+        z0 = SIGMA * math.fsum(q[h] * rows[0]); z1 = SIGMA * math.fsum(q[h] * rows[1])
+        w1 = 1.0 / (1.0 + math.exp(z0 - z1)); w0 = 1.0 / (1.0 + math.exp(z1 - z0))
+        assert np.allclose(o[h], w0 * rows[0, :512] + w1 * rows[1, :512], rtol=0, atol=1e-13)
+        assert abs(lse[h] - np.logaddexp(z0, z1)) < 1e-12
+
+
+def test_equal_scores_give_mean_of_values_and_log_count():
+    rng = np.random.default_rng(2)
+    rows = bf16_to_f64(_bf16(rng.standard_normal((37, 576))))
+    o, lse = attend(np.zeros((4, 576)), rows, SIGMA)
+    assert np.allclose(o, rows[:, :512].mean(axis=0), rtol=0, atol=1e-14)
+    assert np.allclose(lse, math.log(37), rtol=0, atol=1e-14)
+    # equal non-zero scores: query only in the RoPE dims, every row shares its RoPE dims
+    rows[:, 512:] = rows[0, 512:]
+    q = np.zeros((3, 576)); q[:, 512:] = bf16_to_f64(_bf16(rng.standard_normal((3, 64))))
+    o, lse = attend(q, rows, SIGMA)
+    z = SIGMA * (q[:, 512:] @ rows[0, 512:])
+    assert np.allclose(o, rows[:, :512].mean(axis=0), rtol=0, atol=1e-13)
+    assert np.allclose(lse, z + math.log(37), rtol=0, atol=1e-12)
+
+
+def test_empty_visible_set():
+    o, lse = attend(np.ones((2, 576)), np.zeros((0, 576)), SIGMA)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# ----------------------------------------------------------------- library special case
+def test_paged_matches_torch_sdpa_and_logsumexp():
+    inp = make_paged(3, 2, 16, [1, 77, 200], causal=False, seed=5)
+    O, LSE = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    flat = torch.from_numpy(bf16_to_f64(inp.kcache.reshape(-1, 576)))
+    for b in range(3):
+        L = int(inp.seqlens[b])
+        tok = torch.arange(L)
+        rid = torch.from_numpy(inp.block_table[b]).long()[tok // 64] * 64 + tok % 64
+        K = flat.index_select(0, rid)                        # [L, 576]
+        V = K[:, :512].contiguous()
+        for s in range(2):
+            q = torch.from_numpy(bf16_to_f64(inp.q[b, s]))   # [16, 576]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None], K[None].contiguous(), V[None], scale=inp.softmax_scale)[0]
+            assert np.allclose(O[b, s], ref.numpy(), rtol=0, atol=1e-12)
+            lse = torch.logsumexp(inp.softmax_scale * torch.mm(q, K.t().contiguous()), dim=1)
+            assert np.allclose(LSE[b, s], lse.numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- invariants
+def test_block_table_permutation_is_bitwise_invariant():
+    rng = np.random.default_rng(3)
+    rows = rng.standard_normal((300, 576)).astype(np.float32)
+    kc1, bt1 = _one_seq_cache(rows)
+    kc2, bt2 = _one_seq_cache(rows, page_order=rng.permutation(5))
+    q = _bf16(rng.standard_normal((1, 1, 16, 576)))
+    L = np.array([300], dtype=np.int32)
+    o1, l1 = paged_decode(q, kc1, bt1[None], L, SIGMA, False)
+    o2, l2 = paged_decode(q, kc2, bt2[None], L, SIGMA, False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_poisoned_tails_and_unused_slots_are_never_read():
+    inp = make_paged(4, 3, 16, [1, 63, 64, 130], causal=True, seed=7, poison=True)
+    assert inp.poison_page >= 0
+    O, LSE = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    # L=1 with s_q=3 causal: query 0 and 1 see nothing, query 2 sees token 0
+    assert np.all(O[0, :2] == 0) and np.all(np.isneginf(LSE[0, :2]))
+    assert np.all(np.isfinite(O[0, 2])) and np.all(np.isfinite(O[1:]))
+    assert np.all(np.isfinite(LSE[1:]))
+
+
+def test_causal_query_equals_noncausal_on_truncated_sequence():
+    inp = make_paged(2, 4, 16, [150, 67], causal=True, seed=11)
+    O, LSE = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    for b in range(2):
+        L = int(inp.seqlens[b])
+        for s in range(4):
+            Lt = np.array([L - 4 + s + 1], dtype=np.int32)
+            o, l = paged_decode(inp.q[b:b + 1, s:s + 1], inp.kcache, inp.block_table[b:b + 1], Lt,
+                                inp.softmax_scale, False)
+            assert np.array_equal(O[b, s], o[0, 0]) and np.array_equal(LSE[b, s], l[0, 0])
+
+
+def test_causal_mask_ignores_poisoned_future_rows():
+    inp = make_paged(1, 3, 16, [100], causal=True, seed=12, poison=False)
+    O, LSE = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    kc = inp.kcache.copy()
+    page = inp.block_table[0, 1]
+    kc[page, 98 - 64, 0, :] = 0x7FC0      # token 98: visible only to the last query
+    O2, LSE2 = paged_decode(inp.q, kc, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    assert np.array_equal(O[0, 0], O2[0, 0]) and np.array_equal(LSE[0, 0], LSE2[0, 0])
+    assert np.all(np.isnan(O2[0, 1])) and np.all(np.isnan(O2[0, 2]))   # tokens 98 is visible to queries 1, 2
+    assert visible_count(100, 3, 0, True) == 98
+
+
+def test_causal_with_one_query_equals_noncausal():
+    inp = make_paged(3, 1, 16, [5, 64, 129], causal=True, seed=13)
+    a = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    c = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def test_split_then_combine_equals_unsplit():
+    rng = np.random.default_rng(17)
+    q = bf16_to_f64(_bf16(rng.standard_normal((16, 576))))
+    rows = bf16_to_f64(_bf16(rng.standard_normal((500, 576))))
+    o_full, l_full = attend(q, rows, SIGMA)
+    for trial in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, 500), size=trial + 1, replace=False))
+        bounds = [0, *cuts.tolist(), 500]
+        parts = [attend(q, rows[a:b], SIGMA) for a, b in zip(bounds[:-1], bounds[1:])]
+        o, l = lse_combine(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        assert np.allclose(o, o_full, rtol=0, atol=1e-13)
+        assert np.allclose(l, l_full, rtol=0, atol=1e-12)
+        assert np.allclose(l, np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0), rtol=0, atol=1e-12)
+    # empty parts carry no weight; all empty gives (0, -inf)
+    e = attend(q, rows[:0], SIGMA)
+    o, l = lse_combine(np.stack([e[0], o_full, e[0]]), np.stack([e[1], l_full, e[1]]))
+    assert np.allclose(o, o_full, rtol=0, atol=1e-15) and np.allclose(l, l_full, rtol=0, atol=1e-15)
+    o, l = lse_combine(np.stack([e[0], e[0]]), np.stack([e[1], e[1]]))
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+# ----------------------------------------------------------------- sparse
+def _small_sparse(seed=21, topk=40, p_invalid=0.1):
+    return make_sparse(2, 3, 16, 96, topk, p_invalid, seed)
+
+
+def test_sparse_minus_one_entries_are_ignored_bitwise():
+    inp = _small_sparse()
+    O, LSE = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+    idx = np.full((2, 3, 70), -1, dtype=np.int32)
+    rng = np.random.default_rng(0)
+    for b in range(2):
+        for s in range(3):
+            keep = inp.indices[b, s]
+            pos = np.sort(rng.choice(70, size=keep.size, replace=False))
+            idx[b, s, pos] = keep
+    O2, LSE2 = sparse_decode(inp.q, inp.kv, idx, inp.softmax_scale)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2)
+
+
+def test_sparse_all_minus_one_gives_zero_and_neg_inf():
+    inp = _small_sparse()
+    idx = inp.indices.copy(); idx[1, 2] = -1
+    O, LSE = sparse_decode(inp.q, inp.kv, idx, inp.softmax_scale)
+    assert np.all(O[1, 2] == 0) and np.all(np.isneginf(LSE[1, 2]))
+    assert np.all(np.isfinite(O[0])) and np.all(np.isfinite(LSE[0]))
+
+
+def test_sparse_duplicate_entry_counts_twice():
+    inp = _small_sparse(topk=2, p_invalid=0.0)
+    a, c = int(inp.indices[0, 0, 0]), int(inp.indices[0, 0, 1])
+    idx = np.array([[[a, a, c]]], dtype=np.int32)
+    O, LSE = sparse_decode(inp.q[:1, :1], inp.kv, idx, inp.softmax_scale)
+    rows = sparse_rows_f64(inp.kv, np.array([a, c]))
+    q = bf16_to_f64(inp.q[0, 0])
+    for h in range(16):
+        za = inp.softmax_scale * math.fsum(q[h] * rows[0]); zc = inp.softmax_scale * math.fsum(q[h] * rows[1])
+        wa = 2 * math.exp(za); wc = math.exp(zc)
+        assert np.allclose(O[0, 0, h], (wa * rows[0, :512] + wc * rows[1, :512]) / (wa + wc), rtol=0, atol=1e-12)
+        assert abs(LSE[0, 0, h] - math.log(wa + wc)) < 1e-12
+
+
+def test_sparse_equals_paged_on_the_same_rows():
+    """Sparse decode over all visible positions == paged decode on a cache holding the same values.
+
+    With power-of-two scales every dequantised fp8 value is a bf16 value, so
+    both entry points see identical rows.
+    """
+    rng = np.random.default_rng(23)
+    T = 150
+    rec = np.zeros((T, 640), dtype=np.uint8)
+    codes = rng.integers(0, 256, size=(T, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    rec[:, :576] = codes
+    rec[:, 576:580] = (2.0 ** rng.integers(-4, 3, size=T)).astype("<f4").view(np.uint8).reshape(T, 4)
+    vals = sparse_rows_f64(rec, np.arange(T))
+    kc, bt = _one_seq_cache(vals.astype(np.float32), page_order=rng.permutation(3))
+    assert np.array_equal(bf16_to_f64(_bf16(vals.astype(np.float32))), vals)
+    q = _bf16(rng.standard_normal((1, 2, 16, 576)))
+    L = np.array([T], dtype=np.int32)
+    Op, Lp = paged_decode(q, kc, bt[None], L, SIGMA, causal=True)
+    idx = np.full((1, 2, T), -1, dtype=np.int32)
+    idx[0, 0, :T - 1] = np.arange(T - 1)
+    idx[0, 1, :] = np.arange(T)
+    Os, Ls = sparse_decode(q, rec, idx, SIGMA)
+    assert np.allclose(Op, Os, rtol=0, atol=1e-13) and np.allclose(Lp, Ls, rtol=0, atol=1e-13)
+
+
+def test_visible_count():
+    assert visible_count(10, 1, 0, False) == 10
+    assert visible_count(10, 1, 0, True) == 10
+    assert [visible_count(10, 3, s, True) for s in range(3)] == [8, 9, 10]
+    assert [visible_count(1, 3, s, True) for s in range(3)] == [0, 0, 1]
+    assert visible_count(0, 2, 1, False) == 0
