@@ -1,0 +1,212 @@
+"""Python binding of libmla.so: paged and sparse MLA decode on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/mla.h``; there is no CPU or
+PyTorch fallback.  PyTorch provides device memory and the current stream.
+Importing this package raises if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+D_QK, D_V, PAGE, SPARSE_REC, META_INTS = 576, 512, 64, 640, 8
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTS = (
+    "mla_status_string", "mla_num_parts", "mla_get_metadata", "mla_get_metadata_host",
+    "mla_workspace_size", "mla_decode_paged", "mla_sparse_splits", "mla_workspace_size_sparse",
+    "mla_decode_sparse",
+)
+
+
+class MLAError(RuntimeError):
+    """A non-OK status returned by libmla.so."""
+
+    def __init__(self, call: str, status: int, msg: str):
+        super().__init__("%s failed: %s" % (call, msg))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmla.so is not built (%s); run __graft_entry__.build() or "
+                          "python head_latent_attention_paged_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_num_parts.argtypes = [i32, i32, i32]
+    lib.mla_num_parts.restype = i32
+    lib.mla_get_metadata.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_get_metadata.restype = i32
+    lib.mla_get_metadata_host.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    lib.mla_get_metadata_host.restype = i32
+    lib.mla_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.mla_workspace_size.restype = sz
+    lib.mla_decode_paged.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32,
+                                     vp, vp, i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_paged.restype = i32
+    lib.mla_sparse_splits.argtypes = [i32, i32, i32, i32]
+    lib.mla_sparse_splits.restype = i32
+    lib.mla_workspace_size_sparse.argtypes = [i32, i32, i32, i32, i32]
+    lib.mla_workspace_size_sparse.restype = sz
+    lib.mla_decode_sparse.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_sparse.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.mla_status_string(status).decode()
+
+
+def _check(call: str, status: int) -> None:
+    if status != MLA_OK:
+        raise MLAError(call, status, status_string(status))
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+# --------------------------------------------------------------------------
+# Metadata
+# --------------------------------------------------------------------------
+def num_parts(h_q: int, s_q: int, num_cus: int = 0) -> int:
+    return int(lib.mla_num_parts(num_cus, h_q, s_q))
+
+
+def get_metadata(cache_seqlens: torch.Tensor, h_q: int, s_q: int,
+                 num_parts_: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tile-scheduler metadata for one decode step: (tile_meta [P, 8], num_splits [batch+1]) int32."""
+    _require(cache_seqlens, "cache_seqlens", torch.int32)
+    batch = cache_seqlens.shape[0]
+    P = num_parts(h_q, s_q) if num_parts_ is None else int(num_parts_)
+    dev = cache_seqlens.device
+    tile_meta = torch.empty((P, META_INTS), dtype=torch.int32, device=dev)
+    num_splits = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _check("mla_get_metadata", lib.mla_get_metadata(
+        cache_seqlens.data_ptr(), batch, h_q, s_q, P, tile_meta.data_ptr(), num_splits.data_ptr(),
+        _stream_ptr(dev)))
+    return tile_meta, num_splits
+
+
+def get_metadata_host(cache_seqlens, num_parts_: int, h_q: int = 16, s_q: int = 1):
+    """Host twin of get_metadata on host int32 arrays (numpy); returns numpy arrays."""
+    import numpy as np
+
+    L = np.ascontiguousarray(cache_seqlens, dtype=np.int32)
+    batch = L.shape[0]
+    tile_meta = np.zeros((num_parts_, META_INTS), dtype=np.int32)
+    num_splits = np.zeros((batch + 1,), dtype=np.int32)
+    _check("mla_get_metadata_host", lib.mla_get_metadata_host(
+        L.ctypes.data, batch, h_q, s_q, num_parts_, tile_meta.ctypes.data, num_splits.ctypes.data))
+    return tile_meta, num_splits
+
+
+# --------------------------------------------------------------------------
+# Paged decode
+# --------------------------------------------------------------------------
+def workspace_size(batch: int, s_q: int, h_q: int, num_parts_: int) -> int:
+    return int(lib.mla_workspace_size(batch, s_q, h_q, num_parts_))
+
+
+def decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                 cache_seqlens: torch.Tensor, metadata: Tuple[torch.Tensor, torch.Tensor],
+                 softmax_scale: float = D_QK ** -0.5, causal: bool = False,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged MLA decode; returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q])."""
+    batch, s_q, h_q, d = q.shape
+    if d != D_QK:
+        raise ValueError("q must have 576 dims per head")
+    _require(q, "q", torch.bfloat16)
+    _require(kcache, "kcache", torch.bfloat16)
+    if kcache.dim() != 4 or tuple(kcache.shape[1:]) != (PAGE, 1, D_QK):
+        raise ValueError("kcache must be [num_blocks, 64, 1, 576]")
+    _require(block_table, "block_table", torch.int32)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
+    tile_meta, num_splits = metadata
+    P = tile_meta.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, (batch, s_q, h_q, D_V))
+    _require(lse, "lse", torch.float32, (batch, s_q, h_q))
+    need = workspace_size(batch, s_q, h_q, P)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_paged", lib.mla_decode_paged(
+        q.data_ptr(), kcache.data_ptr(), kcache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
+        tile_meta.data_ptr(), num_splits.data_ptr(), P,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Sparse fp8 decode
+# --------------------------------------------------------------------------
+def sparse_splits(batch: int, s_q: int, h_q: int, topk: int) -> int:
+    return int(lib.mla_sparse_splits(batch, s_q, h_q, topk))
+
+
+def workspace_size_sparse(batch: int, s_q: int, h_q: int, topk: int, splits: int = 0) -> int:
+    return int(lib.mla_workspace_size_sparse(batch, s_q, h_q, topk, splits))
+
+
+def decode_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                  softmax_scale: float = D_QK ** -0.5, splits: int = 0,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse fp8 MLA decode over 640-byte records; indices -1 = skip."""
+    batch, s_q, h_q, d = q.shape
+    if d != D_QK:
+        raise ValueError("q must have 576 dims per head")
+    _require(q, "q", torch.bfloat16)
+    _require(kv, "kv", torch.uint8)
+    if kv.dim() != 2 or kv.shape[1] != SPARSE_REC:
+        raise ValueError("kv must be [num_tokens, 640] uint8 records")
+    _require(indices, "indices", torch.int32)
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (batch, s_q):
+        raise ValueError("indices must be [batch, s_q, topk]")
+    topk = indices.shape[2]
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, (batch, s_q, h_q, D_V))
+    _require(lse, "lse", torch.float32, (batch, s_q, h_q))
+    need = workspace_size_sparse(batch, s_q, h_q, topk, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_sparse", lib.mla_decode_sparse(
+        q.data_ptr(), kv.data_ptr(), kv.shape[0], indices.data_ptr(), topk, batch, s_q, h_q,
+        float(softmax_scale), int(splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, lse

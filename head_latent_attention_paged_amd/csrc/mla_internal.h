@@ -1,0 +1,63 @@
+// Internal declarations shared by the host API (mla_api.cpp) and the gfx950 kernels (mla_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace mla {
+
+constexpr int kDqk = 576;            // latent (512) + RoPE (64) dims of one cached row
+constexpr int kDv = 512;             // value dims (first 512 of the row)
+constexpr int kPage = 64;            // tokens per page
+constexpr int kRec = 640;            // bytes per sparse fp8 record
+constexpr int kChunk = 32;           // tokens per kernel chunk
+constexpr int kMetaInts = 8;
+constexpr int kMetaOverheadBlocks = 1;   // per-sequence fixed cost, in 64-token blocks
+constexpr int kMaxBatchMeta = 16384;
+constexpr int kMaxRows = 4096;       // s_q * h_q limit
+constexpr int kSparseTargetItems = 1024;  // work items the sparse split count aims for
+
+// Row tiling of one sequence's s_q*h_q query rows.  A workgroup holds 4 waves:
+// `rw` of them split the rows (16*nt rows each), the other factor 4/rw splits
+// the KV chunks between independent softmax streams merged at the end.
+struct Tiling {
+    int nt;          // 16-row MFMA tiles per wave (1 or 2)
+    int rw;          // row-waves per workgroup (1, 2 or 4)
+    int rows_wg;     // rows per workgroup = 16 * nt * rw
+    int row_groups;  // workgroups per sequence (or per sparse query token)
+};
+Tiling choose_tiling(int rows);
+
+struct AttnArgs {
+    const void* q;              // bf16 [groups, M, 576]
+    const void* kv;             // paged: bf16 [blocks, 64, 576]; sparse: [tokens, 640] records
+    const int32_t* block_table; // paged
+    const int32_t* seqlens;     // paged
+    const int32_t* indices;     // sparse [groups, topk]
+    const int32_t* tile_meta;   // paged
+    const int32_t* num_splits;  // paged: prefix [batch+1]
+    void* out;                  // bf16 [groups, M, 512]
+    float* lse;                 // [groups, M]
+    float* part_o;              // [slots, M, 512]
+    float* part_lse;            // [slots, M]
+    int batch;                  // paged: sequences; sparse: query tokens (batch*s_q)
+    int s_q, h_q, M;            // M = rows per group (paged s_q*h_q, sparse h_q)
+    int max_blocks;
+    int topk;
+    int causal;
+    int num_parts;              // paged parts; sparse: splits per query token
+    int split_len;              // sparse entries per split (multiple of kChunk)
+    float scale_log2;           // softmax_scale * log2(e)
+};
+
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts,
+                           int32_t* tile_meta, int32_t* num_splits, hipStream_t stream);
+void metadata_host(const int32_t* seqlens, int batch, int num_parts,
+                   int32_t* tile_meta, int32_t* num_splits);
+hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream);
+hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
+                          int uniform_splits, int groups, int rows, void* out, float* lse,
+                          hipStream_t stream);
+
+}  // namespace mla

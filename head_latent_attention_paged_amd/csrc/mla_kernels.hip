@@ -1,0 +1,745 @@
+// gfx950 (CDNA4) kernels for paged and sparse MLA decode.
+//
+// K0  mla_metadata_kernel   tile-scheduler metadata from device sequence lengths
+// K1  mla_decode_kernel     gather -> Q.K^T (576) -> online softmax -> P.V (512) -> final or partial
+//                           (paged bf16 cache, or sparse fp8 records through an index list)
+// K2  mla_combine_kernel    LSE-weighted merge of split-KV partials
+//
+// The attention follows S = Q K^T, P = softmax(S), O = P V ("FlashMLA-ETAP: Efficient
+// Transpose Attention Pipeline ...", section 방법론 / 핵심 메커니즘).  As in that paper's
+// transposed form, each wave computes S^T = K Q^T with the KV tokens on the MFMA's M side,
+// so 16 query rows fill a 16x16x32 bf16 MFMA without padding; the S^T accumulator layout is
+// then directly the B operand of O^T = V^T P^T, and only V needs a transposed LDS read
+// (ds_read_b64_tr_b16).  Everything else (chunking, LDS layout, XCD mapping, splits) is
+// designed for CDNA4 here and not taken from the pages.
+#include "mla_internal.h"
+
+#include <cmath>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+constexpr int kRowBytes = kDqk * 2;       // 1152: one bf16 row in HBM
+constexpr int kChunkBytes = kChunk * kRowBytes;
+// LDS chunk layout: region A holds dims 0..511 of the 32 rows (1024 B per row), region B the
+// 64 RoPE dims (128 B per row), so each region can be filled by whole-wave 1 KB writes.
+constexpr int kRowA = 1024;
+constexpr int kRegionB = kChunk * kRowA;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// --------------------------------------------------------------------------
+// Small helpers
+// --------------------------------------------------------------------------
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// LDS row layout: row r holds 72 granules of 16 B (8 dims each); granule c sits at slot
+// c ^ swz(r).  swz permutes within aligned groups of 8 granules so that (a) 8 consecutive
+// rows reading the same granule (QK^T A operand, ds_read_b128) hit 8 distinct 16-B bank
+// groups and (b) 4 consecutive rows reading the same 32-B pair (V^T transposed read) hit 4
+// distinct 32-B bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// granule c (0..63) of row r in region A; granule c (0..7) of row r in region B
+__device__ __forceinline__ int lds_a(int r, int c) { return r * kRowA + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int lds_b(int r, int c) { return kRegionB + r * 128 + ((c ^ swz(r)) << 4); }
+
+__device__ __forceinline__ f4 mfma16(bf16x8 a, bf16x8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(unsigned, v);
+}
+
+// 16 e4m3 codes -> 16 bf16 (exact: every finite e4m3 value is a bf16 value)
+__device__ __forceinline__ void fp8x16_to_bf16(uint4 c, uint4& lo, uint4& hi) {
+#define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))
+    lo = make_uint4(MLA_CVT(c.x, false), MLA_CVT(c.x, true), MLA_CVT(c.y, false), MLA_CVT(c.y, true));
+    hi = make_uint4(MLA_CVT(c.z, false), MLA_CVT(c.z, true), MLA_CVT(c.w, false), MLA_CVT(c.w, true));
+#undef MLA_CVT
+}
+
+// --------------------------------------------------------------------------
+// K1: decode kernel
+// --------------------------------------------------------------------------
+template <int NT, int RW, bool SPARSE>
+struct DecodeCfg {
+    static constexpr int TS = 4 / RW;                         // independent token streams
+    static constexpr int ROWS_WAVE = 16 * NT;
+    static constexpr int ROWS_WG = ROWS_WAVE * RW;
+    static constexpr int LOADERS = 64 * RW;                   // threads loading one chunk
+    // Loader shape.  Each wave of a stream owns rows rw, rw+RW, ...: one load instruction per
+    // row puts lane L on 16-B granule L of that row (bf16: dims 8L..8L+7 of the first 512;
+    // sparse fp8: granules 0..35 are the 576 codes and lane 36 fetches the granule holding
+    // the fp32 scale).  bf16 rows also have granules 64..71 (the RoPE dims), spread over all
+    // loaders of the stream.
+    static constexpr int RA = kChunk / RW;                    // rows per loader wave
+    static constexpr int RB = SPARSE ? 0 : (kChunk * 8) / LOADERS;
+    static constexpr int BUF_BYTES = TS * kChunkBytes;
+    static constexpr int MERGE_ACC_BYTES = (TS - 1) * RW * 32 * 64 * 16;   // one tile of acc per wave
+    static constexpr int MERGE_ML_BYTES = (TS - 1) * RW * 64 * 8;
+    static constexpr int MAIN_BYTES = BUF_BYTES > MERGE_ACC_BYTES + MERGE_ML_BYTES
+                                          ? BUF_BYTES : MERGE_ACC_BYTES + MERGE_ML_BYTES;
+    static constexpr int AUX_BYTES = SPARSE ? TS * kChunk * 8 : 0;          // per-row scale + valid flag
+    static constexpr int LDS_BYTES = MAIN_BYTES + AUX_BYTES;
+};
+
+template <int NT, int RW, bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_kernel(const AttnArgs a) {
+    using C = DecodeCfg<NT, RW, SPARSE>;
+    constexpr int TS = C::TS;
+    constexpr int RA = C::RA;
+    constexpr int RB = C::RB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rw = wave % RW;
+    const int ts = wave / RW;
+    const int lt = rw * 64 + lane;             // loader index within this token stream
+    const int g4 = lane >> 4;                  // lane group (0..3)
+    const int l16 = lane & 15;
+
+    char* buf = smem + ts * kChunkBytes;
+    float* aux = reinterpret_cast<float*>(smem + C::MAIN_BYTES) + ts * kChunk;                // token scale
+    int* auxok = reinterpret_cast<int*>(smem + C::MAIN_BYTES) + TS * kChunk + ts * kChunk;    // token used
+
+    // ---- work item -> (part or sparse split, row group), XCD-aware -------------------------
+    const int R = ceil_div(a.M, C::ROWS_WG);
+    const int n_items = (SPARSE ? a.batch * a.num_parts : a.num_parts);
+    int item, rg;
+    {
+        const int bid = blockIdx.x;
+        if ((n_items & 7) == 0) {
+            // blocks are dispatched round-robin over the 8 XCDs: keep the R row groups of one
+            // work item on one XCD, launched back to back, so they share its L2 copy of the KV.
+            const int xcd = bid & 7, k = bid >> 3;
+            item = (k / R) * 8 + xcd;
+            rg = k % R;
+        } else {
+            item = bid / R;
+            rg = bid % R;
+        }
+    }
+    const int rbase = rg * C::ROWS_WG + rw * C::ROWS_WAVE;   // first row of this wave
+
+    // LDS byte offsets that do not depend on the chunk.
+    // K operand of S^T (ds_read_b128): row tt*16 + l16, granule ks*4 + g4; the XOR only touches
+    // the low 3 granule bits, so for ks < 16 granule 8*(ks/2) + (4*(ks&1) + g4) sits at
+    // kbase[tt][ks&1] + 128*(ks/2); ks = 16, 17 are the RoPE granules in region B.
+    int kbase[2][2], kbaseB[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int row = tt * 16 + l16;
+            kbase[tt][par] = lds_a(row, 4 * par + g4);
+            kbaseB[tt][par] = lds_b(row, 4 * par + g4);
+        }
+    auto kaddr = [&](int tt, int ks) {
+        return ks < 16 ? kbase[tt][ks & 1] + 128 * (ks >> 1) : kbaseB[tt][ks & 1];
+    };
+    // V^T operand (ds_read_b64_tr_b16): lane supplies token row 4*g4 + l16/4 (+16 for the upper
+    // 16 tokens), dims 16*dt + 4*(l16&3) .. +3, i.e. granule 2*dt + ((l16&3)>>1), byte (l16&1)*8.
+    // granule 8*(dt/4) + (2*(dt&3) + h) maps to vbase[half][dt&3] + 128*(dt/4).
+    int vbase[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) {
+            const int row = 4 * g4 + (l16 >> 2) + 16 * hf;
+            vbase[hf][d4] = lds_a(row, 2 * d4 + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+        }
+
+    // per-segment state
+    bf16x8 qf[NT][18];
+    f4 acc[32][NT];
+    float m_run[NT], l_run[NT];
+    uint4 preA[RA];
+    uint4 preB[RB > 0 ? RB : 1];
+    int my_idx = -1;
+
+    // ---- one segment: a contiguous token range of one sequence (or one sparse split) -------
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
+        // Q fragments (B operand of S^T = K Q^T): lane holds row l16 of tile n, dims 8*g4 + 32*ks
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int r = rbase + 16 * n + l16;
+            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (r < a.M ? r : 0)) * (kDqk * 2);
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
+                if (r >= a.M) v = make_uint4(0, 0, 0, 0);
+                qf[n][ks] = __builtin_bit_cast(bf16x8, v);
+            }
+            m_run[n] = -INFINITY;
+            l_run[n] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) acc[dt][n] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+        const int nch = ceil_div(t1 - t0, kChunk);
+
+        // causal limit per row of this lane (paged): query s sees t <= L - s_q + s
+        int limit[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int r = rbase + 16 * n + l16;
+            limit[n] = a.causal ? (L - a.s_q + r / a.h_q) : (L - 1);
+        }
+
+        // issue the global loads of chunk c into registers
+        auto load_chunk = [&](int c, int jlo = 0, int jhi = C::RA) {
+            if (c >= nch) return;
+            const int tb = t0 + c * kChunk;
+            const int nrows = min(kChunk, t1 - tb);
+            if constexpr (!SPARSE && RW == 1) {
+                // one wave per stream: copy HBM -> LDS directly (no registers).  Each instruction
+                // writes 64 consecutive 16-B LDS slots; lane L of row r fetches the granule the
+                // swizzle puts in slot L.  Rows past the segment end repeat its last row (finite
+                // data, weight 0), so stale or NaN memory never reaches P.V.
+                const int page = a.block_table[(size_t)grp * a.max_blocks + (tb >> 6)];
+                const char* base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int r = 0; r < kChunk; ++r) {
+                    const int rr = min(r, nrows - 1);
+                    __builtin_amdgcn_global_load_lds(base + rr * kRowBytes + ((lane ^ swz(r)) << 4),
+                                                     (__attribute__((address_space(3))) void*)(buf + r * kRowA),
+                                                     16, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int slot = j * 64 + lane;
+                    const int row = slot >> 3;
+                    const int rr = min(row, nrows - 1);
+                    __builtin_amdgcn_global_load_lds(base + rr * kRowBytes + (64 + ((slot & 7) ^ swz(row))) * 16,
+                                                     (__attribute__((address_space(3))) void*)(buf + kRegionB + j * 1024),
+                                                     16, 0, 0);
+                }
+            } else if constexpr (!SPARSE) {
+                // a chunk is 32 consecutive rows of one page: contiguous in HBM
+                const int page = a.block_table[(size_t)grp * a.max_blocks + (tb >> 6)];
+                const char* base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+#pragma unroll
+                for (int j = 0; j < RA; ++j) {
+                    const int row = rw + RW * j;
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (row < nrows) v = *reinterpret_cast<const uint4*>(base + row * kRowBytes + lane * 16);
+                    preA[j] = v;
+                }
+#pragma unroll
+                for (int j = 0; j < RB; ++j) {
+                    const int q = lt + C::LOADERS * j;
+                    const int row = q >> 3, col = 64 + (q & 7);
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (row < nrows) v = *reinterpret_cast<const uint4*>(base + row * kRowBytes + col * 16);
+                    preB[j] = v;
+                }
+            } else {
+                // lanes 0..31 fetch the chunk's 32 indices; each row's index is then wave-uniform
+                if (jlo == 0) {
+                    my_idx = -1;
+                    if (lane < nrows) my_idx = a.indices[(size_t)grp * a.topk + tb + lane];
+                }
+                const char* kvb = static_cast<const char*>(a.kv);
+#pragma unroll
+                for (int j = 0; j < RA; ++j) {
+                    if (j < jlo || j >= jhi) continue;
+                    const int row = rw + RW * j;
+                    const int idx = __builtin_amdgcn_readlane(my_idx, row);
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (idx >= 0 && lane <= 36)
+                        v = *reinterpret_cast<const uint4*>(kvb + (size_t)idx * kRec + lane * 16);
+                    preA[j] = v;
+                }
+            }
+        };
+
+        // write the prefetched chunk into this stream's LDS buffer (bf16, swizzled rows)
+        auto store_chunk = [&](int jlo = 0, int jhi = C::RA) {
+            if constexpr (!SPARSE && RW == 1) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the direct copies have landed
+            } else if constexpr (!SPARSE) {
+#pragma unroll
+                for (int j = 0; j < RA; ++j) {
+                    const int row = rw + RW * j;
+                    *reinterpret_cast<uint4*>(buf + lds_a(row, lane)) = preA[j];
+                }
+#pragma unroll
+                for (int j = 0; j < RB; ++j) {
+                    const int q = lt + C::LOADERS * j;
+                    *reinterpret_cast<uint4*>(buf + lds_b(q >> 3, q & 7)) = preB[j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < RA; ++j) {
+                    if (j < jlo || j >= jhi) continue;
+                    const int row = rw + RW * j;
+                    if (lane < 36) {
+                        uint4 lo, hi;
+                        fp8x16_to_bf16(preA[j], lo, hi);
+                        const int o0 = lane < 32 ? lds_a(row, 2 * lane) : lds_b(row, 2 * lane - 64);
+                        const int o1 = lane < 32 ? lds_a(row, 2 * lane + 1) : lds_b(row, 2 * lane - 63);
+                        *reinterpret_cast<uint4*>(buf + o0) = lo;
+                        *reinterpret_cast<uint4*>(buf + o1) = hi;
+                    } else if (lane == 36) {
+                        const int idx = __builtin_amdgcn_readlane(my_idx, row);
+                        aux[row] = __builtin_bit_cast(float, preA[j].x);
+                        auxok[row] = idx >= 0;
+                    }
+                }
+            }
+        };
+
+        // compute on the chunk in LDS
+        auto compute_chunk = [&](int c) {
+            const int tb = t0 + c * kChunk;
+            // S^T[token][row] = sum_k K[token][k] Q[row][k]
+            f4 s[2][NT];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) s[tt][n] = f4{0.f, 0.f, 0.f, 0.f};
+            // software-pipelined: the K fragments of step ks+1 are read while step ks multiplies;
+            // the scheduling barriers keep the compiler from hoisting all 36 reads at once.
+            bf16x8 kf[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) kf[0][tt] = *reinterpret_cast<const bf16x8*>(buf + kaddr(tt, 0));
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                if (ks + 1 < 18) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        kf[(ks + 1) & 1][tt] = *reinterpret_cast<const bf16x8*>(buf + kaddr(tt, ks + 1));
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) s[tt][n] = mfma16(kf[ks & 1][tt], qf[n][ks], s[tt][n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // this lane's tokens are tt*16 + 4*g4 + i
+            float tsc[2][4];
+            bool tok_ok[2][4];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = tt * 16 + 4 * g4 + i;
+                    if constexpr (SPARSE) {
+                        tsc[tt][i] = aux[tok];
+                        tok_ok[tt][i] = auxok[tok] != 0;
+                    } else {
+                        tsc[tt][i] = 1.f;
+                        tok_ok[tt][i] = tb + tok < t1;
+                    }
+                }
+            bf16x8 pT[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                float x[2][4];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tb + tt * 16 + 4 * g4 + i;
+                        bool valid = tok_ok[tt][i];
+                        if constexpr (!SPARSE) valid = valid && (t <= limit[n]);
+                        const float f = SPARSE ? a.scale_log2 * tsc[tt][i] : a.scale_log2;
+                        x[tt][i] = valid ? s[tt][n][i] * f : -INFINITY;
+                        mx = fmaxf(mx, x[tt][i]);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run[n], mx);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = exp2_fast(m_run[n] - m_use);
+                float p[2][4];
+                float psum = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[tt][i] = exp2_fast(x[tt][i] - m_use);
+                        psum += p[tt][i];
+                        if constexpr (SPARSE) p[tt][i] *= tsc[tt][i];
+                    }
+                l_run[n] = l_run[n] * alpha + psum;
+                m_run[n] = m_new;
+#pragma unroll
+                for (int dt = 0; dt < 32; ++dt) acc[dt][n] *= alpha;
+                // B operand of O^T = V^T P^T: k index 8*g4 + j <-> token j<4 ? 4*g4+j : 16+4*g4+(j-4)
+                const uint4 pk = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
+                pT[n] = __builtin_bit_cast(bf16x8, pk);
+            }
+            // O^T[d][row] += sum_token V[token][d] P[row][token]; V^T fragments of dt+1 are read
+            // (transposing LDS reads) while dt multiplies.
+            auto read_vt = [&](int dt) {
+                const int off = 128 * (dt >> 2);
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4v*)(buf + vbase[0][dt & 3] + off));
+                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4v*)(buf + vbase[1][dt & 3] + off));
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            bf16x8 vf[2];
+            vf[0] = read_vt(0);
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) {
+                if (dt + 1 < 32) vf[(dt + 1) & 1] = read_vt(dt + 1);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[dt][n] = mfma16(vf[dt & 1], pT[n], acc[dt][n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        // ---- chunk loop: all waves run the same trip count (barriers inside) ----
+        // With one wave per stream (RW == 1) the stream's LDS buffer is private to that wave: it
+        // orders its own LDS writes and reads, and the 4 waves of the block run unsynchronised,
+        // so one wave's loads overlap another's compute.  With several waves per stream the
+        // chunk is shared and the next chunk is prefetched into registers during compute.
+        auto stream_sync = [&]() {
+            if constexpr (RW == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            else __syncthreads();
+        };
+        constexpr bool kPrefetch = RW > 1;
+        if constexpr (kPrefetch) load_chunk(ts);
+        for (int cb = 0; cb < nch; cb += TS) {
+            const int c = cb + ts;
+            stream_sync();               // previous chunk's LDS reads are done
+            if constexpr (SPARSE && !kPrefetch) {
+                // gathered rows go through registers: two halves keep the register count down
+                if (c < nch) {
+                    load_chunk(c, 0, RA / 2);
+                    store_chunk(0, RA / 2);
+                    load_chunk(c, RA / 2, RA);
+                    store_chunk(RA / 2, RA);
+                }
+            } else {
+                if constexpr (!kPrefetch) load_chunk(c);
+                if (kPrefetch || c < nch) store_chunk();
+            }
+            stream_sync();               // chunk visible to the stream's waves
+            if constexpr (kPrefetch) load_chunk(c + TS);   // next chunk in flight during compute
+            if (c < nch) compute_chunk(c);
+        }
+
+        // ---- finish: row sums, merge token streams, write ----
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            l_run[n] += __shfl_xor(l_run[n], 16);
+            l_run[n] += __shfl_xor(l_run[n], 32);
+        }
+        if constexpr (TS > 1) {
+            f4* macc = reinterpret_cast<f4*>(smem);
+            float* mml = reinterpret_cast<float*>(smem + C::MERGE_ACC_BYTES);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                __syncthreads();
+                if (ts > 0) {
+                    const int w = (ts - 1) * RW + rw;
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) macc[(w * 32 + dt) * 64 + lane] = acc[dt][n];
+                    mml[(w * 64 + lane) * 2 + 0] = m_run[n];
+                    mml[(w * 64 + lane) * 2 + 1] = l_run[n];
+                }
+                __syncthreads();
+                if (ts == 0) {
+                    float mk[TS], lk[TS];
+                    mk[0] = m_run[n];
+                    lk[0] = l_run[n];
+                    float m_new = mk[0];
+#pragma unroll
+                    for (int k = 1; k < TS; ++k) {
+                        const int w = (k - 1) * RW + rw;
+                        mk[k] = mml[(w * 64 + lane) * 2 + 0];
+                        lk[k] = mml[(w * 64 + lane) * 2 + 1];
+                        m_new = fmaxf(m_new, mk[k]);
+                    }
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    float al[TS];
+                    float l_new = 0.f;
+#pragma unroll
+                    for (int k = 0; k < TS; ++k) {
+                        al[k] = exp2_fast(mk[k] - m_use);
+                        l_new += al[k] * lk[k];
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) {
+                        f4 v = acc[dt][n] * al[0];
+#pragma unroll
+                        for (int k = 1; k < TS; ++k) {
+                            const int w = (k - 1) * RW + rw;
+                            v += macc[(w * 32 + dt) * 64 + lane] * al[k];
+                        }
+                        acc[dt][n] = v;
+                    }
+                    m_run[n] = m_new;
+                    l_run[n] = l_new;
+                }
+            }
+        }
+        if (ts == 0) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const int r = rbase + 16 * n + l16;
+                const float l = l_run[n];
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+                const float lse_v = l > 0.f ? (m_run[n] + __log2f(l)) * kLn2 : -INFINITY;
+                if (r < a.M) {
+                    if (final_out) {
+                        __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + r) * kDv + 4 * g4;
+#pragma unroll
+                        for (int dt = 0; dt < 32; ++dt) {
+                            const f4 v = acc[dt][n] * inv;
+                            const uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                            *reinterpret_cast<uint2*>(orow + dt * 16) = pk;
+                        }
+                        if (g4 == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
+                    } else {
+                        float* prow = a.part_o + ((size_t)slot * a.M + r) * kDv + 4 * g4;
+#pragma unroll
+                        for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f4*>(prow + dt * 16) = acc[dt][n] * inv;
+                        if (g4 == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
+                    }
+                }
+            }
+        }
+    };
+
+    if constexpr (!SPARSE) {
+        const int* meta = a.tile_meta + (size_t)item * kMetaInts;
+        const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
+        for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
+            const int L = a.seqlens[bb];
+            const int nb = ceil_div(L, kPage);
+            const int lo = (bb == b0) ? blk0 : 0;
+            const int hi = (bb == b1) ? blk1 : nb;
+            if (lo >= hi) continue;
+            const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
+            const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
+            run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+            __syncthreads();
+        }
+    } else {
+        const int grp = item / a.num_parts;          // query token (b*s_q + s)
+        const int split = item % a.num_parts;
+        const int e0 = split * a.split_len;
+        const int e1 = min(e0 + a.split_len, a.topk);
+        if (e0 < e1)
+            run_segment(grp, e0, e1, 0, a.num_parts == 1, grp * a.num_parts + split);
+    }
+}
+
+// --------------------------------------------------------------------------
+// K2: combine split-KV partials (one 128-thread half-block per output row)
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          const int32_t* __restrict__ prefix,
+                                                          int uniform_splits, int rows,
+                                                          __bf16* __restrict__ out, float* __restrict__ lse) {
+    const int grp = blockIdx.x;
+    const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
+    const int d4 = threadIdx.x & 127;
+    if (r >= rows) return;
+    int base, n;
+    if (prefix) {
+        base = prefix[grp];
+        n = prefix[grp + 1] - base;
+    } else {
+        base = grp * uniform_splits;
+        n = uniform_splits;
+    }
+    if (n == 1) return;   // the decode kernel wrote this row directly
+    __bf16* orow = out + ((size_t)grp * rows + r) * kDv + d4 * 4;
+    float mu = -INFINITY;
+    for (int i = 0; i < n; ++i) mu = fmaxf(mu, part_lse[(size_t)(base + i) * rows + r]);
+    f4 o = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (mu != -INFINITY) {
+        for (int i = 0; i < n; ++i) {
+            const float li = part_lse[(size_t)(base + i) * rows + r];
+            const float w = (li == -INFINITY) ? 0.f : expf(li - mu);
+            wsum += w;
+            const f4 v = *reinterpret_cast<const f4*>(part_o + ((size_t)(base + i) * rows + r) * kDv + d4 * 4);
+            o += v * w;
+        }
+        o *= 1.f / wsum;
+    }
+    const uint2 pk = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    *reinterpret_cast<uint2*>(orow) = pk;
+    if (d4 == 0) lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
+}
+
+// --------------------------------------------------------------------------
+// K0: tile-scheduler metadata (one workgroup; integer only, same partition as the host twin)
+// --------------------------------------------------------------------------
+constexpr int kMetaThreads = 1024;
+
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp) {
+    // exclusive scan of v over the 1024 threads; tmp holds 1024 ints
+    const int t = threadIdx.x;
+    tmp[t] = v;
+    __syncthreads();
+    for (int off = 1; off < kMetaThreads; off <<= 1) {
+        const int add = (t >= off) ? tmp[t - off] : 0;
+        __syncthreads();
+        tmp[t] += add;
+        __syncthreads();
+    }
+    const int incl = tmp[t];
+    __syncthreads();
+    return incl - v;
+}
+
+__global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_t* __restrict__ seqlens, int batch,
+                                                                    int num_parts, int32_t* __restrict__ tile_meta,
+                                                                    int32_t* __restrict__ num_splits) {
+    __shared__ int cpre[kMaxBatchMeta + 1];   // cost prefix C_b
+    __shared__ int spre[kMaxBatchMeta + 1];   // split prefix
+    __shared__ int tmp[kMetaThreads];
+    __shared__ int s_payload;
+    const int t = threadIdx.x;
+    // cost prefix
+    int carry = 0;
+    for (int b0 = 0; b0 < batch; b0 += kMetaThreads) {
+        const int b = b0 + t;
+        int cost = 0;
+        if (b < batch) {
+            const int L = seqlens[b];
+            const int nb = L > 0 ? (L + kPage - 1) / kPage : 0;
+            cost = nb > 0 ? nb + kMetaOverheadBlocks : 0;
+        }
+        const int ex = block_excl_scan(cost, tmp);
+        if (b < batch) cpre[b] = carry + ex;
+        __syncthreads();
+        if (t == kMetaThreads - 1) tmp[0] = ex + cost;
+        __syncthreads();
+        carry += tmp[0];
+        __syncthreads();
+    }
+    if (t == 0) cpre[batch] = carry;
+    const int total = carry;
+    if (t == 0) s_payload = total > 0 ? (total + num_parts - 1) / num_parts : 1;
+    __syncthreads();
+    const int payload = s_payload;
+    // splits per sequence and their prefix
+    carry = 0;
+    for (int b0 = 0; b0 < batch; b0 += kMetaThreads) {
+        const int b = b0 + t;
+        int sp = 0;
+        if (b < batch) {
+            const int L = seqlens[b];
+            const int nb = L > 0 ? (L + kPage - 1) / kPage : 0;
+            if (nb > 0) {
+                const int u0 = cpre[b] + kMetaOverheadBlocks;
+                sp = (u0 + nb - 1) / payload - u0 / payload + 1;
+            }
+        }
+        const int ex = block_excl_scan(sp, tmp);
+        if (b < batch) spre[b] = carry + ex;
+        __syncthreads();
+        if (t == kMetaThreads - 1) tmp[0] = ex + sp;
+        __syncthreads();
+        carry += tmp[0];
+        __syncthreads();
+    }
+    if (t == 0) spre[batch] = carry;
+    __syncthreads();
+    for (int b = t; b <= batch; b += kMetaThreads) num_splits[b] = spre[b];
+    // parts
+    for (int p = t; p < num_parts; p += kMetaThreads) {
+        int bb[2], blk[2];
+        for (int e = 0; e < 2; ++e) {
+            const long long u = (long long)(p + e) * payload;
+            if (u >= total) {
+                bb[e] = batch;
+                blk[e] = 0;
+                continue;
+            }
+            // b = number of sequences whose cost range ends at or before u
+            int lo = 0, hi = batch;   // find first b with cpre[b+1] > u
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (cpre[mid + 1] <= u) lo = mid + 1; else hi = mid;
+            }
+            bb[e] = lo;
+            const int off = (int)(u - cpre[lo]) - kMetaOverheadBlocks;
+            blk[e] = off > 0 ? off : 0;
+        }
+        int slot = 0;
+        if (bb[0] < batch) {
+            const int first = (cpre[bb[0]] + kMetaOverheadBlocks) / payload;
+            slot = spre[bb[0]] + (p - first);
+            if (p < first) slot = 0;
+        }
+        int32_t* m = tile_meta + (size_t)p * kMetaInts;
+        m[0] = bb[0]; m[1] = blk[0]; m[2] = bb[1]; m[3] = blk[1]; m[4] = slot;
+        m[5] = 0; m[6] = 0; m[7] = 0;
+    }
+}
+
+// --------------------------------------------------------------------------
+// Launchers
+// --------------------------------------------------------------------------
+Tiling choose_tiling(int rows) {
+    Tiling t;
+    t.nt = 1;
+    t.rw = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    t.rows_wg = 16 * t.nt * t.rw;
+    t.row_groups = (rows + t.rows_wg - 1) / t.rows_wg;
+    return t;
+}
+
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts,
+                           int32_t* tile_meta, int32_t* num_splits, hipStream_t stream) {
+    hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(kMetaThreads), 0, stream,
+                       seqlens, batch, num_parts, tile_meta, num_splits);
+    return hipGetLastError();
+}
+
+template <int NT, int RW, bool SPARSE>
+static hipError_t launch_decode_t(const AttnArgs& a, int items, int R, hipStream_t stream) {
+    hipLaunchKernelGGL((mla_decode_kernel<NT, RW, SPARSE>), dim3(items * R), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
+    const Tiling t = choose_tiling(a.M);
+    const int items = sparse ? a.batch * a.num_parts : a.num_parts;
+    const int R = t.row_groups;
+#define MLA_DISPATCH(NT_, RW_)                                                     \
+    if (t.nt == NT_ && t.rw == RW_)                                                \
+        return sparse ? launch_decode_t<NT_, RW_, true>(a, items, R, stream)       \
+                      : launch_decode_t<NT_, RW_, false>(a, items, R, stream);
+    MLA_DISPATCH(1, 1)
+    MLA_DISPATCH(1, 2)
+    MLA_DISPATCH(1, 4)
+#undef MLA_DISPATCH
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* prefix,
+                          int uniform_splits, int groups, int rows, void* out, float* lse,
+                          hipStream_t stream) {
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
+                       part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse);
+    return hipGetLastError();
+}
+
+}  // namespace mla

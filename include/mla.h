@@ -1,0 +1,166 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) paged / sparse MLA decode library (libmla.so).
+ *
+ * Multi-head latent attention decode: every query head attends over one
+ * shared 576-wide latent row per cached token (512 latent dims + 64 RoPE
+ * dims); the row's first 512 dims are the value ("[flashinfer] FlashInfer,
+ * NVFP4를 활용한 DeepSeek-V4 디코딩 성능 최적화", section "코드 분석", item 2:
+ * paged MQA over a latent row that is both K and V).  Scores are
+ * softmax_scale * q.k over all 576 dims; O = softmax(scores) V; the returned
+ * LSE is the natural log of the softmax denominator, fp32 (same README
+ * table).  Queries that see no token get O = 0 and LSE = -inf.
+ *
+ * Conventions for every call below:
+ *  - Pointers marked [device] are device pointers, [host] host pointers.
+ *    Tensors are dense and row-major.  q, kcache, kv, out and workspace must
+ *    be 16-byte aligned.
+ *  - The caller allocates and owns every buffer and the stream.  The library
+ *    allocates nothing, keeps no state between calls and never synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    All work is enqueued on it asynchronously.
+ *  - Arguments the host can check are validated before anything is
+ *    launched; a bad argument returns an error status and enqueues nothing.
+ *    Values that live in device memory (block-table entries, sequence
+ *    lengths, indices) are the caller's responsibility: an out-of-range
+ *    value there is undefined behaviour.  Device faults surface at the
+ *    caller's next synchronisation.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_D_QK 576           /* dims of a cached latent row: 512 latent + 64 RoPE */
+#define MLA_D_V 512            /* value dims: the first 512 dims of the same row    */
+#define MLA_PAGE 64            /* tokens per KV-cache page                          */
+#define MLA_SPARSE_REC 640     /* bytes per fp8 record of the sparse cache          */
+#define MLA_META_INTS 8        /* int32 per part in the tile-scheduler metadata     */
+#define MLA_MAX_BATCH_META 16384 /* largest batch mla_get_metadata accepts          */
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, misalignment, non-finite scale */
+    MLA_ERR_UNSUPPORTED = 2,   /* a shape outside what the kernels handle             */
+    MLA_ERR_WORKSPACE = 3,     /* workspace_bytes smaller than the size function's value */
+    MLA_ERR_HIP = 4            /* the HIP runtime refused a launch                     */
+} mla_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(mla_status_t status);
+
+/*
+ * Number of KV parts the tile scheduler splits one decode step into: about
+ * one workgroup per compute unit once the row groups of a sequence are
+ * counted.  num_cus <= 0 queries the current device.  Returns >= 1, a
+ * multiple of 8 when num_cus is (so the part -> XCD mapping is exact).
+ * Any value >= 1 is valid for the calls below; larger values force more
+ * KV splits.
+ */
+int mla_num_parts(int num_cus, int h_q, int s_q);
+
+/*
+ * Tile-scheduler metadata, computed on the device from the device-resident
+ * sequence lengths, once per decode step and reused by every layer
+ * ("Qu'est-ce que FlashMLA ?", section "Installation et utilisation de
+ * FlashMLA", steps 2-3: get_mla_metadata, then one decode call per layer).
+ *
+ *   cache_seqlens [device] int32[batch]  tokens in each sequence's cache,
+ *                                        including its s_q new query tokens
+ *   tile_meta     [device] int32[num_parts * MLA_META_INTS]  (out)
+ *   num_splits    [device] int32[batch + 1]                  (out)
+ *
+ * Work is counted in 64-token blocks plus a fixed per-sequence overhead and
+ * cut into num_parts contiguous, equally sized ranges of the flattened
+ * (sequence, block) order; a sequence crossing a range edge is split.
+ * num_splits is the exclusive prefix sum of the number of parts touching
+ * each sequence (num_splits[b+1] - num_splits[b] = splits of sequence b);
+ * it indexes the partial results in the workspace.  tile_meta[p] holds
+ * {begin_seq, begin_block, end_seq, end_block, first_partial_slot, 0,0,0}.
+ * h_q and s_q are accepted for the call shape of the pages' API; the
+ * partition does not depend on them.  batch <= MLA_MAX_BATCH_META.
+ */
+mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q,
+                              int num_parts, int32_t* tile_meta, int32_t* num_splits,
+                              void* stream);
+
+/* The same partition computed on the host from host arrays ([host] pointers, synchronous). */
+mla_status_t mla_get_metadata_host(const int32_t* cache_seqlens, int batch, int h_q, int s_q,
+                                   int num_parts, int32_t* tile_meta, int32_t* num_splits);
+
+/* Bytes of workspace mla_decode_paged needs (split-KV partial outputs and LSEs). */
+size_t mla_workspace_size(int batch, int s_q, int h_q, int num_parts);
+
+/*
+ * Paged MLA decode ("Qu'est-ce que FlashMLA ?", step 3: flash_mla_with_kvcache
+ * with q, kvcache, block_table, cache_seqlens, dv, metadata, num_splits,
+ * causal; "DeepSeek, FlashMLA 오픈소스 공개", summary: BF16, 64-token pages).
+ *
+ *   q             [device] bf16 [batch, s_q, h_q, 576]
+ *   kcache        [device] bf16 [num_blocks, 64, 1, 576]
+ *   block_table   [device] int32[batch, max_blocks]; logical token t of
+ *                 sequence b is row t % 64 of page block_table[b][t / 64]
+ *   cache_seqlens [device] int32[batch]; must equal what the metadata saw
+ *   softmax_scale fp32 multiplier of q.k (e.g. 576^-0.5)
+ *   causal        nonzero: the s_q queries are the sequence's last s_q
+ *                 tokens and query s sees tokens <= L - s_q + s ("[flashinfer]
+ *                 ...", README: causal mask against the request's last tokens)
+ *   tile_meta, num_splits, num_parts: from mla_get_metadata
+ *   workspace     [device] >= mla_workspace_size(batch, s_q, h_q, num_parts) bytes
+ *   out           [device] bf16 [batch, s_q, h_q, 512]   (written)
+ *   lse           [device] fp32 [batch, s_q, h_q], natural log (written)
+ *
+ * Rows past a sequence's end and block-table slots past its last page are
+ * never used, whatever they hold.  s_q * h_q <= 4096.
+ */
+mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blocks,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                              float softmax_scale, int causal,
+                              const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                              void* workspace, size_t workspace_bytes,
+                              void* out, float* lse, void* stream);
+
+/*
+ * Number of topk splits mla_decode_sparse uses per query token for a given
+ * shape when called with splits = 0, and the workspace it then needs.
+ */
+int mla_sparse_splits(int batch, int s_q, int h_q, int topk);
+size_t mla_workspace_size_sparse(int batch, int s_q, int h_q, int topk, int splits);
+
+/*
+ * Sparse fp8 MLA decode ("deepseek-ai/FlashMLA" project summary, sections
+ * "사용 방법" and "기술적 세부 사항": token-level sparse attention over an fp8
+ * cache holding raw quantised values plus a per-token scale; a 3-D indices
+ * tensor lists the tokens each query reads, -1 entries are ignored).
+ *
+ *   q        [device] bf16 [batch, s_q, h_q, 576]
+ *   kv       [device] uint8[num_tokens, 640] records: bytes [0,576) are OCP
+ *            E4M3FN codes of the 576 dims, bytes [576,580) the token's fp32
+ *            scale (little endian), bytes [580,640) unused.  Row value =
+ *            e4m3(code) * scale.
+ *   indices  [device] int32[batch, s_q, topk]: global token rows in
+ *            [0, num_tokens), or -1 to skip.  Each entry is one term
+ *            (a repeated row counts repeatedly).  There is no causal flag:
+ *            the index lists carry any masking.
+ *   splits   0 = mla_sparse_splits(...); otherwise topk is cut into this many
+ *            ranges (clamped to [1, ceil(topk/32)]) merged by an LSE combine
+ *   workspace[device] >= mla_workspace_size_sparse(batch, s_q, h_q, topk, splits)
+ *   out, lse as for mla_decode_paged.
+ */
+mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens,
+                               const int32_t* indices, int topk,
+                               int batch, int s_q, int h_q, float softmax_scale, int splits,
+                               void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

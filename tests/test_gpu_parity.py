@@ -1,0 +1,202 @@
+"""GPU parity: libmla.so on the MI355X against the float64 CPU oracle, element by element.
+
+Bar: max|O - O_ref| <= 1e-2 * max|O_ref| + 2e-3 and |LSE - LSE_ref| <= 1e-3 (rows that see
+no token: O = 0 and LSE = -inf exactly).  Metadata (integer) is compared bit-exactly with
+the host twin.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from mla_inputs import make_config, make_paged, make_sparse
+from oracle import paged_decode, sparse_decode
+from tests.helpers import check_parity, dev_bf16, dev_i32, dev_u8, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import head_latent_attention_paged_amd as mla
+
+    return mla, torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_paged(env, inp, num_parts=None):
+    import torch
+
+    mla, dev = env
+    q = dev_bf16(inp.q, dev)
+    kc = dev_bf16(inp.kcache, dev)
+    bt = dev_i32(inp.block_table, dev)
+    sl = dev_i32(inp.seqlens, dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
+    out, lse = mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal)
+    torch.cuda.synchronize()
+    return to_host(out, lse)
+
+
+def run_sparse(env, inp, splits=0):
+    import torch
+
+    mla, dev = env
+    out, lse = mla.decode_sparse(dev_bf16(inp.q, dev), dev_u8(inp.kv, dev), dev_i32(inp.indices, dev),
+                                 inp.softmax_scale, splits)
+    torch.cuda.synchronize()
+    return to_host(out, lse)
+
+
+# ----------------------------------------------------------------- metadata
+@pytest.mark.parametrize("L,P", [
+    ([37, 130], 256), ([4096] * 128, 256), ([65536] * 16, 256), ([1, 64, 65, 0, 128, 3000], 7),
+    ([0, 0, 5], 4), ([100] * 9, 1), (list(range(0, 3000, 37)), 64),
+    (list(np.random.default_rng(1).integers(0, 9000, size=3000)), 128),
+])
+def test_metadata_kernel_matches_host_twin(env, L, P):
+    import torch
+
+    mla, dev = env
+    _say("metadata", len(L), P)
+    L = np.asarray(L, dtype=np.int32)
+    meta_h, ns_h = mla.get_metadata_host(L, P)
+    meta_d, ns_d = mla.get_metadata(dev_i32(L, dev), 16, 1, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(meta_d.cpu().numpy(), meta_h)
+    assert np.array_equal(ns_d.cpu().numpy(), ns_h)
+
+
+# ----------------------------------------------------------------- paged
+def test_tiny_config(env):
+    inp = make_config(1)
+    o, l = run_paged(env, inp)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, inp.causal)
+    check_parity(o, l, o_ref, l_ref, "tiny")
+
+
+PAGED_CASES = [
+    # batch, s_q, h_q, seqlens, causal, num_parts
+    (3, 1, 16, [1, 64, 65], False, None),
+    (4, 1, 16, [63, 128, 129, 300], False, 1),
+    (2, 1, 16, [1000, 777], False, 64),
+    (3, 2, 16, [2, 100, 257], True, None),
+    (2, 4, 16, [3, 200], True, 5),
+    (2, 3, 16, [40, 96], True, 3),
+    (2, 2, 128, [130, 700], True, None),
+    (2, 2, 128, [1, 2], True, 4),
+    (2, 1, 64, [500, 64], False, 3),
+    (3, 1, 16, [0, 50, 0], False, None),
+    (2, 1, 48, [77, 300], False, None),
+    (1, 2, 64, [4000], False, 16),
+    (5, 1, 32, [33, 31, 32, 1, 97], False, 2),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[str(i) for i in range(len(PAGED_CASES))])
+def test_paged_cases(env, case):
+    batch, s_q, h_q, L, causal, P = case
+    _say("paged case", case)
+    inp = make_paged(batch, s_q, h_q, L, causal, seed=100 + sum(L) + h_q, poison=True)
+    o, l = run_paged(env, inp, P)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
+    check_parity(o, l, o_ref, l_ref, str(case))
+
+
+def test_forced_splits_and_rerun_determinism(env):
+    inp = make_paged(3, 2, 32, [900, 1500, 64], True, seed=5, poison=True)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    for P in (1, 2, 8, 64, 256):
+        _say("split", P)
+        o, l = run_paged(env, inp, P)
+        check_parity(o, l, o_ref, l_ref, "P=%d" % P)
+        o2, l2 = run_paged(env, inp, P)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2), "rerun differs at P=%d" % P
+
+
+def test_block_table_permutation_is_bitwise_invariant(env):
+    inp = make_paged(2, 1, 16, [300, 200], False, seed=9, poison=False)
+    o1, l1 = run_paged(env, inp, 8)
+    rng = np.random.default_rng(4)
+    perm = rng.permutation(inp.num_pages)
+    kc2 = np.empty_like(inp.kcache)
+    kc2[perm] = inp.kcache
+    inp.kcache = kc2
+    inp.block_table = perm[inp.block_table].astype(np.int32)
+    o2, l2 = run_paged(env, inp, 8)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------- sparse
+SPARSE_CASES = [
+    # batch, s_q, h_q, tokens_per_seq, topk, p_invalid, splits
+    (2, 2, 16, 256, 100, 0.1, 0),
+    (2, 1, 64, 512, 33, 0.0, 0),
+    (1, 3, 32, 300, 290, 0.5, 3),
+    (2, 2, 128, 4096, 2048, 0.05, 0),
+    (1, 1, 16, 64, 1, 0.0, 0),
+    (2, 6, 64, 2000, 512, 0.05, 1),
+    (1, 2, 48, 700, 600, 0.2, 7),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=[str(i) for i in range(len(SPARSE_CASES))])
+def test_sparse_cases(env, case):
+    batch, s_q, h_q, T, topk, p, splits = case
+    _say("sparse case", case)
+    inp = make_sparse(batch, s_q, h_q, T, topk, p, seed=200 + topk + h_q)
+    o, l = run_sparse(env, inp, splits)
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+    check_parity(o, l, o_ref, l_ref, str(case))
+
+
+def test_sparse_all_skipped_and_duplicates(env):
+    inp = make_sparse(2, 2, 16, 300, 64, 0.0, seed=31)
+    inp.indices[0, 1, :] = -1                         # a query that reads nothing
+    inp.indices[1, 0, 10:20] = inp.indices[1, 0, 0]   # repeated rows count repeatedly
+    for splits in (0, 1, 2):
+        o, l = run_sparse(env, inp, splits)
+        o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+        check_parity(o, l, o_ref, l_ref, "skip/dup splits=%d" % splits)
+        assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
+
+
+# ----------------------------------------------------------------- full-size workloads
+def _sampled(o, l, o_ref, l_ref, rows, what):
+    return check_parity(o[rows], l[rows], o_ref[rows], l_ref[rows], what)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_full_size_paged_config_sampled(env, k):
+    _say("full-size config", k)
+    inp = make_config(k, poison=False)
+    o, l = run_paged(env, inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    rng = np.random.default_rng(k)
+    sample = sorted(rng.choice(inp.batch, size=3 if k == 4 else 6, replace=False).tolist())
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale,
+                                inp.causal, batches=sample)
+    err, rmse = _sampled(o, l, o_ref, l_ref, sample, "config %d" % k)
+    _say("config", k, "sampled max err", err, "rmse", rmse)
+
+
+def test_full_size_sparse_config_sampled(env):
+    _say("full-size config 5")
+    inp = make_config(5)
+    o, l = run_sparse(env, inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    rng = np.random.default_rng(5)
+    sets = [(int(b), int(s)) for b, s in zip(rng.integers(0, 32, 16), rng.integers(0, 6, 16))]
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale, sets=sets)
+    bs = tuple(np.array(sets).T)
+    err, rmse = check_parity(o[bs], l[bs], o_ref[bs], l_ref[bs], "config 5")
+    _say("config 5 sampled max err", err, "rmse", rmse)

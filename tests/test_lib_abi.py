@@ -1,0 +1,154 @@
+"""libmla.so without a GPU: exports, status codes, argument validation, host metadata twin."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import head_latent_attention_paged_amd as m
+
+    return m
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(mla):
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(mla.lib, n), n
+    assert sorted(names) == sorted(mla.EXPORTS)
+
+
+def test_status_strings(mla):
+    assert mla.status_string(0) == "MLA_OK"
+    assert mla.status_string(3) == "MLA_ERR_WORKSPACE"
+    assert mla.status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_num_parts_and_workspace(mla):
+    assert mla.num_parts(16, 1, num_cus=256) == 256
+    assert mla.num_parts(128, 2, num_cus=256) % 8 == 0
+    assert mla.num_parts(16, 1, num_cus=3) >= 1
+    ws = mla.workspace_size(128, 1, 16, 256)
+    assert ws >= (128 + 256) * 16 * 513 * 4
+    assert mla.workspace_size(0, 1, 16, 8) == 0
+    assert mla.sparse_splits(32, 6, 64, 2048) >= 1
+    assert mla.workspace_size_sparse(1, 1, 16, 32, 1) == 0          # one split needs no workspace
+
+
+def _paged_call(mla, **kw):
+    args = dict(q=16, kc=16, nb=4, bt=16, maxb=1, sl=16, batch=1, s_q=1, h_q=16, scale=0.04, causal=0,
+                meta=16, ns=16, P=8, ws=16, wsb=1 << 30, out=16, lse=16)
+    args.update(kw)
+    return mla.lib.mla_decode_paged(args["q"], args["kc"], args["nb"], args["bt"], args["maxb"], args["sl"],
+                                    args["batch"], args["s_q"], args["h_q"], args["scale"], args["causal"],
+                                    args["meta"], args["ns"], args["P"], args["ws"], args["wsb"],
+                                    args["out"], args["lse"], None)
+
+
+def test_paged_validation_before_launch(mla):
+    # every case is rejected on the host, so no device is touched
+    assert _paged_call(mla, q=None) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, lse=None) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, batch=0) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, h_q=-1) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, scale=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, q=24) == mla.MLA_ERR_INVALID_ARG          # misaligned
+    assert _paged_call(mla, s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
+    assert _paged_call(mla, wsb=100) == mla.MLA_ERR_WORKSPACE
+    assert _paged_call(mla, ws=None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_sparse_validation_before_launch(mla):
+    f = mla.lib.mla_decode_sparse
+    ok = dict(q=16, kv=16, nt=10, idx=16, topk=64, batch=1, s_q=1, h_q=16, scale=0.04, splits=0,
+              ws=16, wsb=1 << 30, out=16, lse=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["kv"], a["nt"], a["idx"], a["topk"], a["batch"], a["s_q"], a["h_q"], a["scale"],
+                 a["splits"], a["ws"], a["wsb"], a["out"], a["lse"], None)
+
+    assert call(idx=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(topk=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(splits=-1) == mla.MLA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == mla.MLA_ERR_INVALID_ARG
+    assert call(kv=8) == mla.MLA_ERR_INVALID_ARG
+    assert call(splits=2, wsb=10) == mla.MLA_ERR_WORKSPACE
+    assert call(h_q=5000) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_metadata_validation(mla):
+    assert mla.lib.mla_get_metadata(None, 1, 16, 1, 8, 16, 16, None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.lib.mla_get_metadata(16, 0, 16, 1, 8, 16, 16, None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.lib.mla_get_metadata(16, 20000, 16, 1, 8, 16, 16, None) == mla.MLA_ERR_UNSUPPORTED
+
+
+def _check_partition(L, P, meta, ns):
+    """Every (sequence, block) is covered by exactly one part; split counts and slots agree."""
+    L = np.asarray(L)
+    nb = (L + 63) // 64
+    batch = len(L)
+    cover = [np.zeros(n, dtype=np.int32) for n in nb]
+    seen_slots = set()
+    touched = np.zeros(batch, dtype=np.int32)
+    for p in range(P):
+        b0, k0, b1, k1, slot0 = meta[p, :5]
+        assert (b0, k0) <= (b1, k1)
+        for b in range(b0, min(b1, batch - 1) + 1):
+            lo = k0 if b == b0 else 0
+            hi = k1 if b == b1 else nb[b]
+            if lo >= hi:
+                continue
+            cover[b][lo:hi] += 1
+            slot = slot0 if b == b0 else ns[b]
+            assert ns[b] <= slot < ns[b + 1]
+            assert (b, slot) not in seen_slots
+            seen_slots.add((b, slot))
+            touched[b] += 1
+    for b in range(batch):
+        assert np.all(cover[b] == 1), b
+    assert np.array_equal(np.diff(ns), touched)
+    assert ns[0] == 0 and ns[-1] == touched.sum() <= batch + P
+
+
+@pytest.mark.parametrize("L,P", [
+    ([37, 130], 256), ([4096] * 128, 256), ([65536] * 16, 256), ([1, 64, 65, 0, 128, 3000], 7),
+    ([0, 0, 5], 4), ([100] * 9, 1), (list(range(0, 3000, 37)), 64), ([8192, 1024, 5000], 128),
+])
+def test_host_metadata_partition(mla, L, P):
+    meta, ns = mla.get_metadata_host(np.array(L, dtype=np.int32), P)
+    _check_partition(L, P, meta, ns)
+
+
+def test_host_metadata_balance(mla):
+    rng = np.random.default_rng(0)
+    L = rng.integers(1024, 8193, size=128)
+    P = 128
+    meta, ns = mla.get_metadata_host(L.astype(np.int32), P)
+    nb = (L + 63) // 64
+    loads = []
+    for p in range(P):
+        b0, k0, b1, k1 = meta[p, :4]
+        tot = 0
+        for b in range(b0, min(b1, 127) + 1):
+            lo = k0 if b == b0 else 0
+            hi = k1 if b == b1 else nb[b]
+            if hi > lo:
+                tot += hi - lo + 1
+        loads.append(tot)
+    mean = (nb.sum() + len(nb)) / P
+    assert max(loads) <= mean + 2 + 1
