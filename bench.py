@@ -1,0 +1,262 @@
+"""Benchmark: paged MLA decode on one MI355X against the HBM / bf16-MFMA roofline.
+
+One step = one pass of the hot path over one batch: the tile-scheduler metadata, the
+decode kernel (gather, Q.K^T, online softmax, P.V, split epilogue) and the split-KV
+combine, on the memory-bound workload (batch 128, s_q 1, 16 heads, 4096 cached tokens
+each, 8192 pages permuted over the pool).  Inputs are seeded synthetic data resident in
+HBM before timing.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA datasheet (2.5 PFLOP/s)
+D_QK, D_V = 576, 512
+
+
+def paged_counts(inp):
+    """Algorithmic bytes and flops of one paged decode step.
+
+    Bytes: every visible KV row once per sequence (1152 B; V lies inside K), Q, O (bf16),
+    LSE (fp32), the used block-table entries and the sequence lengths.  Flops:
+    2 * (576 + 512) per (query row, visible token)."""
+    L = inp.seqlens.astype(np.int64)
+    b, s_q, h_q = inp.batch, inp.s_q, inp.h_q
+    M = s_q * h_q
+    kv = int(L.sum()) * D_QK * 2
+    nblk = int(((L + 63) // 64).sum())
+    byts = kv + b * M * D_QK * 2 + b * M * D_V * 2 + b * M * 4 + nblk * 4 + b * 4
+    vis = 0
+    for s in range(s_q):
+        if inp.causal:
+            vis += int(np.clip(L - s_q + s + 1, 0, None).sum())
+        else:
+            vis += int(L.sum())
+    flops = 2 * (D_QK + D_V) * h_q * vis
+    return byts, flops
+
+
+def sparse_counts(inp):
+    """Valid index entries read 580 B each (576 fp8 codes + the fp32 scale); plus Q, O, LSE, indices."""
+    valid = int((inp.indices >= 0).sum())
+    b, s_q, h_q = inp.batch, inp.s_q, inp.h_q
+    byts = valid * 580 + inp.indices.size * 4 + b * s_q * h_q * (D_QK * 2 + D_V * 2 + 4)
+    flops = 2 * (D_QK + D_V) * h_q * valid
+    return byts, flops
+
+
+class Flusher:
+    """Reads a 512 MB buffer to evict L2 and the 256 MB Infinity Cache between timed calls
+    (a read leaves clean lines, so the timed call pays no write-back for the flush)."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.sink = self.buf.sum()
+
+
+def time_calls(torch, fn, n, flush=None):
+    """Per-call device time (ms) with events on the current stream; optional flush between calls."""
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return np.array(times)
+
+
+def setup_paged(torch, mla, inp, dev):
+    from tests.helpers import dev_bf16, dev_i32
+
+    q, kc = dev_bf16(inp.q, dev), dev_bf16(inp.kcache, dev)
+    bt, sl = dev_i32(inp.block_table, dev), dev_i32(inp.seqlens, dev)
+    P = mla.num_parts(inp.h_q, inp.s_q)
+    out = torch.empty((inp.batch, inp.s_q, inp.h_q, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    ws = torch.zeros((max(mla.workspace_size(inp.batch, inp.s_q, inp.h_q, P), 256),), dtype=torch.uint8, device=dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
+
+    def decode():
+        mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws)
+
+    def step():
+        m = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
+        mla.decode_paged(q, kc, bt, sl, m, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws)
+
+    return step, decode
+
+
+def setup_sparse(torch, mla, inp, dev):
+    from tests.helpers import dev_bf16, dev_i32, dev_u8
+
+    q, kv, idx = dev_bf16(inp.q, dev), dev_u8(inp.kv, dev), dev_i32(inp.indices, dev)
+    out = torch.empty((inp.batch, inp.s_q, inp.h_q, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    ws = torch.zeros((max(mla.workspace_size_sparse(inp.batch, inp.s_q, inp.h_q, inp.topk), 256),),
+                     dtype=torch.uint8, device=dev)
+
+    def decode():
+        mla.decode_sparse(q, kv, idx, inp.softmax_scale, 0, out=out, lse=lse, workspace=ws)
+
+    return decode, decode
+
+
+def cpu_baseline(inp, kind, counts_fn, budget_s=15.0):
+    """The float64 oracle on a bounded sample of the same workload, scaled to GB/s."""
+    from oracle import paged_decode, sparse_decode
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    total_bytes, _ = counts_fn(inp)
+    t0 = time.perf_counter()
+    done = 0
+    if kind == "paged":
+        per_seq = total_bytes / inp.batch
+        for b in range(inp.batch):
+            paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, inp.causal, batches=[b])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = "%d of %d sequences" % (done, inp.batch)
+        byts = per_seq * done
+    else:
+        sets = [(b, s) for b in range(inp.batch) for s in range(inp.s_q)]
+        per_set = total_bytes / len(sets)
+        for bs in sets:
+            sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale, sets=[bs])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = "%d of %d query tokens" % (done, len(sets))
+        byts = per_set * done
+    dt = time.perf_counter() - t0
+    return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads (flushed, per call)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import head_latent_attention_paged_amd as mla
+    from mla_inputs import CONFIGS, make_config
+
+    dev = torch.device("cuda:0")
+    print("[bench] generating the memory-bound workload", file=sys.stderr, flush=True)
+    inp = make_config(2, poison=False)
+    byts, flops = paged_counts(inp)
+    step, decode = setup_paged(torch, mla, inp, dev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # the decode call (decode kernel + combine) timed with events on the launch stream
+    ev = time_calls(torch, decode, max(args.steps, 20))
+    dec_ms = float(np.mean(ev))
+    achieved = byts / (dec_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "paged MLA decode us/call, achieved HBM GB/s and TFLOPS vs MI355X roofline",
+        "value": round(byts / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[2]["name"], "batch": inp.batch, "s_q": inp.s_q, "h_q": inp.h_q,
+                   "seq_len": int(inp.seqlens[0]), "page": 64, "pages": inp.num_pages,
+                   "parallelism": "single GPU"},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "tflops_per_step": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "algorithmic_bytes": byts,
+        "algorithmic_flops": flops,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_decode_paged call (decode + combine)", "us_per_launch": round(dec_ms * 1e3, 2)},
+    }
+
+    if args.extra:
+        flush = Flusher(torch, dev)
+        extra = {}
+        for k in (2, 3, 4, 5):
+            print("[bench] workload %d" % k, file=sys.stderr, flush=True)
+            ik = inp if k == 2 else make_config(k, poison=False)
+            if CONFIGS[k]["kind"] == "paged":
+                _, fn = setup_paged(torch, mla, ik, dev)
+                b_k, f_k = paged_counts(ik)
+            else:
+                _, fn = setup_sparse(torch, mla, ik, dev)
+                b_k, f_k = sparse_counts(ik)
+            for _ in range(3):
+                fn()
+            t = time_calls(torch, fn, 30, flush=flush)
+            us = float(np.median(t)) * 1e3
+            extra["config%d" % k] = {
+                "workload": CONFIGS[k]["name"], "us_median": round(us, 2),
+                "us_p10": round(float(np.percentile(t, 10)) * 1e3, 2),
+                "us_p90": round(float(np.percentile(t, 90)) * 1e3, 2),
+                "GBps": round(b_k / (us * 1e-6) / 1e9, 1), "TFLOPS": round(f_k / (us * 1e-6) / 1e12, 1),
+                "hbm_frac": round(b_k / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(f_k / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "algorithmic_bytes": b_k, "algorithmic_flops": f_k,
+            }
+            if k != 2:
+                del ik
+                torch.cuda.empty_cache()
+        res["workloads_flushed"] = extra
+
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, "paged", paged_counts)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -34,6 +34,11 @@ constexpr int kRowA = 1024;
 constexpr int kRegionB = kChunk * kRowA;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax with a lagging reference: probabilities are exp2(x - m) with m the row's
+// reference, which only moves when the row maximum exceeds it by more than kSlack, so
+// p <= 2^kSlack and the accumulator is rescaled rarely.  The final O = acc / l and
+// LSE = m + log2(l) use the same reference, so the result is exact up to rounding.
+constexpr float kSlack = 8.f;
 
 // --------------------------------------------------------------------------
 // Small helpers
@@ -55,6 +60,15 @@ __device__ __forceinline__ f4 mfma16(bf16x8 a, bf16x8 b, f4 c) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes land at
+// LDS byte lds_addr + 16*L.  Written as a statement the compiler does not see as an LDS
+// store, so it does not stall reads of the other LDS buffer on this copy; the caller waits
+// with s_waitcnt vmcnt before reading the destination.  No register is written.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_ptr) {
+    const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_ptr;
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+}
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
     bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -346,11 +360,13 @@ void mla_decode_kernel(const AttnArgs a) {
                         tok_ok[tt][i] = tb + tok < t1;
                     }
                 }
-            bf16x8 pT[NT];
+            // scaled, masked scores and their per-row chunk maximum
+            float x[NT][2][4];
+            float mx[NT];
+            bool grow = false;
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                float x[2][4];
-                float mx = -INFINITY;
+                mx[n] = -INFINITY;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -359,28 +375,41 @@ void mla_decode_kernel(const AttnArgs a) {
                         bool valid = tok_ok[tt][i];
                         if constexpr (!SPARSE) valid = valid && (t <= limit[n]);
                         const float f = SPARSE ? a.scale_log2 * tsc[tt][i] : a.scale_log2;
-                        x[tt][i] = valid ? s[tt][n][i] * f : -INFINITY;
-                        mx = fmaxf(mx, x[tt][i]);
+                        x[n][tt][i] = valid ? s[tt][n][i] * f : -INFINITY;
+                        mx[n] = fmaxf(mx[n], x[n][tt][i]);
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[n], mx);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = exp2_fast(m_run[n] - m_use);
+                mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 16));
+                mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 32));
+                grow = grow || (mx[n] > m_run[n] + kSlack);
+            }
+            // the softmax reference of a row only moves when the row's maximum outgrows it by
+            // more than kSlack (log2 units); then the whole wave rescales once.
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const float m_new = fmaxf(m_run[n], mx[n]);
+                    const float alpha = exp2_fast(m_run[n] - (m_new == -INFINITY ? 0.f : m_new));
+                    l_run[n] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) acc[dt][n] *= alpha;
+                    m_run[n] = m_new;
+                }
+            }
+            bf16x8 pT[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
                 float p[2][4];
                 float psum = 0.f;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        p[tt][i] = exp2_fast(x[tt][i] - m_use);
+                        p[tt][i] = exp2_fast(x[n][tt][i] - m_use);
                         psum += p[tt][i];
                         if constexpr (SPARSE) p[tt][i] *= tsc[tt][i];
                     }
-                l_run[n] = l_run[n] * alpha + psum;
-                m_run[n] = m_new;
-#pragma unroll
-                for (int dt = 0; dt < 32; ++dt) acc[dt][n] *= alpha;
+                l_run[n] += psum;
                 // B operand of O^T = V^T P^T: k index 8*g4 + j <-> token j<4 ? 4*g4+j : 16+4*g4+(j-4)
                 const uint4 pk = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                                             pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
@@ -542,6 +571,232 @@ void mla_decode_kernel(const AttnArgs a) {
         const int e1 = min(e0 + a.split_len, a.topk);
         if (e0 < e1)
             run_segment(grp, e0, e1, 0, a.num_parts == 1, grp * a.num_parts + split);
+    }
+}
+
+// --------------------------------------------------------------------------
+// K1m: paged decode for one 16-row tile (s_q * h_q <= 16), the memory-bound shape.
+// Four independent token streams per block (one per wave, one wave per SIMD).  Each stream
+// double-buffers 16-token chunks (18 KB) that go HBM -> LDS by direct copies, so one chunk is
+// always in flight while the previous one is multiplied; the streams merge at the end.
+// --------------------------------------------------------------------------
+constexpr int kMChunk = 16;
+constexpr int kMBuf = kMChunk * kRowA + kMChunk * 128;      // 18 KB: region A then region B
+constexpr int kMRegionB = kMChunk * kRowA;
+constexpr int kMDmaOps = kMChunk + 2;                        // copy instructions per chunk and wave
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_m16_kernel(const AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[4 * 2 * kMBuf];   // 144 KB
+    const int lane = threadIdx.x & 63;
+    const int ts = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // stream = wave
+    const int g4 = lane >> 4, l16 = lane & 15;
+    char* bufs = smem + ts * 2 * kMBuf;
+    const int item = blockIdx.x;
+
+    // K fragment (A operand of S^T): token row l16, granule 4*ks + g4
+    int kA[2], kB[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        kA[par] = l16 * kRowA + (((4 * par + g4) ^ swz(l16)) << 4);
+        kB[par] = kMRegionB + l16 * 128 + (((4 * par + g4) ^ swz(l16)) << 4);
+    }
+    // V^T fragment (A operand of O^T, 16x16x16): tokens 4*g4..+3, dims 16*dt + l16 via one
+    // transposing read; lane supplies row 4*g4 + l16/4, dims 16*dt + 4*(l16&3)..+3
+    int vb[4];
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) {
+        const int row = 4 * g4 + (l16 >> 2);
+        vb[d4] = lds_a(row, 2 * d4 + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+    }
+
+    bf16x8 qf[18];
+    f4 acc[32];
+    float m_run, l_run;
+
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
+        const int r = l16;
+        {
+            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (r < a.M ? r : 0)) * (kDqk * 2);
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
+                if (r >= a.M) v = make_uint4(0, 0, 0, 0);
+                qf[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+        const int limit = a.causal ? (L - a.s_q + r / a.h_q) : (L - 1);
+        const int nch = ceil_div(t1 - t0, kMChunk);
+
+        // Wave ts handles chunks c = ts + 4k: rows 16*ts..16*ts+15 of page lo + k.  The page
+        // numbers come 64 at a time from one vector load of the block table.
+        const int lo_page = t0 >> 6;
+        int bt_win = 0, bt_base = -1000000;
+        auto page_of = [&](int k) {
+            if (k - bt_base >= 64 || k < bt_base) {
+                bt_base = k;
+                const int np = ceil_div(t1, kPage) - lo_page;
+                bt_win = (lane < np - k) ? a.block_table[(size_t)grp * a.max_blocks + lo_page + k + lane] : 0;
+            }
+            return __builtin_amdgcn_readlane(bt_win, k - bt_base);
+        };
+        // copy chunk c = ts + 4k (16 rows of one page, contiguous in HBM) into buffer b
+        auto issue = [&](int k, int b) {
+            const int c = ts + 4 * k;
+            const int tb = t0 + c * kMChunk;
+            const int nrows = min(kMChunk, t1 - tb);
+            const int page = page_of(k);
+            const char* base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+            char* dst = bufs + b * kMBuf;
+#pragma unroll
+            for (int row = 0; row < kMChunk; ++row) {
+                const int rr = min(row, nrows - 1);   // rows past the end repeat the last row (weight 0)
+                dma16(base + rr * kRowBytes + ((lane ^ swz(row)) << 4), dst + row * kRowA);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int sl = j * 64 + lane;
+                const int row = sl >> 3;
+                const int rr = min(row, nrows - 1);
+                dma16(base + rr * kRowBytes + (64 + ((sl & 7) ^ swz(row))) * 16, dst + kMRegionB + j * 1024);
+            }
+        };
+
+        if (ts < nch) {
+            issue(0, 0);
+        }
+        int k = 0;
+        for (int c = ts; c < nch; c += 4, ++k) {
+            const char* buf = bufs + (k & 1) * kMBuf;
+            if (c + 4 < nch) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the other buffer done
+                issue(k + 1, (k + 1) & 1);
+                asm volatile("s_waitcnt vmcnt(18)" ::: "memory");    // chunk c landed, c+4 in flight
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            const int tb = t0 + c * kMChunk;
+            // S^T[token][row] over 576 dims: two accumulators (even / odd k steps) break the chain
+            f4 sacc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                const int off = ks < 16 ? kA[ks & 1] + 128 * (ks >> 1) : kB[ks & 1];
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + off);
+                sacc[ks & 1] = mfma16(kf, qf[ks], sacc[ks & 1]);
+            }
+            const f4 sv = sacc[0] + sacc[1];
+            float x[4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb + 4 * g4 + i;
+                x[i] = (t < t1 && t <= limit) ? sv[i] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, x[i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.f : m_new));
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = exp2_fast(x[i] - m_use);
+                l_run += p[i];
+            }
+            // P^T (B operand, k = tokens 4*g4..+3, n = row l16) is the S^T accumulator layout
+            const short4v pT = __builtin_bit_cast(short4v, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) {
+                const short4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4v*)(buf + vb[dt & 3] + 128 * (dt >> 2)));
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pT, acc[dt], 0, 0, 0);
+            }
+        }
+
+        // row sums, merge the 4 streams (stream 0 keeps the result), write
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        f4* macc = reinterpret_cast<f4*>(smem);
+        float* mml = reinterpret_cast<float*>(smem + 3 * 32 * 64 * 16);
+        __syncthreads();
+        if (ts > 0) {
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) macc[((ts - 1) * 32 + dt) * 64 + lane] = acc[dt];
+            mml[((ts - 1) * 64 + lane) * 2 + 0] = m_run;
+            mml[((ts - 1) * 64 + lane) * 2 + 1] = l_run;
+        }
+        __syncthreads();
+        if (ts == 0) {
+            float mk[4], lk[4];
+            mk[0] = m_run;
+            lk[0] = l_run;
+            float m_new = m_run;
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                mk[w] = mml[((w - 1) * 64 + lane) * 2 + 0];
+                lk[w] = mml[((w - 1) * 64 + lane) * 2 + 1];
+                m_new = fmaxf(m_new, mk[w]);
+            }
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            float al[4], l_new = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                al[w] = exp2_fast(mk[w] - m_use);
+                l_new += al[w] * lk[w];
+            }
+            const float inv = l_new > 0.f ? 1.f / l_new : 0.f;
+            const float lse_v = l_new > 0.f ? (m_new + __log2f(l_new)) * kLn2 : -INFINITY;
+            if (r < a.M) {
+                if (final_out) {
+                    __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + r) * kDv + 4 * g4;
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) {
+                        f4 v = acc[dt] * al[0];
+#pragma unroll
+                        for (int w = 1; w < 4; ++w) v += macc[((w - 1) * 32 + dt) * 64 + lane] * al[w];
+                        v *= inv;
+                        *reinterpret_cast<uint2*>(orow + dt * 16) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    }
+                    if (g4 == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
+                } else {
+                    float* prow = a.part_o + ((size_t)slot * a.M + r) * kDv + 4 * g4;
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) {
+                        f4 v = acc[dt] * al[0];
+#pragma unroll
+                        for (int w = 1; w < 4; ++w) v += macc[((w - 1) * 32 + dt) * 64 + lane] * al[w];
+                        *reinterpret_cast<f4*>(prow + dt * 16) = v * inv;
+                    }
+                    if (g4 == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    const int* meta = a.tile_meta + (size_t)item * kMetaInts;
+    const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
+    for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
+        const int L = a.seqlens[bb];
+        const int nb = ceil_div(L, kPage);
+        const int lo = (bb == b0) ? blk0 : 0;
+        const int hi = (bb == b1) ? blk1 : nb;
+        if (lo >= hi) continue;
+        const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
+        const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
+        run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
     }
 }
 
@@ -721,6 +976,10 @@ static hipError_t launch_decode_t(const AttnArgs& a, int items, int R, hipStream
 
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const Tiling t = choose_tiling(a.M);
+    if (!sparse && a.M <= 16) {
+        hipLaunchKernelGGL(mla_decode_m16_kernel, dim3(a.num_parts), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = t.row_groups;
 #define MLA_DISPATCH(NT_, RW_)                                                     \
