@@ -13,7 +13,7 @@ constexpr int kPage = 64;            // tokens per page
 constexpr int kRec = 640;            // bytes per sparse fp8 record
 constexpr int kChunk = 32;           // tokens per kernel chunk
 constexpr int kMetaInts = 8;
-constexpr int kMetaOverheadBlocks = 1;   // per-sequence fixed cost, in 64-token blocks
+constexpr int kMetaOverheadBlocks = 0;   // per-sequence fixed cost, in 64-token blocks
 constexpr int kMaxBatchMeta = 16384;
 constexpr int kMaxRows = 4096;       // s_q * h_q limit
 constexpr int kSparseTargetItems = 1024;  // work items the sparse split count aims for

@@ -75,9 +75,9 @@ int mla_num_parts(int num_cus, int h_q, int s_q);
  *   tile_meta     [device] int32[num_parts * MLA_META_INTS]  (out)
  *   num_splits    [device] int32[batch + 1]                  (out)
  *
- * Work is counted in 64-token blocks plus a fixed per-sequence overhead and
- * cut into num_parts contiguous, equally sized ranges of the flattened
- * (sequence, block) order; a sequence crossing a range edge is split.
+ * Work is counted in 64-token blocks and cut into num_parts contiguous,
+ * equally sized ranges of the flattened (sequence, block) order; a sequence
+ * crossing a range edge is split.
  * num_splits is the exclusive prefix sum of the number of parts touching
  * each sequence (num_splits[b+1] - num_splits[b] = splits of sequence b);
  * it indexes the partial results in the workspace.  tile_meta[p] holds
