@@ -17,12 +17,13 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mla_kernels.hip", "mla_api.cpp"]
+SOURCES = ["mla_kernels.hip", "mla_decode_big.hip", "mla_api.cpp"]
 
 
 def hipcc_cmd(out: str = LIB):
     return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
             "-Rpass-analysis=kernel-resource-usage",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]

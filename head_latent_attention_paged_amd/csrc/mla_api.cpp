@@ -25,13 +25,15 @@ int sparse_effective_splits(int topk, int splits) {
     return (topk + len - 1) / len;
 }
 
+int sparse_min_splits(int topk) { return (topk + mla::kMaxSparseSplit - 1) / mla::kMaxSparseSplit; }
+
 int sparse_auto_splits(int batch, int s_q, int h_q, int topk) {
     const long long sets = (long long)batch * s_q;
     const Tiling t = mla::choose_tiling(h_q);
     const long long per_set = sets * t.row_groups;
     long long want = (mla::kSparseTargetItems + per_set - 1) / per_set;
     const int max_splits = (topk + mla::kChunk - 1) / mla::kChunk;
-    if (want < 1) want = 1;
+    if (want < sparse_min_splits(topk)) want = sparse_min_splits(topk);
     if (want > max_splits) want = max_splits;
     return (int)want;
 }
@@ -87,6 +89,7 @@ size_t mla_workspace_size_sparse(int batch, int s_q, int h_q, int topk, int spli
     if (splits <= 0) splits = sparse_auto_splits(batch, s_q, h_q, topk);
     const int max_splits = (topk + mla::kChunk - 1) / mla::kChunk;
     if (splits > max_splits) splits = max_splits;
+    if (splits < sparse_min_splits(topk)) splits = sparse_min_splits(topk);
     const int eff = sparse_effective_splits(topk, splits);
     if (eff <= 1) return 0;
     return partial_bytes((long long)batch * s_q * eff, h_q);
@@ -187,6 +190,7 @@ mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens
     int req = splits > 0 ? splits : sparse_auto_splits(batch, s_q, h_q, topk);
     const int max_splits = (topk + mla::kChunk - 1) / mla::kChunk;
     if (req > max_splits) req = max_splits;
+    if (req < sparse_min_splits(topk)) req = sparse_min_splits(topk);
     const int eff = sparse_effective_splits(topk, req);
     const size_t need = mla_workspace_size_sparse(batch, s_q, h_q, topk, req);
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;

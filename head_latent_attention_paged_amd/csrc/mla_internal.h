@@ -16,7 +16,13 @@ constexpr int kMetaInts = 8;
 constexpr int kMetaOverheadBlocks = 0;   // per-sequence fixed cost, in 64-token blocks
 constexpr int kMaxBatchMeta = 16384;
 constexpr int kMaxRows = 4096;       // s_q * h_q limit
-constexpr int kSparseTargetItems = 1024;  // work items the sparse split count aims for
+constexpr int kSparseTargetItems = 256;   // work items (one per compute unit) sparse splitting aims for
+constexpr int kMaxSparseSplit = 2048;     // index entries one sparse split may hold
+
+// Wave pairs (32 query rows each) per workgroup of the large-row decode kernel, used for
+// s_q*h_q (paged) or h_q (sparse) above 16 rows: one pair (and two token streams) up to 32
+// rows, two pairs (64 rows per workgroup) beyond.
+inline __host__ __device__ int big_pairs(int rows) { return rows <= 32 ? 1 : 2; }
 
 // Row tiling of one sequence's s_q*h_q query rows.  A workgroup holds 4 waves:
 // `rw` of them split the rows (16*nt rows each), the other factor 4/rw splits
@@ -56,6 +62,7 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts,
 void metadata_host(const int32_t* seqlens, int batch, int num_parts,
                    int32_t* tile_meta, int32_t* num_splits);
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream);
+hipError_t launch_decode_big(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream);

@@ -12,85 +12,9 @@
 // then directly the B operand of O^T = V^T P^T, and only V needs a transposed LDS read
 // (ds_read_b64_tr_b16).  Everything else (chunking, LDS layout, XCD mapping, splits) is
 // designed for CDNA4 here and not taken from the pages.
-#include "mla_internal.h"
-
-#include <cmath>
+#include "mla_device.h"
 
 namespace mla {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4v;
-
-constexpr int kRowBytes = kDqk * 2;       // 1152: one bf16 row in HBM
-constexpr int kChunkBytes = kChunk * kRowBytes;
-// LDS chunk layout: region A holds dims 0..511 of the 32 rows (1024 B per row), region B the
-// 64 RoPE dims (128 B per row), so each region can be filled by whole-wave 1 KB writes.
-constexpr int kRowA = 1024;
-constexpr int kRegionB = kChunk * kRowA;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-// Online softmax with a lagging reference: probabilities are exp2(x - m) with m the row's
-// reference, which only moves when the row maximum exceeds it by more than kSlack, so
-// p <= 2^kSlack and the accumulator is rescaled rarely.  The final O = acc / l and
-// LSE = m + log2(l) use the same reference, so the result is exact up to rounding.
-constexpr float kSlack = 8.f;
-
-// --------------------------------------------------------------------------
-// Small helpers
-// --------------------------------------------------------------------------
-__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-// LDS row layout: row r holds 72 granules of 16 B (8 dims each); granule c sits at slot
-// c ^ swz(r).  swz permutes within aligned groups of 8 granules so that (a) 8 consecutive
-// rows reading the same granule (QK^T A operand, ds_read_b128) hit 8 distinct 16-B bank
-// groups and (b) 4 consecutive rows reading the same 32-B pair (V^T transposed read) hit 4
-// distinct 32-B bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-// granule c (0..63) of row r in region A; granule c (0..7) of row r in region B
-__device__ __forceinline__ int lds_a(int r, int c) { return r * kRowA + ((c ^ swz(r)) << 4); }
-__device__ __forceinline__ int lds_b(int r, int c) { return kRegionB + r * 128 + ((c ^ swz(r)) << 4); }
-
-__device__ __forceinline__ f4 mfma16(bf16x8 a, bf16x8 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes land at
-// LDS byte lds_addr + 16*L.  Written as a statement the compiler does not see as an LDS
-// store, so it does not stall reads of the other LDS buffer on this copy; the caller waits
-// with s_waitcnt vmcnt before reading the destination.  No register is written.  The KV
-// cache is streamed once per call, so the copy is nontemporal (nt): measured on MI355X it
-// lifts a random-page 604 MB stream from about 5.8 to 6.9 TB/s.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds_ptr) {
-    const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_ptr;
-    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
-}
-
-// Nontemporal 16-byte load of streamed KV data into registers.
-__device__ __forceinline__ uint4 load_nt(const void* p) {
-    typedef unsigned u4v __attribute__((ext_vector_type(4)));
-    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
-    return make_uint4(t[0], t[1], t[2], t[3]);
-}
-
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-    bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(unsigned, v);
-}
-
-// 16 e4m3 codes -> 16 bf16 (exact: every finite e4m3 value is a bf16 value)
-__device__ __forceinline__ void fp8x16_to_bf16(uint4 c, uint4& lo, uint4& hi) {
-#define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))
-    lo = make_uint4(MLA_CVT(c.x, false), MLA_CVT(c.x, true), MLA_CVT(c.y, false), MLA_CVT(c.y, true));
-    hi = make_uint4(MLA_CVT(c.z, false), MLA_CVT(c.z, true), MLA_CVT(c.w, false), MLA_CVT(c.w, true));
-#undef MLA_CVT
-}
 
 // --------------------------------------------------------------------------
 // K1: decode kernel
@@ -592,6 +516,7 @@ constexpr int kMDmaOps = kMChunk + 2;                        // copy instruction
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_m16_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[4 * 2 * kMBuf];   // 144 KB
+    __shared__ int s_pages[4][64];                                       // per-wave page window
     const int lane = threadIdx.x & 63;
     const int ts = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // stream = wave
     const int g4 = lane >> 4, l16 = lane & 15;
@@ -637,16 +562,19 @@ void mla_decode_m16_kernel(const AttnArgs a) {
         const int nch = ceil_div(t1 - t0, kMChunk);
 
         // Wave ts handles chunks c = ts + 4k: rows 16*ts..16*ts+15 of page lo + k.  The page
-        // numbers come 64 at a time from one vector load of the block table.
+        // numbers come 64 at a time into a per-wave LDS window, so looking one up never waits
+        // on the vector-memory counter (which also counts the in-flight KV copies).
         const int lo_page = t0 >> 6;
-        int bt_win = 0, bt_base = -1000000;
+        int bt_base = -1000000;
         auto page_of = [&](int k) {
             if (k - bt_base >= 64 || k < bt_base) {
                 bt_base = k;
                 const int np = ceil_div(t1, kPage) - lo_page;
-                bt_win = (lane < np - k) ? a.block_table[(size_t)grp * a.max_blocks + lo_page + k + lane] : 0;
+                const int v = (lane < np - k) ? a.block_table[(size_t)grp * a.max_blocks + lo_page + k + lane] : 0;
+                s_pages[ts][lane] = v;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
-            return __builtin_amdgcn_readlane(bt_win, k - bt_base);
+            return __builtin_amdgcn_readfirstlane(s_pages[ts][k - bt_base]);
         };
         // copy chunk c = ts + 4k (16 rows of one page, contiguous in HBM) into buffer b
         auto issue = [&](int k, int b) {
@@ -957,9 +885,16 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
 // Launchers
 // --------------------------------------------------------------------------
 Tiling choose_tiling(int rows) {
+    // <= 16 rows: one 16-row tile per workgroup (mla_decode_m16_kernel, or the 16-row sparse
+    // kernel); more rows: 32-row waves of mla_decode_big_kernel.
     Tiling t;
-    t.nt = 1;
-    t.rw = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    if (rows <= 16) {
+        t.nt = 1;
+        t.rw = 1;
+    } else {
+        t.nt = 2;
+        t.rw = big_pairs(rows);
+    }
     t.rows_wg = 16 * t.nt * t.rw;
     t.row_groups = (rows + t.rows_wg - 1) / t.rows_wg;
     return t;
@@ -984,6 +919,7 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
         hipLaunchKernelGGL(mla_decode_m16_kernel, dim3(a.num_parts), dim3(256), 0, stream, a);
         return hipGetLastError();
     }
+    if (a.M > 16) return launch_decode_big(a, sparse, stream);
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = t.row_groups;
 #define MLA_DISPATCH(NT_, RW_)                                                     \
@@ -991,8 +927,6 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
         return sparse ? launch_decode_t<NT_, RW_, true>(a, items, R, stream)       \
                       : launch_decode_t<NT_, RW_, false>(a, items, R, stream);
     MLA_DISPATCH(1, 1)
-    MLA_DISPATCH(1, 2)
-    MLA_DISPATCH(1, 4)
 #undef MLA_DISPATCH
     return hipErrorInvalidValue;
 }

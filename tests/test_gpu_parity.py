@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from mla_inputs import make_config, make_paged, make_sparse
+from mla_inputs.gen import bf16_bits_from_f32, bf16_bits_to_f32
 from oracle import paged_decode, sparse_decode
 from tests.helpers import check_parity, dev_bf16, dev_i32, dev_u8, to_host
 
@@ -168,6 +169,63 @@ def test_sparse_all_skipped_and_duplicates(env):
         o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
         check_parity(o, l, o_ref, l_ref, "skip/dup splits=%d" % splits)
         assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
+
+
+# ----------------------------------------------------------------- wide score ranges
+def _ramp(inp, top, seed=7):
+    """Scores that move linearly along each sequence, from ~0 to ~`top` nats (top < 0: falling
+    from ~|top| to ~0).  Rising scores keep outgrowing the softmax reference the kernels hold;
+    falling ones drive later probabilities far below the first chunk's."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(576)
+    u /= np.linalg.norm(u)
+    sigma_inv = 1.0 / inp.softmax_scale
+    qf = u * sigma_inv + 0.02 * sigma_inv * rng.standard_normal(inp.q.shape)
+    inp.q = bf16_bits_from_f32(qf.astype(np.float32))
+    kc = bf16_bits_to_f32(inp.kcache).astype(np.float64)
+    for b, L in enumerate(inp.seqlens):
+        for t in range(int(L)):
+            f = (t + 1) / L if top > 0 else (L - t) / L
+            kc[inp.block_table[b, t // 64], t % 64, 0, :] = abs(top) * f * u + 0.5 * rng.standard_normal(576)
+    inp.kcache = bf16_bits_from_f32(kc.astype(np.float32))
+    return inp
+
+
+RAMP_CASES = [
+    # batch, s_q, h_q, seqlens, causal, top (nats), num_parts
+    (2, 1, 16, [1500, 700], False, 150.0, None),
+    (2, 1, 16, [1500, 700], False, -150.0, None),
+    (2, 1, 64, [1500, 700], False, 150.0, None),
+    (2, 1, 64, [1500, 700], False, -150.0, None),
+    (2, 1, 32, [1200, 333], False, 150.0, 8),
+    (1, 2, 128, [2000], True, 120.0, None),
+    (2, 2, 64, [900, 1300], True, 150.0, 16),
+]
+
+
+@pytest.mark.parametrize("case", RAMP_CASES, ids=[str(i) for i in range(len(RAMP_CASES))])
+def test_paged_wide_score_range(env, case):
+    batch, s_q, h_q, L, causal, top, P = case
+    _say("paged ramp case", case)
+    inp = _ramp(make_paged(batch, s_q, h_q, L, causal, seed=300 + h_q, poison=True), top)
+    o, l = run_paged(env, inp, P)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
+    check_parity(o, l, o_ref, l_ref, "ramp " + str(case))
+
+
+@pytest.mark.parametrize("h_q,scale", [(16, 2.5), (64, 2.5), (16, 0.7), (64, 0.7)])
+def test_large_softmax_scale(env, h_q, scale):
+    """Scores with a spread of tens to hundreds of nats on random data, paged and sparse."""
+    _say("large scale", h_q, scale)
+    inp = make_paged(2, 1, h_q, [1800, 900], False, seed=400 + h_q, poison=True, softmax_scale=scale)
+    o, l = run_paged(env, inp)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    check_parity(o, l, o_ref, l_ref, "paged scale %g h_q %d" % (scale, h_q))
+    sp = make_sparse(2, 1, h_q, 2048, 1024, 0.05, seed=500 + h_q, softmax_scale=scale)
+    for splits in (0, 1):
+        o, l = run_sparse(env, sp, splits)
+        o_ref, l_ref = sparse_decode(sp.q, sp.kv, sp.indices, sp.softmax_scale)
+        check_parity(o, l, o_ref, l_ref, "sparse scale %g h_q %d splits %d" % (scale, h_q, splits))
 
 
 # ----------------------------------------------------------------- full-size workloads
