@@ -59,6 +59,64 @@ def sparse_counts(inp):
     return byts, flops
 
 
+CSRC = os.path.join(ROOT, "head_latent_attention_paged_amd", "csrc")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_paged_membound_b128_L4096_hbm_traffic.txt")
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources (csrc/*), to tell whether a stored counter profile still
+    describes the kernels being run."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(path=TRAFFIC_PROFILE):
+    """HBM bytes per decode call from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    each counter divided by what it read for a plain copy kernel of known size.  None when
+    the summary is missing or was taken on other kernel sources."""
+    if not os.path.exists(path):
+        return None, "no counter profile"
+    kv = {}
+    kernels = []
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            key, val = line.split(":", 1)
+            key, val = key.strip(), val.strip()
+            if key == "kernel":
+                fields = dict(x.split("=") for x in val.split()[1:])
+                kernels.append((val.split()[0], float(fields["fetch_kib"]), float(fields["write_kib"])))
+            else:
+                kv[key] = val
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    copy_bytes = float(kv["copy_bytes_each_way"])
+    f_fetch = float(kv["copy_fetch_kib"]) * 1024 / copy_bytes
+    f_write = float(kv["copy_write_kib"]) * 1024 / copy_bytes
+    total = sum(fk * 1024 / f_fetch + wk * 1024 / f_write for _, fk, wk in kernels)
+    return int(total), "rocprofv3 FETCH_SIZE+WRITE_SIZE of %s, scaled by copy-kernel factors %.3f / %.3f" % (
+        "+".join(k for k, _, _ in kernels), f_fetch, f_write)
+
+
+def copy_probe(nbytes=1 << 30, reps=5):
+    """A plain copy kernel of known size (reads and writes nbytes each), for counter calibration."""
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    print("copy probe: %d bytes each way x %d" % (nbytes, reps))
+
+
 class Flusher:
     """Reads a 512 MB buffer to evict L2 and the 256 MB Infinity Cache between timed calls
     (a read leaves clean lines, so the timed call pays no write-back for the flush)."""
@@ -85,6 +143,20 @@ def time_calls(torch, fn, n, flush=None):
         e1.synchronize()
         times.append(e0.elapsed_time(e1))
     return np.array(times)
+
+
+def time_back_to_back(torch, fn, n):
+    """Mean device time (ms) per call of n back-to-back calls between two events on the current
+    stream: the kernels' own durations plus the gaps between consecutive launches."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def setup_paged(torch, mla, inp, dev):
@@ -123,8 +195,10 @@ def setup_sparse(torch, mla, inp, dev):
     return decode, decode
 
 
-def cpu_baseline(inp, kind, counts_fn, budget_s=15.0):
-    """The float64 oracle on a bounded sample of the same workload, scaled to GB/s."""
+def cpu_baseline(inp, kind, counts_fn, min_s=10.0, max_s=30.0):
+    """The float64 oracle on a bounded sample of the same workload, scaled to GB/s: whole
+    sequences (paged) or query tokens (sparse) in order, repeating the workload when one pass
+    takes under min_s, stopping at max_s."""
     from oracle import paged_decode, sparse_decode
 
     try:
@@ -133,28 +207,32 @@ def cpu_baseline(inp, kind, counts_fn, budget_s=15.0):
     except Exception:  # pragma: no cover
         threads = 1
     total_bytes, _ = counts_fn(inp)
+    if kind == "paged":
+        units = list(range(inp.batch))
+        what = "sequences"
+
+        def run(b):
+            paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, inp.causal, batches=[b])
+    else:
+        units = [(b, s) for b in range(inp.batch) for s in range(inp.s_q)]
+        what = "query tokens"
+
+        def run(bs):
+            sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale, sets=[bs])
+    per_unit = total_bytes / len(units)
     t0 = time.perf_counter()
     done = 0
-    if kind == "paged":
-        per_seq = total_bytes / inp.batch
-        for b in range(inp.batch):
-            paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, inp.causal, batches=[b])
+    while True:
+        for u in units:
+            run(u)
             done += 1
-            if time.perf_counter() - t0 > budget_s:
+            dt = time.perf_counter() - t0
+            if dt > max_s:
                 break
-        sample = "%d of %d sequences" % (done, inp.batch)
-        byts = per_seq * done
-    else:
-        sets = [(b, s) for b in range(inp.batch) for s in range(inp.s_q)]
-        per_set = total_bytes / len(sets)
-        for bs in sets:
-            sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale, sets=[bs])
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        sample = "%d of %d query tokens" % (done, len(sets))
-        byts = per_set * done
-    dt = time.perf_counter() - t0
+        if dt > min_s:
+            break
+    byts = per_unit * done
+    sample = "%d %s of the %d in the workload (%.2f passes), in order" % (done, what, len(units), done / len(units))
     return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
 
@@ -166,7 +244,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads (flushed, per call)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB copy kernel (HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
@@ -192,10 +275,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # the decode call (decode kernel + combine) timed with events on the launch stream
-    ev = time_calls(torch, decode, max(args.steps, 20))
-    dec_ms = float(np.mean(ev))
+    # the decode call (decode kernel + combine) timed with events on the stream it launches on
+    dec_ms = time_back_to_back(torch, decode, max(args.steps, 20))
     achieved = byts / (dec_ms * 1e-3) / 1e9
+    traffic, traffic_note = traffic_from_profile()
 
     res = {
         "metric": "paged MLA decode us/call, achieved HBM GB/s and TFLOPS vs MI355X roofline",
@@ -218,8 +301,10 @@ def main():
         "algorithmic_bytes": byts,
         "algorithmic_flops": flops,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "mla_decode_paged call (decode + combine)", "us_per_launch": round(dec_ms * 1e3, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_note": traffic_note, "algorithmic_bytes_per_launch": byts,
+                     "kernel": "mla_decode_paged call (mla_decode_m16_kernel + mla_combine_kernel)",
+                     "us_per_launch": round(dec_ms * 1e3, 2)},
     }
 
     if args.extra:
