@@ -2,13 +2,16 @@
 //
 // Each wave owns 32 query rows (two 16-row MFMA tiles), so every K or V^T fragment read
 // from LDS feeds two 16x16x32 bf16 MFMAs; the waves of a workgroup cover its rows and share
-// one stream of 32-token KV chunks.  Chunks travel HBM -> LDS by direct nontemporal copies into
-// a ring of DEPTH buffers, DEPTH-1 chunks ahead of the one being multiplied, with one
-// workgroup barrier per chunk.  The math per chunk is the same as in the other decode
-// kernels: S^T = K Q^T with tokens on the MFMA M side ("FlashMLA-ETAP: Efficient Transpose
-// Attention Pipeline ...", section 방법론 / 핵심 메커니즘, transposed form), a lagging-
-// reference online softmax, O^T += V^T P^T with P^T taken straight from the S^T
-// accumulators.
+// one stream of 32-token KV chunks.  Chunks travel HBM -> LDS by direct copies into a ring of
+// DEPTH buffers.  The math per chunk is the same as in the other decode kernels: S^T = K Q^T
+// with tokens on the MFMA M side ("FlashMLA-ETAP: Efficient Transpose Attention Pipeline ...",
+// section 핵심 메커니즘, transposed form), online softmax, O^T += V^T P^T with P^T taken
+// straight from the S^T accumulators.
+//
+// With two wave pairs per workgroup (64 rows) the chunk loop is software-pipelined so that one
+// wave per SIMD keeps its MFMA pipe busy: iteration k multiplies S^T(k) while it turns S^T(k-1)
+// into probabilities and issues the copies of a later chunk, then (after one barrier) multiplies
+// O^T += V^T(k-1) P^T(k-1) while it masks S^T(k) and takes its row maxima.
 //
 // Sparse fp8: a chunk is 32 gathered records ("deepseek-ai/FlashMLA" project summary,
 // section 기술적 세부 사항: fp8 values plus a per-token scale, -1 = unused index).  The raw
@@ -17,10 +20,14 @@
 // scale multiplies the token's score and its probability before P.V.
 #include "mla_device.h"
 
+#include <type_traits>
+
 namespace mla {
 
-// fp8 record rows in LDS: 40 slots of 16 B (granules 0..35 hold codes, 36 the scale) with an
-// XOR on the low granule bits that also separates rows r and r+16.
+// fp8 record rows in LDS: 40 slots of 16 B (granules 0..35 hold codes, 36 the scale, 37..39
+// padding), slot s holding granule s ^ swz8(r), an XOR on the low granule bits that also
+// separates rows r and r+16.  The rows of a chunk are contiguous, so one 64-lane copy fills
+// 1 KB of it (parts of two rows) and a chunk takes 20 copies with every lane active.
 constexpr int kRec8Row = 640;
 constexpr int kPF = 4;       // LDS fragment prefetch distance (MFMA steps)
 // The softmax reference of a row is the first finite chunk maximum it sees and never moves
@@ -31,9 +38,8 @@ constexpr int kPF = 4;       // LDS fragment prefetch distance (MFMA steps)
 constexpr float kRefSlack = 64.f;
 __device__ __forceinline__ int swz8(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ ((r >> 4) & 1); }
 
-// An all-zero record: unused index entries and rows past a split's end are copied from it,
-// so every row of a chunk costs exactly one copy (exact s_waitcnt accounting) and its
-// (zero-weight) V row is finite.
+// An all-zero record: unused index entries are copied from it, so a chunk always costs the same
+// copies (exact s_waitcnt accounting) and its zero-weight V rows are finite.
 __device__ __attribute__((aligned(16))) const unsigned char kZeroRecord[kRec8Row] = {0};
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exact
@@ -52,21 +58,25 @@ template <bool SPARSE, int PAIRS>
 struct BigCfg {
     static constexpr int WAVES = 2 * PAIRS;
     static constexpr int ROWS_WG = 32 * PAIRS;
+    static constexpr bool PIPELINED = PAIRS == 2;
     static constexpr int BUF = SPARSE ? kChunk * kRec8Row : kChunkBytes;
-    // ring depth: two pairs fill a compute unit alone; one pair leaves room for a second block
+    // ring slots.  Pipelined: chunk k-1 (P.V), k (Q.K^T) and DEPTH-2 chunks in flight.  Serial
+    // (one pair, leaving room for a second workgroup per CU): DEPTH-1 chunks in flight.
     static constexpr int DEPTH = PAIRS == 2 ? (SPARSE ? 6 : 4) : (SPARSE ? 3 : 2);
     static constexpr int RING = DEPTH * BUF;
-    static constexpr int OPS = (SPARSE ? kChunk : kChunk + 4) / WAVES;  // copies per wave per chunk
+    // copies per wave per chunk: bf16 32 rows of region A + 4 KB of region B; fp8 20 KB
+    static constexpr int OPS = (SPARSE ? kChunk * kRec8Row / 1024 : kChunk + 4) / WAVES;
     static constexpr int MAIN = RING;
     static constexpr int XCH = WAVES * 2 * 16 * 4;                     // row maxima / sums [wave][n][row]
     static constexpr int PEX = WAVES * 2 * 64 * 8;                     // P^T halves [wave][n][lane]
     static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;       // a split's index list
     static constexpr int PAGES = SPARSE ? 0 : WAVES * 64 * 4;            // per-wave page windows
     static constexpr int FLAGS = 64;                                     // per-wave restart votes
-    static constexpr int LDS = MAIN + XCH + PEX + IDX + PAGES + FLAGS;
+    static constexpr int SINK = WAVES * 64 * 4;                         // targets of masked-off lanes
+    static constexpr int LDS = MAIN + XCH + PEX + IDX + PAGES + FLAGS + SINK;
 };
 
-template <bool SPARSE, int PAIRS>
+template <bool SPARSE, int PAIRS, bool SHARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_big_kernel(const AttnArgs a) {
     using C = BigCfg<SPARSE, PAIRS>;
@@ -78,6 +88,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
     int* lidx = reinterpret_cast<int*>(smem + C::MAIN + C::XCH + C::PEX);
     int* lpages = reinterpret_cast<int*>(smem + C::MAIN + C::XCH + C::PEX + C::IDX);
     int* votes = reinterpret_cast<int*>(smem + C::MAIN + C::XCH + C::PEX + C::IDX + C::PAGES);
+    float* sink = reinterpret_cast<float*>(smem + C::MAIN + C::XCH + C::PEX + C::IDX + C::PAGES + C::FLAGS);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -86,6 +97,8 @@ void mla_decode_big_kernel(const AttnArgs a) {
     const int partner = wave ^ 1;
     const int g4 = lane >> 4, l16 = lane & 15;
     char* ring = smem;
+    // lanes that must not store write their own word of the sink instead (no branch)
+    float* my_sink = sink + wave * 64 + lane;
 
     // ---- work item -> (part or sparse split, row group); row groups of one item share an XCD
     const int R = ceil_div(a.M, C::ROWS_WG);
@@ -103,13 +116,21 @@ void mla_decode_big_kernel(const AttnArgs a) {
         }
     }
     const int rbase = rg * C::ROWS_WG + pair * 32;
-    const bool kv_shared = R > 1;              // row groups re-read the same KV: keep it in L2
+    // row groups that re-read the same KV keep it in L2 (default policy); a single reader
+    // streams it (nontemporal)
+    auto copy = [&](const void* g, const void* l) {
+        if constexpr (SHARED) dma16_shared(g, l);
+        else dma16(g, l);
+    };
 
     // fragment addresses that do not depend on the chunk
     const int krow = 16 * h + l16;               // this wave's K rows: tokens 16h..16h+15
     int kaddr[2], kaddrB[2];                     // bf16: [ks&1] (+128 per ks/2 in region A)
     int vaddr[2][4];                             // bf16 tr16: [half][dt&3] (+128 per dt/4)
-    int v8row = 0;                               // fp8 tr8: source token row of this lane
+    // fp8: the XOR of the row layout only touches the low 3 granule bits, so fragment offsets
+    // repeat with a constant 128 B stride: K step ks uses k8addr[ks&3] + 128*(ks/4), V^T tile
+    // dt uses v8addr[dt&7] + 128*(dt/8)
+    int k8addr[4], v8addr[8];
     if constexpr (!SPARSE) {
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
@@ -124,9 +145,16 @@ void mla_decode_big_kernel(const AttnArgs a) {
                 vaddr[hf][d4] = lds_a(row, 2 * d4 + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
             }
     } else {
+        // K: lane (g4, l16) reads 8 codes of token krow at dims 16*ks + 8*g4 .. (granule
+        // 2*ks + g4/2, half g4&1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            k8addr[r] = krow * kRec8Row + (((2 * r + (g4 >> 1)) ^ swz8(krow)) << 4) + (g4 & 1) * 8;
         // tr8: source lane s of group g supplies token (s/2 < 4 ? 4g + s/2 : 16 + 4g + s/2 - 4)
         const int j = l16 >> 1;
-        v8row = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
+        const int v8row = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8addr[e] = v8row * kRec8Row + ((e ^ swz8(v8row)) << 4) + (l16 & 1) * 8;
     }
 
     bf16x8 qf[2][18];
@@ -173,183 +201,231 @@ void mla_decode_big_kernel(const AttnArgs a) {
             return __builtin_amdgcn_readfirstlane(win[p - bt_base]);
         };
 
-        // copy chunk c of the segment into ring slot c % DEPTH; each wave copies every WAVES-th row
-        auto issue_with = [&](int c, auto shared) {
-            auto copy = [&](const void* g, const void* l) {
-                if constexpr (decltype(shared)::value) dma16_shared(g, l);
-                else dma16(g, l);
-            };
-            char* dst = ring + (c % DEPTH) * C::BUF;
-            const int tb = t0 + c * kChunk;
-            const int nrows = min(kChunk, t1 - tb);
+        // ---- copies of one chunk: each wave copies every WAVES-th row.  A plan holds what
+        // does not depend on the copy (so the copies can be spread over the MFMAs); chunks past
+        // the segment's end re-copy its last chunk into their (unused) slot, which keeps the
+        // number of copies per chunk fixed.
+        struct Plan {
+            const char* base;                      // paged: first row of the chunk in HBM
+            int idx[SPARSE ? C::OPS : 1];          // sparse: record of the row this lane fills, per copy
+            char* dst;
+            int nrows;
+        };
+        auto plan_for = [&](int c) {
+            Plan p;
+            const int cc = min(c, nch - 1);
+            p.dst = ring + (c % DEPTH) * C::BUF;
+            const int tb = t0 + cc * kChunk;
+            p.nrows = min(kChunk, t1 - tb);
             if constexpr (!SPARSE) {
-                const int page = page_of(c >> 1);
-                const char* base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+                const int page = page_of(cc >> 1);
+                p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+            } else {
+                p.base = nullptr;
+                // recomputed per chunk on purpose: hoisted, these addresses would not fit in registers
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
 #pragma unroll
                 for (int j = 0; j < C::OPS; ++j) {
-                    const int q = wave + WAVES * j;
-                    if (j < kChunk / WAVES) {   // region A rows (WAVES divides kChunk)
-                        const int rr = min(q, nrows - 1);
-                        copy(base + rr * kRowBytes + ((lane ^ swz(q)) << 4), dst + q * kRowA);
-                    } else {
-                        const int sl = (q - kChunk) * 64 + lane;
-                        const int row = sl >> 3;
-                        const int rr = min(row, nrows - 1);
-                        copy(base + rr * kRowBytes + (64 + ((sl & 7) ^ swz(row))) * 16,
-                             dst + kRegionB + (q - kChunk) * 1024);
-                    }
+                    const int row = (64 * (wave + WAVES * j) + ln) / 40;   // row of the granule this lane fills
+                    const int v = lidx[cc * kChunk + row];     // inside the list; stale past its end
+                    p.idx[j] = row < p.nrows ? v : -1;
+                }
+            }
+            return p;
+        };
+        auto copy_op = [&](const Plan& p, int j) {
+            if constexpr (!SPARSE) {
+                const int q = wave + WAVES * j;
+                if (j < kChunk / WAVES) {   // region A rows (WAVES divides kChunk)
+                    const int rr = min(q, p.nrows - 1);
+                    copy(p.base + rr * kRowBytes + ((lane ^ swz(q)) << 4), p.dst + q * kRowA);
+                } else {
+                    const int sl = (q - kChunk) * 64 + lane;
+                    const int row = sl >> 3;
+                    const int rr = min(row, p.nrows - 1);
+                    copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swz(row))) * 16,
+                         p.dst + kRegionB + (q - kChunk) * 1024);
                 }
             } else {
-                const char* kvb = static_cast<const char*>(a.kv);
-#pragma unroll
-                for (int j = 0; j < C::OPS; ++j) {
-                    const int row = wave + WAVES * j;
-                    const int idx = row < nrows ? lidx[c * kChunk + row] : -1;
-                    const char* src = idx >= 0 ? kvb + (size_t)idx * kRec : reinterpret_cast<const char*>(kZeroRecord);
-                    const int g = lane ^ swz8(row);
-                    if (lane < 40 && g <= 36) copy(src + g * 16, dst + row * kRec8Row);
-                }
+                const int gg = 64 * (wave + WAVES * j) + lane;
+                const int row = gg / 40, slot_g = gg - 40 * row;
+                const char* rec = p.idx[j] >= 0 ? static_cast<const char*>(a.kv) + (size_t)p.idx[j] * kRec
+                                                : reinterpret_cast<const char*>(kZeroRecord);
+                copy(rec + ((slot_g ^ swz8(row)) << 4), p.dst + 1024 * (wave + WAVES * j));
             }
         };
-        auto issue = [&](int c) {
-            if (c >= nch) return;
-            if (kv_shared) issue_with(c, std::integral_constant<bool, true>{});
-            else issue_with(c, std::integral_constant<bool, false>{});
+
+        // ---- LDS fragments
+        auto kfrag = [&](const char* buf, int ks) -> bf16x8 {
+            if constexpr (!SPARSE) {
+                const int off = ks < 16 ? kaddr[ks & 1] + 128 * (ks >> 1) : kaddrB[ks & 1];
+                return *reinterpret_cast<const bf16x8*>(buf + off);
+            } else {
+                const uint2 w = *reinterpret_cast<const uint2*>(buf + k8addr[ks & 3] + 128 * (ks >> 2));
+                return fp8x8_to_bf16(w.x, w.y);
+            }
+        };
+        auto vfrag = [&](const char* buf, int dt) -> bf16x8 {    // dt: global 16-dim tile 0..31
+            if constexpr (!SPARSE) {
+                const int off = 128 * (dt >> 2);
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0][dt & 3] + off));
+                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[1][dt & 3] + off));
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                typedef int v2i __attribute__((ext_vector_type(2)));
+                const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(buf + v8addr[dt & 7] + 128 * (dt >> 3)));
+                return fp8x8_to_bf16((unsigned)w[0], (unsigned)w[1]);
+            }
         };
 
-        // ---- S^T for this wave's 16 tokens of chunk c, masked and scaled, and the pair's row
-        // maxima (one barrier).  Rows that see their first finite scores take the chunk maximum
-        // as reference; returns whether a row outgrew its reference (a restart vote).
-        auto scores = [&](int c, f4 (&s)[2], float (&mx)[2], float (&tsc)[4]) -> bool {
+        // S^T partial products of chunk c for this wave's 16 tokens: [n][ks&1], four independent
+        // MFMA chains.  side(ks) runs between the steps (work of other stages); fragments are
+        // read kPF steps ahead of their MFMAs, since one wave per SIMD leaves nothing else to
+        // hide the LDS latency.
+        auto qk = [&](int c, f4 (&s2)[2][2], auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
-            const int tb = t0 + c * kChunk;
-            f4 s2[2][2];                // [n][ks&1]: four independent MFMA chains
 #pragma unroll
             for (int n = 0; n < 2; ++n) s2[n][0] = s2[n][1] = f4{0.f, 0.f, 0.f, 0.f};
-            auto kfrag = [&](int ks) -> bf16x8 {
-                if constexpr (!SPARSE) {
-                    const int off = ks < 16 ? kaddr[ks & 1] + 128 * (ks >> 1) : kaddrB[ks & 1];
-                    return *reinterpret_cast<const bf16x8*>(buf + off);
-                } else {
-                    const int gq = 2 * ks + (g4 >> 1);
-                    const uint2 w = *reinterpret_cast<const uint2*>(buf + krow * kRec8Row + ((gq ^ swz8(krow)) << 4) + (g4 & 1) * 8);
-                    return fp8x8_to_bf16(w.x, w.y);
-                }
-            };
-            // fragments are read kPF steps ahead of their MFMAs: with one wave per SIMD nothing
-            // else hides the LDS latency
             bf16x8 kf[kPF];
 #pragma unroll
-            for (int i = 0; i < kPF - 1; ++i) kf[i] = kfrag(i);
+            for (int i = 0; i < kPF - 1; ++i) kf[i] = kfrag(buf, i);
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                if (ks + kPF - 1 < 18) kf[(ks + kPF - 1) % kPF] = kfrag(ks + kPF - 1);
+                if (ks + kPF - 1 < 18) kf[(ks + kPF - 1) % kPF] = kfrag(buf, ks + kPF - 1);
 #pragma unroll
                 for (int n = 0; n < 2; ++n) s2[n][ks & 1] = mfma16(kf[ks % kPF], qf[n][ks], s2[n][ks & 1]);
+                side(ks);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        // O^T[256h + ..][row] += V^T P^T over chunk c's 32 tokens; side(dt) between the steps
+        auto pv = [&](int c, const bf16x8 (&pT)[2], auto&& side) {
+            const char* buf = ring + (c % DEPTH) * C::BUF;
+            bf16x8 vf[kPF];
 #pragma unroll
-            for (int n = 0; n < 2; ++n) s[n] = s2[n][0] + s2[n][1];
-            bool tok_ok[4];
+            for (int i = 0; i < kPF - 1; ++i) vf[i] = vfrag(buf, 16 * h + i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * h + 4 * g4 + i;
-                if constexpr (SPARSE) {
-                    const int idx = tb + tok < t1 ? lidx[c * kChunk + tok] : -1;
-                    tok_ok[i] = idx >= 0;
-                    tsc[i] = idx >= 0 ? *reinterpret_cast<const float*>(buf + tok * kRec8Row + ((36 ^ swz8(tok)) << 4)) : 0.f;
-                } else {
-                    tok_ok[i] = tb + tok < t1;
-                    tsc[i] = 1.f;
-                }
+            for (int dt = 0; dt < 16; ++dt) {
+                if (dt + kPF - 1 < 16) vf[(dt + kPF - 1) % kPF] = vfrag(buf, 16 * h + dt + kPF - 1);
+#pragma unroll
+                for (int n = 0; n < 2; ++n) acc[dt][n] = mfma16(vf[dt % kPF], pT[n], acc[dt][n]);
+                side(dt);
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                mx[n] = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bool valid = tok_ok[i];
-                    if constexpr (!SPARSE) valid = valid && (tb + 16 * h + 4 * g4 + i <= limit[n]);
-                    const float f = SPARSE ? a.scale_log2 * tsc[i] : a.scale_log2;
-                    s[n][i] = valid ? s[n][i] * f : -INFINITY;
-                    mx[n] = fmaxf(mx[n], s[n][i]);
-                }
-                mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 16));
-                mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 32));
-                if (g4 == 0) xch[(wave * 2 + n) * 16 + l16] = mx[n];
-            }
-            __syncthreads();
-            bool outgrown = false;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                mx[n] = fmaxf(mx[n], xch[(partner * 2 + n) * 16 + l16]);
-                if (m_run[n] == -INFINITY) m_run[n] = mx[n];     // acc and l are still exactly 0
-                else outgrown = outgrown || (mx[n] > m_run[n] + kRefSlack);
-            }
-            return __builtin_amdgcn_ballot_w64(outgrown) != 0;
         };
 
-        // ---- P for this wave's tokens, P^T halves exchanged in the pair together with the
-        // restart votes of all waves (one barrier), and O^T[256h + ..][row] += V^T P^T over the
-        // chunk's 32 tokens.  Returns true (and skips P.V) when the workgroup must restart.
-        auto accumulate = [&](int c, const f4 (&s)[2], const float (&tsc)[4], bool vote) -> bool {
+        // ---- softmax stages of one chunk, in steps that can be spread over MFMAs
+        struct Scores {
+            f4 s[2];        // masked, scaled (log2 units) S^T values of this wave's 16 tokens
+            float mx[2];    // row maxima: this wave's tokens, then (prob_step 1) the pair's
+            float tsc[4];   // sparse: token scales
+            bool ok[4];     // token inside the segment and a real index
+        };
+        // step 0: sum the chains; 1: token validity and scales; 2/3: mask and scale tile n,
+        // local max; 4/5: cross-lane maxima; 6: own maxima to LDS
+        auto mask_step = [&](int step, int c, const f4 (&s2)[2][2], Scores& S) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
-            uint2 mine[2];
+            const int tb = t0 + c * kChunk;
+            if (step == 0) {
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+                for (int n = 0; n < 2; ++n) S.s[n] = s2[n][0] + s2[n][1];
+            } else if (step == 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = 16 * h + 4 * g4 + i;
+                    if constexpr (SPARSE) {
+                        const int v = lidx[c * kChunk + tok];   // inside the list; stale past its end
+                        const float sc = *reinterpret_cast<const float*>(buf + tok * kRec8Row + ((36 ^ swz8(tok)) << 4));
+                        S.ok[i] = tb + tok < t1 && v >= 0;
+                        S.tsc[i] = S.ok[i] ? sc : 0.f;
+                    } else {
+                        S.ok[i] = tb + tok < t1;
+                        S.tsc[i] = 1.f;
+                    }
+                }
+            } else if (step == 2 || step == 3) {
+                const int n = step - 2;
+                S.mx[n] = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bool valid = S.ok[i];
+                    if constexpr (!SPARSE) valid = valid && (tb + 16 * h + 4 * g4 + i <= limit[n]);
+                    const float f = SPARSE ? a.scale_log2 * S.tsc[i] : a.scale_log2;
+                    S.s[n][i] = valid ? S.s[n][i] * f : -INFINITY;
+                    S.mx[n] = fmaxf(S.mx[n], S.s[n][i]);
+                }
+            } else if (step == 4) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n) S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 16));
+            } else if (step == 5) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n) S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 32));
+            } else if (step == 6) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n) *(g4 == 0 ? &xch[(wave * 2 + n) * 16 + l16] : my_sink) = S.mx[n];
+            }
+        };
+        // After a barrier: step 0 reads the partner's maxima; 1 takes the pair maxima, sets
+        // first references and votes; 2/3 probabilities of tile n; 4 stores this wave's P^T
+        // half; 5 stores the vote.
+        struct Probs {
+            float other[2];
+            uint2 mine[2];
+            bool vote;
+        };
+        auto prob_step = [&](int step, Scores& S, Probs& P) {
+            if (step == 0) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n) P.other[n] = xch[(partner * 2 + n) * 16 + l16];
+            } else if (step == 1) {
+                bool outgrown = false;
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    S.mx[n] = fmaxf(S.mx[n], P.other[n]);
+                    if (m_run[n] == -INFINITY) m_run[n] = S.mx[n];     // acc and l are still exactly 0
+                    else outgrown = outgrown || (S.mx[n] > m_run[n] + kRefSlack);
+                }
+                P.vote = __builtin_amdgcn_ballot_w64(outgrown) != 0;
+            } else if (step == 2 || step == 3) {
+                const int n = step - 2;
                 const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = exp2_fast(s[n][i] - m_use);
+                    p[i] = exp2_fast(S.s[n][i] - m_use);
                     l_run[n] += p[i];
-                    if constexpr (SPARSE) p[i] *= tsc[i];
+                    if constexpr (SPARSE) p[i] *= S.tsc[i];
                 }
-                mine[n] = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-                pex[(wave * 2 + n) * 64 + lane] = mine[n];
+                P.mine[n] = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+            } else if (step == 4) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n) pex[(wave * 2 + n) * 64 + lane] = P.mine[n];
+            } else if (step == 5) {
+                *(lane == 0 ? reinterpret_cast<float*>(&votes[wave]) : my_sink) = __int_as_float(P.vote ? 1 : 0);
             }
-            if (lane == 0) votes[wave] = vote ? 1 : 0;
-            __syncthreads();
+        };
+        // after the barrier that follows prob_step: any vote in the workgroup?  Else this wave's
+        // B operands of O^T += V^T P^T
+        auto any_vote = [&]() {
             int any = 0;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) any |= votes[w];
-            if (__builtin_amdgcn_readfirstlane(any)) return true;
-            bf16x8 pT[2];
+            return __builtin_amdgcn_readfirstlane(any) != 0;
+        };
+        auto p_operands = [&](const Probs& P, bf16x8 (&pT)[2]) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const uint2 other = pex[(partner * 2 + n) * 64 + lane];
-                const uint4 pk = h == 0 ? make_uint4(mine[n].x, mine[n].y, other.x, other.y)
-                                        : make_uint4(other.x, other.y, mine[n].x, mine[n].y);
+                const uint4 pk = h == 0 ? make_uint4(P.mine[n].x, P.mine[n].y, other.x, other.y)
+                                        : make_uint4(other.x, other.y, P.mine[n].x, P.mine[n].y);
                 pT[n] = __builtin_bit_cast(bf16x8, pk);
             }
-            auto vfrag = [&](int dt) -> bf16x8 {    // dt: global 16-dim tile 0..31
-                if constexpr (!SPARSE) {
-                    const int off = 128 * (dt >> 2);
-                    const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0][dt & 3] + off));
-                    const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[1][dt & 3] + off));
-                    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-                } else {
-                    typedef int v2i __attribute__((ext_vector_type(2)));
-                    const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) v2i*)(buf + v8row * kRec8Row + ((dt ^ swz8(v8row)) << 4) + (l16 & 1) * 8));
-                    return fp8x8_to_bf16((unsigned)w[0], (unsigned)w[1]);
-                }
-            };
-            bf16x8 vf[kPF];
-#pragma unroll
-            for (int i = 0; i < kPF - 1; ++i) vf[i] = vfrag(16 * h + i);
-#pragma unroll
-            for (int dt = 0; dt < 16; ++dt) {
-                if (dt + kPF - 1 < 16) vf[(dt + kPF - 1) % kPF] = vfrag(16 * h + dt + kPF - 1);
-#pragma unroll
-                for (int n = 0; n < 2; ++n) acc[dt][n] = mfma16(vf[dt % kPF], pT[n], acc[dt][n]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            return false;
         };
+        auto no_side = [](int) {};
 
-        // ---- passes over the segment (a second one only after a restart vote).  Pipeline:
-        // DEPTH-1 chunks in flight; all waves run the same barriers.
+        // ---- passes over the segment (a second one only after a restart vote)
         for (;;) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
@@ -357,37 +433,121 @@ void mla_decode_big_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int dt = 0; dt < 16; ++dt) acc[dt][n] = f4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int c = 0; c < DEPTH - 1; ++c) issue(c);
             bool restart = false;
-            float mx[2];
-            for (int k = 0; k < nch; ++k) {
-                // copies are counted exactly (every chunk issues C::OPS per wave), so chunk k has
-                // landed once at most DEPTH-2 later chunks' copies remain in flight
-                if (k + DEPTH - 2 < nch) {
+            Scores S;
+            if constexpr (C::PIPELINED) {
+                // DEPTH-2 chunks ahead.  Every chunk slot gets exactly C::OPS copies per wave, so
+                // chunk k has landed once at most DEPTH-3 later chunks' copies are outstanding.
+                constexpr int AHEAD = DEPTH - 2;
+#pragma unroll
+                for (int c = 0; c < AHEAD; ++c) {
+                    const Plan p = plan_for(c);
+#pragma unroll
+                    for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+                }
+                auto wait_chunk = [&]() {
+                    if constexpr (AHEAD - 1 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((AHEAD - 1) * C::OPS) : "memory");
+                };
+                // chunk 0: Q.K^T (copies of chunk AHEAD spread over it), mask and maxima
+                wait_chunk();
+                __syncthreads();
+                {
+                    const Plan p = plan_for(AHEAD);
+                    f4 s2[2][2];
+                    qk(0, s2, [&](int ks) {
+                        if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                    });
+#pragma unroll
+                    for (int step = 0; step < 7; ++step) mask_step(step, 0, s2, S);
+                }
+                for (int k = 1; k < nch; ++k) {
+                    wait_chunk();
+                    // chunk k in LDS; maxima of chunk k-1 visible; slot (k-2) % DEPTH free
+                    __syncthreads();
+                    const Plan p = plan_for(k + AHEAD);
+                    Probs P;
+                    f4 s2[2][2];
+                    // S^T(k) on the MFMAs while chunk k-1 becomes probabilities and chunk
+                    // k+AHEAD is copied
+                    qk(k, s2, [&](int ks) {
+                        if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                        if (ks == 1) prob_step(0, S, P);
+                        if (ks == 3) prob_step(1, S, P);
+                        if (ks == 5) prob_step(2, S, P);
+                        if (ks == 7) prob_step(3, S, P);
+                        if (ks == 9) prob_step(4, S, P);
+                        if (ks == 10) prob_step(5, S, P);
+                    });
+                    __syncthreads();               // P^T halves and votes of chunk k-1 visible
+                    if (any_vote()) {
+                        restart = true;
+                        break;
+                    }
+                    bf16x8 pT[2];
+                    p_operands(P, pT);
+                    // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked
+                    pv(k - 1, pT, [&](int dt) {
+                        if (dt < 7) mask_step(dt, k, s2, S);
+                    });
+                }
+                if (!restart) {
+                    __syncthreads();               // maxima of the last chunk visible
+                    Probs P;
+#pragma unroll
+                    for (int step = 0; step < 6; ++step) prob_step(step, S, P);
+                    __syncthreads();
+                    if (any_vote()) {
+                        restart = true;
+                    } else {
+                        bf16x8 pT[2];
+                        p_operands(P, pT);
+                        pv(nch - 1, pT, no_side);
+                    }
+                }
+            } else {
+                // one pair: DEPTH-1 chunks in flight, the stages of a chunk back to back
+#pragma unroll
+                for (int c = 0; c < DEPTH - 1; ++c) {
+                    const Plan p = plan_for(c);
+#pragma unroll
+                    for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+                }
+                for (int k = 0; k < nch; ++k) {
                     if constexpr (DEPTH - 2 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH - 2) * C::OPS) : "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                }
-                __syncthreads();               // chunk k is in LDS; slot k-1 is no longer read
-                issue(k + DEPTH - 1);
-                f4 sc[2];
-                float tsc[4];
-                const bool vote = scores(k, sc, mx, tsc);
-                if (accumulate(k, sc, tsc, vote)) {
-                    restart = true;
-                    break;
+                    __syncthreads();               // chunk k is in LDS; slot k-1 is no longer read
+                    {
+                        const Plan p = plan_for(k + DEPTH - 1);
+#pragma unroll
+                        for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+                    }
+                    f4 s2[2][2];
+                    qk(k, s2, no_side);
+#pragma unroll
+                    for (int step = 0; step < 7; ++step) mask_step(step, k, s2, S);
+                    __syncthreads();
+                    Probs P;
+#pragma unroll
+                    for (int step = 0; step < 6; ++step) prob_step(step, S, P);
+                    __syncthreads();
+                    if (any_vote()) {
+                        restart = true;
+                        break;
+                    }
+                    bf16x8 pT[2];
+                    p_operands(P, pT);
+                    pv(k, pT, no_side);
                 }
             }
-            if (!restart) break;
-            // drain the copies in flight, then start over with each row's largest maximum so far
+            // the copies past the segment's end (or those in flight at a restart) land first
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (!restart) break;
+            // start over with each row's largest maximum so far
             __syncthreads();
 #pragma unroll
-            for (int n = 0; n < 2; ++n) m_run[n] = fmaxf(m_run[n], mx[n]);
+            for (int n = 0; n < 2; ++n) m_run[n] = fmaxf(m_run[n], S.mx[n]);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         // ---- row sums of the pair (both halves share the reference m), then the output
 #pragma unroll
@@ -402,29 +562,27 @@ void mla_decode_big_kernel(const AttnArgs a) {
         __syncthreads();
 #pragma unroll
         for (int n = 0; n < 2; ++n) l_run[n] += xch[(partner * 2 + n) * 16 + l16];
-        {
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int r = rbase + 16 * n + l16;
-                const float l = l_run[n];
-                const float inv = l > 0.f ? 1.f / l : 0.f;
-                const float lse_v = l > 0.f ? (m_run[n] + __log2f(l)) * kLn2 : -INFINITY;
-                if (r < a.M) {
-                    if (final_out) {
-                        __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + r) * kDv + 256 * h + 4 * g4;
+        for (int n = 0; n < 2; ++n) {
+            const int r = rbase + 16 * n + l16;
+            const float l = l_run[n];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float lse_v = l > 0.f ? (m_run[n] + __log2f(l)) * kLn2 : -INFINITY;
+            if (r < a.M) {
+                if (final_out) {
+                    __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + r) * kDv + 256 * h + 4 * g4;
 #pragma unroll
-                        for (int dt = 0; dt < 16; ++dt) {
-                            const f4 v = acc[dt][n] * inv;
-                            *reinterpret_cast<uint2*>(orow + dt * 16) =
-                                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                        }
-                        if (g4 == 0 && h == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
-                    } else {
-                        float* prow = a.part_o + ((size_t)slot * a.M + r) * kDv + 256 * h + 4 * g4;
-#pragma unroll
-                        for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<f4*>(prow + dt * 16) = acc[dt][n] * inv;
-                        if (g4 == 0 && h == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
+                    for (int dt = 0; dt < 16; ++dt) {
+                        const f4 v = acc[dt][n] * inv;
+                        *reinterpret_cast<uint2*>(orow + dt * 16) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                     }
+                    if (g4 == 0 && h == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
+                } else {
+                    float* prow = a.part_o + ((size_t)slot * a.M + r) * kDv + 256 * h + 4 * g4;
+#pragma unroll
+                    for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<f4*>(prow + dt * 16) = acc[dt][n] * inv;
+                    if (g4 == 0 && h == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
                 }
             }
         }
@@ -457,7 +615,10 @@ template <bool SPARSE, int PAIRS>
 static hipError_t launch_big_t(const AttnArgs& a, int items, hipStream_t stream) {
     using C = BigCfg<SPARSE, PAIRS>;
     const int R = (a.M + C::ROWS_WG - 1) / C::ROWS_WG;
-    hipLaunchKernelGGL((mla_decode_big_kernel<SPARSE, PAIRS>), dim3(items * R), dim3(C::WAVES * 64), 0, stream, a);
+    if (R > 1)
+        hipLaunchKernelGGL((mla_decode_big_kernel<SPARSE, PAIRS, true>), dim3(items * R), dim3(C::WAVES * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((mla_decode_big_kernel<SPARSE, PAIRS, false>), dim3(items * R), dim3(C::WAVES * 64), 0, stream, a);
     return hipGetLastError();
 }
 
