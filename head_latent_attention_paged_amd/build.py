@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mla_kernels.hip", "mla_decode_big.hip", "mla_api.cpp"]
+SOURCES = ["mla_kernels.hip", "mla_decode_big.hip", "mla_decode_rows.hip", "mla_api.cpp"]
 
 
 def hipcc_cmd(out: str = LIB):

@@ -29,14 +29,27 @@ namespace mla {
 // separates rows r and r+16.  The rows of a chunk are contiguous, so one 64-lane copy fills
 // 1 KB of it (parts of two rows) and a chunk takes 20 copies with every lane active.
 constexpr int kRec8Row = 640;
-constexpr int kPF = 4;       // LDS fragment prefetch distance (MFMA steps)
+#ifndef MLA_BIG_SCHED
+#define MLA_BIG_SCHED 1
+#endif
+#ifndef MLA_BIG_PF
+#define MLA_BIG_PF 4
+#endif
+constexpr int kPF = MLA_BIG_PF;   // LDS fragment prefetch distance (MFMA steps)
 // The softmax reference of a row is the first finite chunk maximum it sees and never moves
 // inside a pass, so the accumulators are touched only by MFMAs.  p = 2^(s - m) <= 2^kRefSlack
 // keeps bf16 P and the fp32 sums finite; a row whose scores outgrow the reference by more
 // (scores spanning over 44 nats) makes the workgroup restart the segment with the larger
 // reference.
 constexpr float kRefSlack = 64.f;
-__device__ __forceinline__ int swz8(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ ((r >> 4) & 1); }
+// LDS swizzles for gfx950's 64 banks (256 B per cycle: 16 lanes of a 16-byte read, 32 lanes of an
+// 8-byte read).  bf16 region A: slot = granule ^ swzA(r) on the low 4 bits, so the 16 rows of a
+// K read and the 8 rows x 32 B of a V^T transposing read each hit distinct banks.  Region B
+// (128 B rows, two per 256 B): swzB separates the even and the odd rows.  fp8 rows (640 B):
+// swz8 keeps both the 16 rows of a K read and the 16 rows of a V^T tr8 read apart.
+__device__ __forceinline__ int swzA(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
 
 // An all-zero record: unused index entries are copied from it, so a chunk always costs the same
 // copies (exact s_waitcnt accounting) and its zero-weight V rows are finite.
@@ -125,24 +138,29 @@ void mla_decode_big_kernel(const AttnArgs a) {
 
     // fragment addresses that do not depend on the chunk
     const int krow = 16 * h + l16;               // this wave's K rows: tokens 16h..16h+15
-    int kaddr[2], kaddrB[2];                     // bf16: [ks&1] (+128 per ks/2 in region A)
-    int vaddr[2][4];                             // bf16 tr16: [half][dt&3] (+128 per dt/4)
+    int kaddr[4], kaddrB[2];                     // bf16: [ks&3] (+256 per ks/4 in region A)
+    int vaddr[2][8];                             // bf16 tr16: [half][dt&7] (+256 per dt/8)
     // fp8: the XOR of the row layout only touches the low 3 granule bits, so fragment offsets
     // repeat with a constant 128 B stride: K step ks uses k8addr[ks&3] + 128*(ks/4), V^T tile
     // dt uses v8addr[dt&7] + 128*(dt/8)
     int k8addr[4], v8addr[8];
     if constexpr (!SPARSE) {
+        // K step ks reads granule 8*(ks/2) + 4*(ks&1) + g4 of row krow; the XOR only touches the
+        // low 4 granule bits, so steps ks and ks+4 differ by a constant 256 B
 #pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            kaddr[par] = lds_a(krow, 4 * par + g4);
-            kaddrB[par] = lds_b(krow, 4 * par + g4);
-        }
+        for (int r4 = 0; r4 < 4; ++r4)
+            kaddr[r4] = krow * kRowA + (((8 * (r4 >> 1) + 4 * (r4 & 1) + g4) ^ swzA(krow)) << 4);
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            kaddrB[par] = kRegionB + krow * 128 + (((4 * par + g4) ^ swzB(krow)) << 4);
+        // V^T tile dt: lane supplies row 4*g4 + l16/4 (+16 for the upper tokens), granule
+        // 2*dt + ((l16&3)>>1), byte (l16&1)*8
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int d4 = 0; d4 < 4; ++d4) {
+            for (int e = 0; e < 8; ++e) {
                 const int row = 4 * g4 + (l16 >> 2) + 16 * hf;
-                vaddr[hf][d4] = lds_a(row, 2 * d4 + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+                vaddr[hf][e] = row * kRowA + (((2 * e + ((l16 & 3) >> 1)) ^ swzA(row)) << 4) + (l16 & 1) * 8;
             }
     } else {
         // K: lane (g4, l16) reads 8 codes of token krow at dims 16*ks + 8*g4 .. (granule
@@ -239,12 +257,12 @@ void mla_decode_big_kernel(const AttnArgs a) {
                 const int q = wave + WAVES * j;
                 if (j < kChunk / WAVES) {   // region A rows (WAVES divides kChunk)
                     const int rr = min(q, p.nrows - 1);
-                    copy(p.base + rr * kRowBytes + ((lane ^ swz(q)) << 4), p.dst + q * kRowA);
+                    copy(p.base + rr * kRowBytes + ((lane ^ swzA(q)) << 4), p.dst + q * kRowA);
                 } else {
                     const int sl = (q - kChunk) * 64 + lane;
                     const int row = sl >> 3;
                     const int rr = min(row, p.nrows - 1);
-                    copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swz(row))) * 16,
+                    copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(row))) * 16,
                          p.dst + kRegionB + (q - kChunk) * 1024);
                 }
             } else {
@@ -259,7 +277,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
         // ---- LDS fragments
         auto kfrag = [&](const char* buf, int ks) -> bf16x8 {
             if constexpr (!SPARSE) {
-                const int off = ks < 16 ? kaddr[ks & 1] + 128 * (ks >> 1) : kaddrB[ks & 1];
+                const int off = ks < 16 ? kaddr[ks & 3] + 256 * (ks >> 2) : kaddrB[ks & 1];
                 return *reinterpret_cast<const bf16x8*>(buf + off);
             } else {
                 const uint2 w = *reinterpret_cast<const uint2*>(buf + k8addr[ks & 3] + 128 * (ks >> 2));
@@ -268,9 +286,9 @@ void mla_decode_big_kernel(const AttnArgs a) {
         };
         auto vfrag = [&](const char* buf, int dt) -> bf16x8 {    // dt: global 16-dim tile 0..31
             if constexpr (!SPARSE) {
-                const int off = 128 * (dt >> 2);
-                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0][dt & 3] + off));
-                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[1][dt & 3] + off));
+                const int off = 256 * (dt >> 3);
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0][dt & 7] + off));
+                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[1][dt & 7] + off));
                 return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
             } else {
                 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -297,7 +315,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int n = 0; n < 2; ++n) s2[n][ks & 1] = mfma16(kf[ks % kPF], qf[n][ks], s2[n][ks & 1]);
                 side(ks);
-                __builtin_amdgcn_sched_barrier(0);
+                if (MLA_BIG_SCHED) __builtin_amdgcn_sched_barrier(0);
             }
         };
         // O^T[256h + ..][row] += V^T P^T over chunk c's 32 tokens; side(dt) between the steps
@@ -312,25 +330,31 @@ void mla_decode_big_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int n = 0; n < 2; ++n) acc[dt][n] = mfma16(vf[dt % kPF], pT[n], acc[dt][n]);
                 side(dt);
-                __builtin_amdgcn_sched_barrier(0);
+                if (MLA_BIG_SCHED) __builtin_amdgcn_sched_barrier(0);
             }
         };
 
         // ---- softmax stages of one chunk, in steps that can be spread over MFMAs
         struct Scores {
             f4 s[2];        // masked, scaled (log2 units) S^T values of this wave's 16 tokens
-            float mx[2];    // row maxima: this wave's tokens, then (prob_step 1) the pair's
+            float mx[2];    // row maxima (only taken when a row has no reference yet, or at a restart)
             float tsc[4];   // sparse: token scales
             bool ok[4];     // token inside the segment and a real index
+            bool outgrown;  // a score of a row with a reference exceeds it by more than kRefSlack
+            bool need_max;  // (wave-uniform) some row has no reference yet
         };
-        // step 0: sum the chains; 1: token validity and scales; 2/3: mask and scale tile n,
-        // local max; 4/5: cross-lane maxima; 6: own maxima to LDS
+        // Row maxima are only needed while a row has no reference (its first chunk) and at a
+        // restart; otherwise each lane just compares its own scores with the reference.
+        // step 0: sum the chains; 1: token validity and scales; 2/3: mask and scale tile n and
+        // test it against the reference
         auto mask_step = [&](int step, int c, const f4 (&s2)[2][2], Scores& S) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             const int tb = t0 + c * kChunk;
             if (step == 0) {
 #pragma unroll
                 for (int n = 0; n < 2; ++n) S.s[n] = s2[n][0] + s2[n][1];
+                S.need_max = __builtin_amdgcn_ballot_w64(m_run[0] == -INFINITY || m_run[1] == -INFINITY) != 0;
+                S.outgrown = false;
             } else if (step == 1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -347,47 +371,48 @@ void mla_decode_big_kernel(const AttnArgs a) {
                 }
             } else if (step == 2 || step == 3) {
                 const int n = step - 2;
-                S.mx[n] = -INFINITY;
+                const float cap = m_run[n] + kRefSlack;      // -inf while the row has no reference
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     bool valid = S.ok[i];
                     if constexpr (!SPARSE) valid = valid && (tb + 16 * h + 4 * g4 + i <= limit[n]);
                     const float f = SPARSE ? a.scale_log2 * S.tsc[i] : a.scale_log2;
                     S.s[n][i] = valid ? S.s[n][i] * f : -INFINITY;
-                    S.mx[n] = fmaxf(S.mx[n], S.s[n][i]);
+                    S.outgrown = S.outgrown || (m_run[n] != -INFINITY && S.s[n][i] > cap);
                 }
-            } else if (step == 4) {
-#pragma unroll
-                for (int n = 0; n < 2; ++n) S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 16));
-            } else if (step == 5) {
-#pragma unroll
-                for (int n = 0; n < 2; ++n) S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 32));
-            } else if (step == 6) {
-#pragma unroll
-                for (int n = 0; n < 2; ++n) *(g4 == 0 ? &xch[(wave * 2 + n) * 16 + l16] : my_sink) = S.mx[n];
             }
         };
-        // After a barrier: step 0 reads the partner's maxima; 1 takes the pair maxima, sets
-        // first references and votes; 2/3 probabilities of tile n; 4 stores this wave's P^T
-        // half; 5 stores the vote.
+        // this wave's row maxima of S (cross-lane) into LDS for the partner
+        auto max_to_lds = [&](Scores& S) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                S.mx[n] = fmaxf(fmaxf(S.s[n][0], S.s[n][1]), fmaxf(S.s[n][2], S.s[n][3]));
+                S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 16));
+                S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 32));
+                *(g4 == 0 ? &xch[(wave * 2 + n) * 16 + l16] : my_sink) = S.mx[n];
+            }
+        };
+        // after a barrier: the pair's row maxima
+        auto pair_max = [&](Scores& S) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) S.mx[n] = fmaxf(S.mx[n], xch[(partner * 2 + n) * 16 + l16]);
+        };
+        // After a barrier: step 0 gives rows without a reference the pair's maximum; 1 votes;
+        // 2/3 probabilities of tile n; 4 stores this wave's P^T half; 5 stores the vote.
         struct Probs {
-            float other[2];
             uint2 mine[2];
             bool vote;
         };
         auto prob_step = [&](int step, Scores& S, Probs& P) {
             if (step == 0) {
+                if (S.need_max) {
+                    pair_max(S);
 #pragma unroll
-                for (int n = 0; n < 2; ++n) P.other[n] = xch[(partner * 2 + n) * 16 + l16];
-            } else if (step == 1) {
-                bool outgrown = false;
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    S.mx[n] = fmaxf(S.mx[n], P.other[n]);
-                    if (m_run[n] == -INFINITY) m_run[n] = S.mx[n];     // acc and l are still exactly 0
-                    else outgrown = outgrown || (S.mx[n] > m_run[n] + kRefSlack);
+                    for (int n = 0; n < 2; ++n)
+                        if (m_run[n] == -INFINITY) m_run[n] = S.mx[n];     // acc and l are still exactly 0
                 }
-                P.vote = __builtin_amdgcn_ballot_w64(outgrown) != 0;
+            } else if (step == 1) {
+                P.vote = __builtin_amdgcn_ballot_w64(S.outgrown) != 0;
             } else if (step == 2 || step == 3) {
                 const int n = step - 2;
                 const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
@@ -459,7 +484,8 @@ void mla_decode_big_kernel(const AttnArgs a) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
                     });
 #pragma unroll
-                    for (int step = 0; step < 7; ++step) mask_step(step, 0, s2, S);
+                    for (int step = 0; step < 4; ++step) mask_step(step, 0, s2, S);
+                    if (S.need_max) max_to_lds(S);
                 }
                 for (int k = 1; k < nch; ++k) {
                     wait_chunk();
@@ -488,8 +514,9 @@ void mla_decode_big_kernel(const AttnArgs a) {
                     p_operands(P, pT);
                     // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked
                     pv(k - 1, pT, [&](int dt) {
-                        if (dt < 7) mask_step(dt, k, s2, S);
+                        if (dt < 4) mask_step(dt, k, s2, S);
                     });
+                    if (S.need_max) max_to_lds(S);
                 }
                 if (!restart) {
                     __syncthreads();               // maxima of the last chunk visible
@@ -525,7 +552,8 @@ void mla_decode_big_kernel(const AttnArgs a) {
                     f4 s2[2][2];
                     qk(k, s2, no_side);
 #pragma unroll
-                    for (int step = 0; step < 7; ++step) mask_step(step, k, s2, S);
+                    for (int step = 0; step < 4; ++step) mask_step(step, k, s2, S);
+                    if (S.need_max) max_to_lds(S);
                     __syncthreads();
                     Probs P;
 #pragma unroll
@@ -543,10 +571,13 @@ void mla_decode_big_kernel(const AttnArgs a) {
             // the copies past the segment's end (or those in flight at a restart) land first
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (!restart) break;
-            // start over with each row's largest maximum so far
+            // start over with each row's largest maximum so far (S holds the chunk that voted)
+            max_to_lds(S);
             __syncthreads();
+            pair_max(S);
 #pragma unroll
             for (int n = 0; n < 2; ++n) m_run[n] = fmaxf(m_run[n], S.mx[n]);
+            __syncthreads();
         }
 
         // ---- row sums of the pair (both halves share the reference m), then the output

@@ -1,0 +1,525 @@
+// gfx950 decode kernel for many query rows per KV stream: paged s_q*h_q > 32, sparse h_q > 32.
+//
+// A workgroup holds 64 query rows in four waves (one per SIMD); each wave owns 16 rows end to
+// end: S^T = K Q^T for all 32 tokens of a chunk (tokens on the MFMA M side, "FlashMLA-ETAP:
+// Efficient Transpose Attention Pipeline ...", section 핵심 메커니즘, transposed form), the
+// online softmax of its rows, and O^T += V^T P^T over all 512 value dims.  The two 16-token
+// S^T tiles of a chunk hold, lane by lane, exactly the P^T elements this lane feeds to the
+// 16x16x32 P.V MFMA (with V^T read in the matching token order), so a wave needs no data from
+// another wave: the only workgroup barrier per chunk guards the shared ring of KV chunks.
+//
+// The chunk loop is software-pipelined: iteration k multiplies S^T(k) while it turns S^T(k-1)
+// into probabilities and copies a later chunk, then multiplies O^T += V^T(k-1) P^T(k-1) while
+// it masks S^T(k).  Chunks travel HBM -> LDS by direct copies, spread over all four waves.
+//
+// Softmax reference: a row's reference is its first finite chunk maximum and never moves inside
+// a pass, so the accumulators are touched only by MFMAs.  p = 2^(s - m) <= 2^kRefSlack keeps
+// bf16 P and the fp32 sums finite; a score that outgrows its row's reference by more (scores
+// spanning over 44 nats) makes the workgroup finish the pass, discard it and run it again with
+// the row's maximum over the whole segment as reference (so at most once per segment).
+//
+// Sparse fp8: a chunk is 32 gathered records ("deepseek-ai/FlashMLA" project summary, section
+// 기술적 세부 사항: fp8 values plus a per-token scale, -1 = unused index).  The raw e4m3 codes
+// stay in LDS and are converted exactly to bf16 as fragments are read; the token scale
+// multiplies the score and the probability before P.V.
+#include "mla_device.h"
+
+namespace mla {
+
+namespace rows {
+
+constexpr int kWaves = 4;
+constexpr int kRowsWg = 16 * kWaves;
+constexpr int kRec8Row = 640;     // fp8 record row in LDS: 40 granules (36 codes, scale, padding)
+constexpr int kPF = 4;            // LDS fragment prefetch distance (MFMA steps)
+constexpr float kRefSlack = 64.f;
+
+// LDS layouts, chosen by measuring the decode kernels' read patterns on gfx950 (64 banks):
+// bf16 region A holds dims 0..511 of a row in 1 KB at a 1056-byte row stride, unswizzled: the
+// 16 rows x 64 B of a K read (ds_read_b128) and the 8 rows x 32 B of a V^T transposing read both
+// run conflict-free (at a 1024-byte stride every XOR swizzle tried left the K read at half rate).
+// Region B (the 64 RoPE dims, 128 B rows): slot = granule ^ swzB(r).  fp8 rows (640 B): slot =
+// granule ^ swz8(r) keeps the 16 rows of a K read and of a V^T tr8 read apart.
+constexpr int kRowA16 = 1056;
+constexpr int kRegionB16 = kChunk * kRowA16;
+constexpr int kChunk16 = kRegionB16 + kChunk * 128;
+__device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
+
+// An all-zero record: unused index entries are copied from it, so a chunk always costs the same
+// copies (exact s_waitcnt accounting) and its zero-weight V rows are finite.
+__device__ __attribute__((aligned(16))) const unsigned char kZeroRecord[kRec8Row] = {0};
+
+// 8 e4m3 codes (two dwords) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
+#define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))
+    const uint4 v = make_uint4(MLA_CVT(lo, false), MLA_CVT(lo, true), MLA_CVT(hi, false), MLA_CVT(hi, true));
+#undef MLA_CVT
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool SPARSE>
+struct Cfg {
+    static constexpr int BUF = SPARSE ? kChunk * kRec8Row : kChunk16;
+    // ring slots: chunk k-1 (P.V), chunk k (Q.K^T) and AHEAD chunks in flight
+    static constexpr int DEPTH = SPARSE ? 6 : 4;
+    static constexpr int AHEAD = DEPTH - 2;
+    // copies per wave per chunk: bf16 32 rows of region A + 4 KB of region B; fp8 20 KB (one
+    // 64-lane copy fills 1 KB of the contiguous 640 B rows)
+    static constexpr int OPS = (SPARSE ? kChunk * kRec8Row / 1024 : kChunk + 4) / kWaves;
+    static constexpr int RING = DEPTH * BUF;
+    static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;        // a split's index list
+    static constexpr int PAGES = SPARSE ? 0 : kWaves * 64 * 4;            // per-wave page windows
+    static constexpr int VOTES = 2 * kWaves * 4;                          // restart votes, by chunk parity
+    static constexpr int SINK = kWaves * 64 * 4;                          // targets of masked-off lanes
+    static constexpr int LDS = RING + IDX + PAGES + VOTES + SINK;
+};
+
+template <bool SPARSE, bool SHARED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_rows_kernel(const AttnArgs a) {
+    using C = Cfg<SPARSE>;
+    constexpr int DEPTH = C::DEPTH;
+    constexpr int AHEAD = C::AHEAD;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    char* ring = smem;
+    int* lidx = reinterpret_cast<int*>(smem + C::RING);
+    int* lpages = reinterpret_cast<int*>(smem + C::RING + C::IDX);
+    int* votes = reinterpret_cast<int*>(smem + C::RING + C::IDX + C::PAGES);
+    float* sink = reinterpret_cast<float*>(smem + C::RING + C::IDX + C::PAGES + C::VOTES);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    float* my_sink = sink + wave * 64 + lane;
+
+    // ---- work item -> (part or sparse split, row group); row groups of one item share an XCD
+    const int R = ceil_div(a.M, kRowsWg);
+    const int n_items = SPARSE ? a.batch * a.num_parts : a.num_parts;
+    int item, rg;
+    {
+        const int bid = blockIdx.x;
+        if ((n_items & 7) == 0) {
+            const int xcd = bid & 7, k = bid >> 3;
+            item = (k / R) * 8 + xcd;
+            rg = k % R;
+        } else {
+            item = bid / R;
+            rg = bid % R;
+        }
+    }
+    const int row = rg * kRowsWg + 16 * wave + l16;     // this lane's query row (B / C column)
+    const bool row_ok = row < a.M;
+    // row groups that re-read the same KV keep it in L2 (default policy); a single reader
+    // streams it (nontemporal)
+    auto copy = [&](const void* g, const void* l) {
+        if constexpr (SHARED) dma16_shared(g, l);
+        else dma16(g, l);
+    };
+
+    // ---- LDS fragment offsets that do not depend on the chunk
+    // K, token tile t (tokens 16t + l16), step ks: bf16 dims 32*ks + 8*g4 (kaddr[0][0] + 64*ks +
+    // tile offset; region B for ks = 16, 17 via kaddrB); fp8 granule 2*ks + g4/2, half g4&1
+    // (kaddr[t][ks&3] + 128*(ks/4): the XOR only touches the low 3 granule bits)
+    int kaddr[2][4], kaddrB[2];
+    // V^T, dims 16*dt + l16 of the A operand: lane supplies token row 4*g4 + l16/4 (+16 for the
+    // second half of the tokens), bf16 dims 16*dt + 8*((l16&3)>>1) + 4*(l16&1) (vaddr[0] + 32*dt);
+    // fp8 tr8: token row (l16/2 < 4 ? 4*g4 + l16/2 : 16 + 4*g4 + l16/2 - 4), granule dt
+    // (vaddr[dt&7] + 128*(dt/8))
+    int vaddr[8];
+    if constexpr (!SPARSE) {
+        kaddr[0][0] = l16 * kRowA16 + g4 * 16;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            kaddrB[par] = kRegionB16 + l16 * 128 + (((4 * par + g4) ^ swzB(l16)) << 4);
+        vaddr[0] = (4 * g4 + (l16 >> 2)) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
+    } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kr = 16 * t + l16;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                kaddr[t][r4] = kr * kRec8Row + (((2 * r4 + (g4 >> 1)) ^ swz8(kr)) << 4) + (g4 & 1) * 8;
+        }
+        const int j = l16 >> 1;
+        const int vr = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vaddr[e] = vr * kRec8Row + ((e ^ swz8(vr)) << 4) + (l16 & 1) * 8;
+    }
+
+    bf16x8 qf[18];
+    f4 acc[32];
+    float m_run, l_run;
+    float m_lane;     // largest score this lane has seen in the pass (for a restart's reference)
+
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
+        const int nch = ceil_div(t1 - t0, kChunk);
+        // ---- Q fragments (B operand of S^T): dims 32*ks + 8*g4 .. +7 of this lane's row
+        {
+            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (row_ok ? row : 0)) * (kDqk * 2);
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
+                if (!row_ok) v = make_uint4(0, 0, 0, 0);
+                qf[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        m_run = -INFINITY;
+        const int limit = a.causal ? (L - a.s_q + row / a.h_q) : (L - 1);
+
+        // sparse: the split's index list goes to LDS once (no vector loads inside the pipeline)
+        if constexpr (SPARSE) {
+            for (int e = threadIdx.x; e < t1 - t0; e += kWaves * 64) lidx[e] = a.indices[(size_t)grp * a.topk + t0 + e];
+            __syncthreads();
+        }
+
+        // paged: page numbers of the segment, 64 at a time into a per-wave LDS window (a lookup
+        // then never waits on the vector-memory counter, which also counts the KV copies)
+        int bt_base = -1000000;
+        auto page_of = [&](int p) {
+            int* win = lpages + wave * 64;
+            if (p - bt_base >= 64 || p < bt_base) {
+                bt_base = p;
+                const int np = ceil_div(t1, kPage) - (t0 >> 6);
+                const int v = (lane < np - p) ? a.block_table[(size_t)grp * a.max_blocks + (t0 >> 6) + p + lane] : 0;
+                win[lane] = v;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            return __builtin_amdgcn_readfirstlane(win[p - bt_base]);
+        };
+
+        // ---- copies of one chunk, spread over the waves and over the MFMAs.  Chunks past the
+        // segment's end re-copy its last chunk into their (unused) slot, which keeps the number
+        // of copies per chunk fixed.
+        struct Plan {
+            const char* base;                      // paged: first row of the chunk in HBM
+            int idx[SPARSE ? C::OPS : 1];          // sparse: record of the row this lane fills, per copy
+            char* dst;
+            int nrows;
+        };
+        auto plan_for = [&](int c) {
+            Plan p;
+            const int cc = min(c, nch - 1);
+            p.dst = ring + (c % DEPTH) * C::BUF;
+            const int tb = t0 + cc * kChunk;
+            p.nrows = min(kChunk, t1 - tb);
+            if constexpr (!SPARSE) {
+                const int page = page_of(cc >> 1);
+                p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+            } else {
+                p.base = nullptr;
+                // recomputed per chunk on purpose: hoisted, these addresses would not fit in registers
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+#pragma unroll
+                for (int j = 0; j < C::OPS; ++j) {
+                    const int rr = (64 * (wave + kWaves * j) + ln) / 40;   // row of the granule this lane fills
+                    const int v = lidx[cc * kChunk + rr];     // inside the list; stale past its end
+                    p.idx[j] = rr < p.nrows ? v : -1;
+                }
+            }
+            return p;
+        };
+        auto copy_op = [&](const Plan& p, int j) {
+            if constexpr (!SPARSE) {
+                const int q = wave + kWaves * j;
+                if (j < kChunk / kWaves) {   // region A rows
+                    const int rr = min(q, p.nrows - 1);
+                    copy(p.base + rr * kRowBytes + (lane << 4), p.dst + q * kRowA16);
+                } else {                     // region B: 8 rows of 128 B per copy
+                    const int sl = (q - kChunk) * 64 + lane;
+                    const int br = sl >> 3;
+                    const int rr = min(br, p.nrows - 1);
+                    copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(br))) * 16,
+                         p.dst + kRegionB16 + (q - kChunk) * 1024);
+                }
+            } else {
+                const int gg = 64 * (wave + kWaves * j) + lane;
+                const int rr = gg / 40, slot_g = gg - 40 * rr;
+                const char* rec = p.idx[j] >= 0 ? static_cast<const char*>(a.kv) + (size_t)p.idx[j] * kRec
+                                                : reinterpret_cast<const char*>(kZeroRecord);
+                copy(rec + ((slot_g ^ swz8(rr)) << 4), p.dst + 1024 * (wave + kWaves * j));
+            }
+        };
+
+        // ---- LDS fragments
+        auto kfrag = [&](const char* buf, int t, int ks) -> bf16x8 {
+            if constexpr (!SPARSE) {
+                const int off = ks < 16 ? kaddr[0][0] + 64 * ks + 16 * kRowA16 * t
+                                        : kaddrB[ks & 1] + 16 * 128 * t;
+                return *reinterpret_cast<const bf16x8*>(buf + off);
+            } else {
+                const uint2 w = *reinterpret_cast<const uint2*>(buf + kaddr[t][ks & 3] + 128 * (ks >> 2));
+                return fp8x8_to_bf16(w.x, w.y);
+            }
+        };
+        auto vfrag = [&](const char* buf, int dt) -> bf16x8 {
+            if constexpr (!SPARSE) {
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0] + 32 * dt));
+                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0] + 32 * dt + 16 * kRowA16));
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                typedef int v2i __attribute__((ext_vector_type(2)));
+                const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(buf + vaddr[dt & 7] + 128 * (dt >> 3)));
+                return fp8x8_to_bf16((unsigned)w[0], (unsigned)w[1]);
+            }
+        };
+
+        // S^T of chunk c, tile t (tokens 16t..16t+15) x this wave's 16 rows: s2[t][ks&1], four
+        // independent MFMA chains.  side(ks) runs between the steps; fragments are read kPF steps
+        // ahead, since one wave per SIMD leaves nothing else to hide the LDS latency.
+        auto qk = [&](int c, f4 (&s2)[2][2], auto&& side) {
+            const char* buf = ring + (c % DEPTH) * C::BUF;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) s2[t][0] = s2[t][1] = f4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 kf[kPF][2];
+#pragma unroll
+            for (int i = 0; i < kPF - 1; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) kf[i][t] = kfrag(buf, t, i);
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                if (ks + kPF - 1 < 18)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) kf[(ks + kPF - 1) % kPF][t] = kfrag(buf, t, ks + kPF - 1);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) s2[t][ks & 1] = mfma16(kf[ks % kPF][t], qf[ks], s2[t][ks & 1]);
+                side(ks);
+            }
+        };
+        // O^T[16dt..16dt+15][rows] += V^T P^T over chunk c's 32 tokens, dt = 0..31; side(dt)
+        auto pv = [&](int c, bf16x8 pT, auto&& side) {
+            const char* buf = ring + (c % DEPTH) * C::BUF;
+            bf16x8 vf[kPF];
+#pragma unroll
+            for (int i = 0; i < kPF - 1; ++i) vf[i] = vfrag(buf, i);
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) {
+                if (dt + kPF - 1 < 32) vf[(dt + kPF - 1) % kPF] = vfrag(buf, dt + kPF - 1);
+                acc[dt] = mfma16(vf[dt % kPF], pT, acc[dt]);
+                side(dt);
+            }
+        };
+
+        // ---- softmax of one chunk, in steps that can be spread over MFMAs
+        struct Scores {
+            f4 s[2];        // masked, scaled (log2 units) S^T of tiles 0 and 1
+            float tsc[2][4];  // sparse: token scales
+            bool outgrown;  // a score exceeds its row's reference by more than kRefSlack
+        };
+        // step 0: sum the chains; 1/2: mask and scale tile t, compare with the reference;
+        // 3: rows without a reference take the chunk maximum (cross-lane, wave-local); 4: vote
+        auto mask_step = [&](int step, int c, const f4 (&s2)[2][2], Scores& S) {
+            const char* buf = ring + (c % DEPTH) * C::BUF;
+            const int tb = t0 + c * kChunk;
+            if (step == 0) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) S.s[t] = s2[t][0] + s2[t][1];
+                S.outgrown = false;
+            } else if (step == 1 || step == 2) {
+                const int t = step - 1;
+                const float cap = m_run + kRefSlack;      // -inf while the row has no reference
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = 16 * t + 4 * g4 + i;
+                    bool valid;
+                    float f = a.scale_log2;
+                    if constexpr (SPARSE) {
+                        const int v = lidx[c * kChunk + tok];   // inside the list; stale past its end
+                        const float sc = *reinterpret_cast<const float*>(buf + tok * kRec8Row + ((36 ^ swz8(tok)) << 4));
+                        valid = (tb + tok < t1) & (v >= 0);     // bitwise: no branches
+                        S.tsc[t][i] = valid ? sc : 0.f;
+                        f *= sc;
+                    } else {
+                        valid = (tb + tok < t1) & (tb + tok <= limit);
+                    }
+                    S.s[t][i] = valid ? S.s[t][i] * f : -INFINITY;
+                    S.outgrown = S.outgrown | ((m_run != -INFINITY) & (S.s[t][i] > cap));
+                }
+                m_lane = fmaxf(m_lane, fmaxf(fmaxf(S.s[t][0], S.s[t][1]), fmaxf(S.s[t][2], S.s[t][3])));
+            } else if (step == 3) {
+                if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
+                    float mx = fmaxf(fmaxf(fmaxf(S.s[0][0], S.s[0][1]), fmaxf(S.s[0][2], S.s[0][3])),
+                                     fmaxf(fmaxf(S.s[1][0], S.s[1][1]), fmaxf(S.s[1][2], S.s[1][3])));
+                    mx = fmaxf(mx, __shfl_xor(mx, 16));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    if (m_run == -INFINITY) m_run = mx;       // acc and l are still exactly 0
+                }
+            } else if (step == 4) {
+                const bool v = __builtin_amdgcn_ballot_w64(S.outgrown) != 0;
+                *(lane == 0 ? reinterpret_cast<float*>(&votes[(c & 1) * kWaves + wave]) : my_sink) = __int_as_float(v ? 1 : 0);
+            }
+        };
+        // step 0/1: probabilities of tile t; 2: P^T operand
+        struct Probs {
+            unsigned pk[4];
+        };
+        auto prob_step = [&](int step, const Scores& S, Probs& P) {
+            if (step == 0 || step == 1) {
+                const int t = step;
+                const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = exp2_fast(S.s[t][i] - m_use);
+                    l_run += p[i];
+                    if constexpr (SPARSE) p[i] *= S.tsc[t][i];
+                }
+                P.pk[2 * t] = pack_bf16x2(p[0], p[1]);
+                P.pk[2 * t + 1] = pack_bf16x2(p[2], p[3]);
+            }
+        };
+        // B operand element j of lane (l16, g4) is token (j < 4 ? 4*g4 + j : 16 + 4*g4 + j - 4):
+        // tile 0's then tile 1's S^T values of this lane
+        auto p_operand = [&](const Probs& P) {
+            return __builtin_bit_cast(bf16x8, make_uint4(P.pk[0], P.pk[1], P.pk[2], P.pk[3]));
+        };
+        // after the barrier that follows mask_step 4 of chunk c: any vote in the workgroup?
+        auto any_vote = [&](int c) {
+            int any = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) any |= votes[(c & 1) * kWaves + w];
+            return __builtin_amdgcn_readfirstlane(any) != 0;
+        };
+        auto no_side = [](int) {};
+        // copies are counted exactly (AHEAD-1 later chunks may still be in flight)
+        auto wait_chunk = [&]() {
+            if constexpr (AHEAD - 1 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((AHEAD - 1) * C::OPS) : "memory");
+        };
+
+        // ---- passes over the segment (a second one only after a restart vote).  A vote does not
+        // leave the chunk loop early: the pass runs to its end (its results are discarded), so
+        // the loop has a single exit and m_lane sees every score of the segment.
+        for (;;) {
+            l_run = 0.f;
+            m_lane = -INFINITY;
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+            bool restart = false;
+            Scores S;
+#pragma unroll
+            for (int c = 0; c < AHEAD; ++c) {
+                const Plan p = plan_for(c);
+#pragma unroll
+                for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+            }
+            // chunk 0: Q.K^T (copies of chunk AHEAD spread over it), mask
+            wait_chunk();
+            __syncthreads();
+            {
+                const Plan p = plan_for(AHEAD);
+                f4 s2[2][2];
+                qk(0, s2, [&](int ks) {
+                    if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                });
+#pragma unroll
+                for (int step = 0; step < 5; ++step) mask_step(step, 0, s2, S);
+            }
+            for (int k = 1; k < nch; ++k) {
+                wait_chunk();
+                // chunk k in LDS; votes of chunk k-1 visible; slot (k-2) % DEPTH free
+                __syncthreads();
+                restart = restart | any_vote(k - 1);
+                const Plan p = plan_for(k + AHEAD);
+                Probs P;
+                f4 s2[2][2];
+                // S^T(k) on the MFMAs while chunk k-1 becomes probabilities and chunk k+AHEAD is
+                // copied
+                qk(k, s2, [&](int ks) {
+                    if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                    if (ks == 3) prob_step(0, S, P);
+                    if (ks == 7) prob_step(1, S, P);
+                });
+                // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked
+                pv(k - 1, p_operand(P), [&](int dt) {
+                    if (dt == 1) mask_step(0, k, s2, S);
+                    if (dt == 3) mask_step(1, k, s2, S);
+                    if (dt == 5) mask_step(2, k, s2, S);
+                    if (dt == 7) mask_step(4, k, s2, S);
+                });
+                mask_step(3, k, s2, S);        // rare: rows still without a reference
+            }
+            __syncthreads();                   // votes of the last chunk visible
+            restart = restart | any_vote(nch - 1);
+            if (!restart) {
+                Probs P;
+                prob_step(0, S, P);
+                prob_step(1, S, P);
+                pv(nch - 1, p_operand(P), no_side);
+            }
+            // the copies past the segment's end land first
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (!restart) break;
+            // run the pass again with each row's maximum over the segment as reference
+            float mx = m_lane;
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_run = mx;
+            __syncthreads();
+        }
+
+        // ---- row sums across the four lanes of a row, then the output
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        if (row_ok) {
+            if (final_out) {
+                __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + row) * kDv + 4 * g4;
+#pragma unroll
+                for (int dt = 0; dt < 32; ++dt) {
+                    const f4 v = acc[dt] * inv;
+                    *reinterpret_cast<uint2*>(orow + dt * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+                if (g4 == 0) a.lse[(size_t)grp * a.M + row] = lse_v;
+            } else {
+                float* prow = a.part_o + ((size_t)slot * a.M + row) * kDv + 4 * g4;
+#pragma unroll
+                for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f4*>(prow + dt * 16) = acc[dt] * inv;
+                if (g4 == 0) a.part_lse[(size_t)slot * a.M + row] = lse_v;
+            }
+        }
+        __syncthreads();                    // LDS (ring, index list, votes) free for the next segment
+    };
+
+    if constexpr (!SPARSE) {
+        const int* meta = a.tile_meta + (size_t)item * kMetaInts;
+        const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
+        for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
+            const int L = a.seqlens[bb];
+            const int nb = ceil_div(L, kPage);
+            const int lo = (bb == b0) ? blk0 : 0;
+            const int hi = (bb == b1) ? blk1 : nb;
+            if (lo >= hi) continue;
+            const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
+            const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
+            run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+        }
+    } else {
+        const int grp = item / a.num_parts;
+        const int split = item % a.num_parts;
+        const int e0 = split * a.split_len;
+        const int e1 = min(e0 + a.split_len, a.topk);
+        if (e0 < e1) run_segment(grp, e0, e1, 0, a.num_parts == 1, grp * a.num_parts + split);
+    }
+}
+
+}  // namespace rows
+
+hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream) {
+    const int items = sparse ? a.batch * a.num_parts : a.num_parts;
+    const int R = (a.M + rows::kRowsWg - 1) / rows::kRowsWg;
+    const dim3 grid(items * R), block(rows::kWaves * 64);
+    if (sparse) {
+        if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<true, false>), grid, block, 0, stream, a);
+    } else {
+        if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<false, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mla

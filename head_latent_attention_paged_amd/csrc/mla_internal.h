@@ -63,6 +63,7 @@ void metadata_host(const int32_t* seqlens, int batch, int num_parts,
                    int32_t* tile_meta, int32_t* num_splits);
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_big(const AttnArgs& a, bool sparse, hipStream_t stream);
+hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream);

@@ -886,7 +886,8 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
 // --------------------------------------------------------------------------
 Tiling choose_tiling(int rows) {
     // <= 16 rows: one 16-row tile per workgroup (mla_decode_m16_kernel, or the 16-row sparse
-    // kernel); more rows: 32-row waves of mla_decode_big_kernel.
+    // kernel); up to 32 rows: one wave pair of mla_decode_big_kernel; more: 64-row workgroups
+    // of mla_decode_rows_kernel.
     Tiling t;
     if (rows <= 16) {
         t.nt = 1;
@@ -919,6 +920,7 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
         hipLaunchKernelGGL(mla_decode_m16_kernel, dim3(a.num_parts), dim3(256), 0, stream, a);
         return hipGetLastError();
     }
+    if (!sparse && a.M > 32) return launch_decode_rows(a, false, stream);
     if (a.M > 16) return launch_decode_big(a, sparse, stream);
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = t.row_groups;
