@@ -42,12 +42,14 @@ constexpr int kPF = MLA_BIG_PF;   // LDS fragment prefetch distance (MFMA steps)
 // (scores spanning over 44 nats) makes the workgroup restart the segment with the larger
 // reference.
 constexpr float kRefSlack = 64.f;
-// LDS swizzles for gfx950's 64 banks (256 B per cycle: 16 lanes of a 16-byte read, 32 lanes of an
-// 8-byte read).  bf16 region A: slot = granule ^ swzA(r) on the low 4 bits, so the 16 rows of a
-// K read and the 8 rows x 32 B of a V^T transposing read each hit distinct banks.  Region B
-// (128 B rows, two per 256 B): swzB separates the even and the odd rows.  fp8 rows (640 B):
-// swz8 keeps both the 16 rows of a K read and the 16 rows of a V^T tr8 read apart.
-__device__ __forceinline__ int swzA(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// LDS layouts, chosen by measuring the kernels' read patterns on gfx950 (64 banks): bf16 region A
+// holds dims 0..511 of a row in 1 KB at a 1056-byte row stride, unswizzled, which keeps both the
+// 16 rows x 64 B of a K read (ds_read_b128) and the 8 rows x 32 B of a V^T transposing read
+// conflict-free.  Region B (the RoPE dims, 128 B rows): slot = granule ^ swzB(r).  fp8 rows
+// (640 B): slot = granule ^ swz8(r) keeps the 16 rows of a K read and of a V^T tr8 read apart.
+constexpr int kRowA16 = 1056;
+constexpr int kRegionB16 = kChunk * kRowA16;
+constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
 
@@ -72,7 +74,7 @@ struct BigCfg {
     static constexpr int WAVES = 2 * PAIRS;
     static constexpr int ROWS_WG = 32 * PAIRS;
     static constexpr bool PIPELINED = PAIRS == 2;
-    static constexpr int BUF = SPARSE ? kChunk * kRec8Row : kChunkBytes;
+    static constexpr int BUF = SPARSE ? kChunk * kRec8Row : kChunk16;
     // ring slots.  Pipelined: chunk k-1 (P.V), k (Q.K^T) and DEPTH-2 chunks in flight.  Serial
     // (one pair, leaving room for a second workgroup per CU): DEPTH-1 chunks in flight.
     static constexpr int DEPTH = PAIRS == 2 ? (SPARSE ? 6 : 4) : (SPARSE ? 3 : 2);
@@ -138,30 +140,23 @@ void mla_decode_big_kernel(const AttnArgs a) {
 
     // fragment addresses that do not depend on the chunk
     const int krow = 16 * h + l16;               // this wave's K rows: tokens 16h..16h+15
-    int kaddr[4], kaddrB[2];                     // bf16: [ks&3] (+256 per ks/4 in region A)
-    int vaddr[2][8];                             // bf16 tr16: [half][dt&7] (+256 per dt/8)
+    int kaddr = 0, kaddrB[2];                    // bf16: region A + 64*ks, region B [ks&1]
+    int vaddr[2];                                // bf16 tr16: [half] + 32*dt
     // fp8: the XOR of the row layout only touches the low 3 granule bits, so fragment offsets
     // repeat with a constant 128 B stride: K step ks uses k8addr[ks&3] + 128*(ks/4), V^T tile
     // dt uses v8addr[dt&7] + 128*(dt/8)
     int k8addr[4], v8addr[8];
     if constexpr (!SPARSE) {
-        // K step ks reads granule 8*(ks/2) + 4*(ks&1) + g4 of row krow; the XOR only touches the
-        // low 4 granule bits, so steps ks and ks+4 differ by a constant 256 B
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            kaddr[r4] = krow * kRowA + (((8 * (r4 >> 1) + 4 * (r4 & 1) + g4) ^ swzA(krow)) << 4);
+        // K step ks reads dims 32*ks + 8*g4 .. +7 of row krow (ks >= 16: the RoPE dims)
+        kaddr = krow * kRowA16 + g4 * 16;
 #pragma unroll
         for (int par = 0; par < 2; ++par)
-            kaddrB[par] = kRegionB + krow * 128 + (((4 * par + g4) ^ swzB(krow)) << 4);
-        // V^T tile dt: lane supplies row 4*g4 + l16/4 (+16 for the upper tokens), granule
-        // 2*dt + ((l16&3)>>1), byte (l16&1)*8
+            kaddrB[par] = kRegionB16 + krow * 128 + (((4 * par + g4) ^ swzB(krow)) << 4);
+        // V^T tile dt: lane supplies row 4*g4 + l16/4 (+16 for the upper tokens), dims
+        // 16*dt + 8*((l16&3)>>1) + 4*(l16&1)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = 4 * g4 + (l16 >> 2) + 16 * hf;
-                vaddr[hf][e] = row * kRowA + (((2 * e + ((l16 & 3) >> 1)) ^ swzA(row)) << 4) + (l16 & 1) * 8;
-            }
+            vaddr[hf] = (4 * g4 + (l16 >> 2) + 16 * hf) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
     } else {
         // K: lane (g4, l16) reads 8 codes of token krow at dims 16*ks + 8*g4 .. (granule
         // 2*ks + g4/2, half g4&1)
@@ -257,13 +252,13 @@ void mla_decode_big_kernel(const AttnArgs a) {
                 const int q = wave + WAVES * j;
                 if (j < kChunk / WAVES) {   // region A rows (WAVES divides kChunk)
                     const int rr = min(q, p.nrows - 1);
-                    copy(p.base + rr * kRowBytes + ((lane ^ swzA(q)) << 4), p.dst + q * kRowA);
+                    copy(p.base + rr * kRowBytes + (lane << 4), p.dst + q * kRowA16);
                 } else {
                     const int sl = (q - kChunk) * 64 + lane;
                     const int row = sl >> 3;
                     const int rr = min(row, p.nrows - 1);
                     copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(row))) * 16,
-                         p.dst + kRegionB + (q - kChunk) * 1024);
+                         p.dst + kRegionB16 + (q - kChunk) * 1024);
                 }
             } else {
                 const int gg = 64 * (wave + WAVES * j) + lane;
@@ -277,7 +272,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
         // ---- LDS fragments
         auto kfrag = [&](const char* buf, int ks) -> bf16x8 {
             if constexpr (!SPARSE) {
-                const int off = ks < 16 ? kaddr[ks & 3] + 256 * (ks >> 2) : kaddrB[ks & 1];
+                const int off = ks < 16 ? kaddr + 64 * ks : kaddrB[ks & 1];
                 return *reinterpret_cast<const bf16x8*>(buf + off);
             } else {
                 const uint2 w = *reinterpret_cast<const uint2*>(buf + k8addr[ks & 3] + 128 * (ks >> 2));
@@ -286,9 +281,8 @@ void mla_decode_big_kernel(const AttnArgs a) {
         };
         auto vfrag = [&](const char* buf, int dt) -> bf16x8 {    // dt: global 16-dim tile 0..31
             if constexpr (!SPARSE) {
-                const int off = 256 * (dt >> 3);
-                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0][dt & 7] + off));
-                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[1][dt & 7] + off));
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0] + 32 * dt));
+                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[1] + 32 * dt));
                 return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
             } else {
                 typedef int v2i __attribute__((ext_vector_type(2)));

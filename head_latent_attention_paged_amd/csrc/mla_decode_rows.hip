@@ -31,7 +31,15 @@ namespace rows {
 constexpr int kWaves = 4;
 constexpr int kRowsWg = 16 * kWaves;
 constexpr int kRec8Row = 640;     // fp8 record row in LDS: 40 granules (36 codes, scale, padding)
-constexpr int kPF = 4;            // LDS fragment prefetch distance (MFMA steps)
+// LDS fragment prefetch distances (MFMA steps) of the K and the V^T reads
+#ifndef MLA_ROWS_KPF
+#define MLA_ROWS_KPF 4
+#endif
+#ifndef MLA_ROWS_VPF
+#define MLA_ROWS_VPF 4
+#endif
+constexpr int kPF = MLA_ROWS_KPF;
+constexpr int kVPF = MLA_ROWS_VPF;
 constexpr float kRefSlack = 64.f;
 
 // LDS layouts, chosen by measuring the decode kernels' read patterns on gfx950 (64 banks):
@@ -291,13 +299,13 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // O^T[16dt..16dt+15][rows] += V^T P^T over chunk c's 32 tokens, dt = 0..31; side(dt)
         auto pv = [&](int c, bf16x8 pT, auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
-            bf16x8 vf[kPF];
+            bf16x8 vf[kVPF];
 #pragma unroll
-            for (int i = 0; i < kPF - 1; ++i) vf[i] = vfrag(buf, i);
+            for (int i = 0; i < kVPF - 1; ++i) vf[i] = vfrag(buf, i);
 #pragma unroll
             for (int dt = 0; dt < 32; ++dt) {
-                if (dt + kPF - 1 < 32) vf[(dt + kPF - 1) % kPF] = vfrag(buf, dt + kPF - 1);
-                acc[dt] = mfma16(vf[dt % kPF], pT, acc[dt]);
+                if (dt + kVPF - 1 < 32) vf[(dt + kVPF - 1) % kVPF] = vfrag(buf, dt + kVPF - 1);
+                acc[dt] = mfma16(vf[dt % kVPF], pT, acc[dt]);
                 side(dt);
             }
         };
