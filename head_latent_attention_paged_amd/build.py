@@ -17,16 +17,28 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mla_kernels.hip", "mla_decode_big.hip", "mla_decode_rows.hip", "mla_api.cpp"]
+# Sources and their device-code flags.  Kernels whose loop-carried MFMA accumulators are read
+# by VALU code do better with the accumulators in VGPRs (-amdgpu-mfma-vgpr-form); the row-split
+# kernel keeps them in AGPRs, which only MFMAs touch inside its loop.
+VGPR_FORM = ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]
+SOURCES = {
+    "mla_kernels.hip": VGPR_FORM,
+    "mla_decode_big.hip": VGPR_FORM,
+    "mla_decode_rows.hip": [],
+    "mla_api.cpp": [],
+}
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def hipcc_cmd(out: str = LIB):
-    return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
-            "-Rpass-analysis=kernel-resource-usage",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+def compile_cmds(objdir: str):
+    cmds = []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmds.append(([HIPCC, *COMMON, *extra, "-Rpass-analysis=kernel-resource-usage",
+                      "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+                      os.path.join(CSRC, src), "-o", obj], obj))
+    return cmds
 
 
 def parse_resource_usage(text: str):
@@ -45,12 +57,27 @@ def parse_resource_usage(text: str):
 
 
 def build(verbose: bool = False) -> str:
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cmds = compile_cmds(objdir)
+    procs = [(subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), c) for c, _ in cmds]
+    remarks = []
+    failed = False
+    for p, c in procs:
+        out, err = p.communicate()
+        remarks.append(err)
+        if p.returncode != 0:
+            sys.stderr.write(out + err)
+            failed = True
+    if failed:
+        raise RuntimeError("hipcc failed compiling libmla.so sources")
     tmp = LIB + ".tmp"
-    proc = subprocess.run(hipcc_cmd(tmp), capture_output=True, text=True)
-    if proc.returncode != 0:
-        sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError("hipcc failed building libmla.so")
-    usage = parse_resource_usage(proc.stderr)
+    link = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in cmds], "-o", tmp],
+                          capture_output=True, text=True)
+    if link.returncode != 0:
+        sys.stderr.write(link.stdout + link.stderr)
+        raise RuntimeError("hipcc failed linking libmla.so")
+    usage = parse_resource_usage("\n".join(remarks))
     spills = {k: v for k, v in usage.items() if v.get("ScratchSize", 0) > 0}
     if verbose:
         for k, v in usage.items():
