@@ -124,6 +124,10 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         if constexpr (SHARED) dma16_shared(g, l);
         else dma16(g, l);
     };
+    auto copy_s = [&](const void* sbase, unsigned voff, const void* l) {
+        if constexpr (SHARED) dma16_s_shared(sbase, voff, l);
+        else dma16_s(sbase, voff, l);
+    };
 
     // ---- LDS fragment offsets that do not depend on the chunk
     // K, token tile t (tokens 16t + l16), step ks: bf16 dims 32*ks + 8*g4 (kaddr[0][0] + 64*ks +
@@ -233,7 +237,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 const int q = wave + kWaves * j;
                 if (j < kChunk / kWaves) {   // region A rows
                     const int rr = min(q, p.nrows - 1);
-                    copy(p.base + rr * kRowBytes + (lane << 4), p.dst + q * kRowA16);
+                    copy_s(p.base + rr * kRowBytes, (unsigned)lane << 4, p.dst + q * kRowA16);
                 } else {                     // region B: 8 rows of 128 B per copy
                     const int sl = (q - kChunk) * 64 + lane;
                     const int br = sl >> 3;
@@ -312,7 +316,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
 
         // ---- softmax of one chunk, in steps that can be spread over MFMAs
         struct Scores {
-            f4 s[2];        // masked, scaled (log2 units) S^T of tiles 0 and 1
+            f4 s[2];        // masked S^T of tiles 0 and 1: sparse scaled (log2 units), paged raw
+            float mxs;      // paged: this lane's largest scaled score of the chunk
             float tsc[2][4];  // sparse: token scales
             bool outgrown;  // a score exceeds its row's reference by more than kRefSlack
         };
@@ -325,6 +330,21 @@ void mla_decode_rows_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) S.s[t] = s2[t][0] + s2[t][1];
                 S.outgrown = false;
+            } else if (!SPARSE && (step == 1 || step == 2)) {
+                // raw scores; a positive scale commutes with the maximum and is applied in the
+                // exponent (the launcher sends other scales to another kernel)
+                const int t = step - 1;
+                const int bnd = min(t1, limit + 1) - tb - 16 * t - 4 * g4;    // valid: i < bnd
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S.s[t][i] = i < bnd ? S.s[t][i] : -INFINITY;
+                const float mt = fmaxf(fmaxf(S.s[t][0], S.s[t][1]), fmaxf(S.s[t][2], S.s[t][3]));
+                if (t == 0) {
+                    S.mxs = mt;
+                } else {
+                    S.mxs = fmaxf(S.mxs, mt) * a.scale_log2;
+                    S.outgrown = (m_run != -INFINITY) & (S.mxs > m_run + kRefSlack);
+                    m_lane = fmaxf(m_lane, S.mxs);
+                }
             } else if (step == 1 || step == 2) {
                 const int t = step - 1;
                 const float cap = m_run + kRefSlack;      // -inf while the row has no reference
@@ -348,8 +368,12 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 m_lane = fmaxf(m_lane, fmaxf(fmaxf(S.s[t][0], S.s[t][1]), fmaxf(S.s[t][2], S.s[t][3])));
             } else if (step == 3) {
                 if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
-                    float mx = fmaxf(fmaxf(fmaxf(S.s[0][0], S.s[0][1]), fmaxf(S.s[0][2], S.s[0][3])),
-                                     fmaxf(fmaxf(S.s[1][0], S.s[1][1]), fmaxf(S.s[1][2], S.s[1][3])));
+                    float mx;
+                    if constexpr (SPARSE)
+                        mx = fmaxf(fmaxf(fmaxf(S.s[0][0], S.s[0][1]), fmaxf(S.s[0][2], S.s[0][3])),
+                                   fmaxf(fmaxf(S.s[1][0], S.s[1][1]), fmaxf(S.s[1][2], S.s[1][3])));
+                    else
+                        mx = S.mxs;
                     mx = fmaxf(mx, __shfl_xor(mx, 16));
                     mx = fmaxf(mx, __shfl_xor(mx, 32));
                     if (m_run == -INFINITY) m_run = mx;       // acc and l are still exactly 0
@@ -370,7 +394,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = exp2_fast(S.s[t][i] - m_use);
+                    if constexpr (SPARSE) p[i] = exp2_fast(S.s[t][i] - m_use);
+                    else p[i] = exp2_fast(__builtin_fmaf(S.s[t][i], a.scale_log2, -m_use));
                     l_run += p[i];
                     if constexpr (SPARSE) p[i] *= S.tsc[t][i];
                 }

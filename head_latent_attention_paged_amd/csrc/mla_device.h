@@ -69,6 +69,17 @@ __device__ __forceinline__ void dma16_shared(const void* gptr, const void* lds_p
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
 }
 
+// The same two copies with the address split into a wave-uniform base (SGPRs) and a 32-bit
+// per-lane offset, so a row copy needs no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, const void* lds_ptr) {
+    const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_ptr;
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma16_s_shared(const void* sbase, unsigned voff, const void* lds_ptr) {
+    const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_ptr;
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+
 // Nontemporal 16-byte load of streamed KV data into registers.
 __device__ __forceinline__ uint4 load_nt(const void* p) {
     typedef unsigned u4v __attribute__((ext_vector_type(4)));

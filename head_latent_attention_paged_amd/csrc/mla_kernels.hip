@@ -920,7 +920,8 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
         hipLaunchKernelGGL(mla_decode_m16_kernel, dim3(a.num_parts), dim3(256), 0, stream, a);
         return hipGetLastError();
     }
-    if (!sparse && a.M > 32) return launch_decode_rows(a, false, stream);
+    // the row-split kernel applies the scale in the exponent, which needs it positive
+    if (!sparse && a.M > 32 && a.scale_log2 > 0.f) return launch_decode_rows(a, false, stream);
     if (a.M > 16) return launch_decode_big(a, sparse, stream);
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = t.row_groups;

@@ -228,6 +228,21 @@ def test_large_softmax_scale(env, h_q, scale):
         check_parity(o, l, o_ref, l_ref, "sparse scale %g h_q %d splits %d" % (scale, h_q, splits))
 
 
+@pytest.mark.parametrize("h_q", [16, 64])
+@pytest.mark.parametrize("scale", [0.0, -0.05])
+def test_non_positive_softmax_scale(env, h_q, scale):
+    """softmax_scale = 0 (uniform weights) and a negative scale, paged and sparse."""
+    _say("scale", scale, "h_q", h_q)
+    inp = make_paged(2, 2, h_q // 2, [300, 97], True, seed=600 + h_q, poison=True, softmax_scale=scale)
+    o, l = run_paged(env, inp)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    check_parity(o, l, o_ref, l_ref, "paged scale %g h_q %d" % (scale, h_q))
+    sp = make_sparse(2, 1, h_q, 512, 200, 0.1, seed=700 + h_q, softmax_scale=scale)
+    o, l = run_sparse(env, sp)
+    o_ref, l_ref = sparse_decode(sp.q, sp.kv, sp.indices, sp.softmax_scale)
+    check_parity(o, l, o_ref, l_ref, "sparse scale %g h_q %d" % (scale, h_q))
+
+
 # ----------------------------------------------------------------- full-size workloads
 def _sampled(o, l, o_ref, l_ref, rows, what):
     return check_parity(o[rows], l[rows], o_ref[rows], l_ref[rows], what)
