@@ -57,7 +57,7 @@ const char* mla_status_string(mla_status_t status);
 /*
  * Number of KV parts the tile scheduler splits one decode step into: about
  * one workgroup per compute unit once the row groups of a sequence are
- * counted.  num_cus <= 0 queries the current device.  Returns >= 1, a
+ * counted (two when s_q*h_q > 32).  num_cus <= 0 queries the current device.  Returns >= 1, a
  * multiple of 8 when num_cus is (so the part -> XCD mapping is exact).
  * Any value >= 1 is valid for the calls below; larger values force more
  * KV splits.
