@@ -214,6 +214,7 @@ mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens
     a.h_q = h_q;
     a.M = h_q;
     a.topk = topk;
+    a.kv_rows = num_tokens;
     a.num_parts = eff;
     a.split_len = sparse_split_len(topk, req);
     a.scale_log2 = softmax_scale * 1.4426950408889634f;

@@ -19,9 +19,11 @@
 // the row's maximum over the whole segment as reference (so at most once per segment).
 //
 // Sparse fp8: a chunk is 32 gathered records ("deepseek-ai/FlashMLA" project summary, section
-// 기술적 세부 사항: fp8 values plus a per-token scale, -1 = unused index).  The raw e4m3 codes
-// stay in LDS and are converted exactly to bf16 as fragments are read; the token scale
-// multiplies the score and the probability before P.V.
+// 기술적 세부 사항: fp8 values plus a per-token scale, -1 = unused index).  The workgroup loads
+// each record once into registers (bounds-checked buffer loads: an unused entry reads zeros),
+// converts the e4m3 codes exactly to bf16 and stores them in the same LDS layout as a paged
+// chunk, so the Q.K^T / P.V core is the paged one; the token scale multiplies the score and the
+// probability before P.V.
 #include "mla_device.h"
 
 namespace mla {
@@ -30,7 +32,6 @@ namespace rows {
 
 constexpr int kWaves = 4;
 constexpr int kRowsWg = 16 * kWaves;
-constexpr int kRec8Row = 640;     // fp8 record row in LDS: 40 granules (36 codes, scale, padding)
 // LDS fragment prefetch distances (MFMA steps) of the K and the V^T reads
 #ifndef MLA_ROWS_KPF
 #define MLA_ROWS_KPF 4
@@ -46,17 +47,18 @@ constexpr float kRefSlack = 64.f;
 // bf16 region A holds dims 0..511 of a row in 1 KB at a 1056-byte row stride, unswizzled: the
 // 16 rows x 64 B of a K read (ds_read_b128) and the 8 rows x 32 B of a V^T transposing read both
 // run conflict-free (at a 1024-byte stride every XOR swizzle tried left the K read at half rate).
-// Region B (the 64 RoPE dims, 128 B rows): slot = granule ^ swzB(r).  fp8 rows (640 B): slot =
-// granule ^ swz8(r) keeps the 16 rows of a K read and of a V^T tr8 read apart.
+// Region B (the 64 RoPE dims, 128 B rows): slot = granule ^ swzB(r).
 constexpr int kRowA16 = 1056;
 constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
 
-// An all-zero record: unused index entries are copied from it, so a chunk always costs the same
-// copies (exact s_waitcnt accounting) and its zero-weight V rows are finite.
-__device__ __attribute__((aligned(16))) const unsigned char kZeroRecord[kRec8Row] = {0};
+// Sparse gathers: a chunk's 32 records are 32 x 36 granules of 16 codes plus 32 scale granules,
+// 8 records per wave = 296 granule loads over 64 lanes x 5.  Index entries become byte offsets
+// into the record pool once per segment; an unused entry (or one past the list) gets kNoRecord,
+// which lies beyond the buffer's range, so its loads return zeros.
+constexpr int kGather = 5;
+constexpr unsigned kNoRecord = 0xFFFFF000u;
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exact
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
@@ -68,13 +70,14 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
 
 template <bool SPARSE>
 struct Cfg {
-    static constexpr int BUF = SPARSE ? kChunk * kRec8Row : kChunk16;
-    // ring slots: chunk k-1 (P.V), chunk k (Q.K^T) and AHEAD chunks in flight
-    static constexpr int DEPTH = SPARSE ? 6 : 4;
+    // a ring slot holds a bf16 chunk; sparse adds the 32 token scales (32-byte stride)
+    static constexpr int BUF = kChunk16 + (SPARSE ? kChunk * 32 : 0);
+    // ring slots: chunk k-1 (P.V), chunk k (Q.K^T) and, paged, AHEAD chunks in flight; sparse,
+    // chunk k+1, converted while chunk k+2 is gathered into registers
+    static constexpr int DEPTH = SPARSE ? 3 : 4;
     static constexpr int AHEAD = DEPTH - 2;
-    // copies per wave per chunk: bf16 32 rows of region A + 4 KB of region B; fp8 20 KB (one
-    // 64-lane copy fills 1 KB of the contiguous 640 B rows)
-    static constexpr int OPS = (SPARSE ? kChunk * kRec8Row / 1024 : kChunk + 4) / kWaves;
+    // paged copies per wave per chunk: 32 rows of region A + 4 KB of region B
+    static constexpr int OPS = (kChunk + 4) / kWaves;
     static constexpr int RING = DEPTH * BUF;
     static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;        // a split's index list
     static constexpr int PAGES = SPARSE ? 0 : kWaves * 64 * 4;            // per-wave page windows
@@ -130,34 +133,42 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     };
 
     // ---- LDS fragment offsets that do not depend on the chunk
-    // K, token tile t (tokens 16t + l16), step ks: bf16 dims 32*ks + 8*g4 (kaddr[0][0] + 64*ks +
-    // tile offset; region B for ks = 16, 17 via kaddrB); fp8 granule 2*ks + g4/2, half g4&1
-    // (kaddr[t][ks&3] + 128*(ks/4): the XOR only touches the low 3 granule bits)
-    int kaddr[2][4], kaddrB[2];
+    // K, token tile t (tokens 16t + l16), step ks: dims 32*ks + 8*g4 (kaddr + 64*ks + tile
+    // offset; region B for ks = 16, 17 via kaddrB)
+    int kaddr, kaddrB[2];
     // V^T, dims 16*dt + l16 of the A operand: lane supplies token row 4*g4 + l16/4 (+16 for the
-    // second half of the tokens), bf16 dims 16*dt + 8*((l16&3)>>1) + 4*(l16&1) (vaddr[0] + 32*dt);
-    // fp8 tr8: token row (l16/2 < 4 ? 4*g4 + l16/2 : 16 + 4*g4 + l16/2 - 4), granule dt
-    // (vaddr[dt&7] + 128*(dt/8))
-    int vaddr[8];
-    if constexpr (!SPARSE) {
-        kaddr[0][0] = l16 * kRowA16 + g4 * 16;
+    // second half of the tokens), dims 16*dt + 8*((l16&3)>>1) + 4*(l16&1) (vaddr + 32*dt)
+    int vaddr;
+    kaddr = l16 * kRowA16 + g4 * 16;
 #pragma unroll
-        for (int par = 0; par < 2; ++par)
-            kaddrB[par] = kRegionB16 + l16 * 128 + (((4 * par + g4) ^ swzB(l16)) << 4);
-        vaddr[0] = (4 * g4 + (l16 >> 2)) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
-    } else {
+    for (int par = 0; par < 2; ++par)
+        kaddrB[par] = kRegionB16 + l16 * 128 + (((4 * par + g4) ^ swzB(l16)) << 4);
+    vaddr = (4 * g4 + (l16 >> 2)) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
+
+    // ---- sparse gathers: load i of this lane fetches granule gran of record tok (of the chunk)
+    // and stores it at g_dst[i] of the ring slot: codes as 16 bf16 (32 B, the second half at
+    // g_dst ^ 16), a scale granule as its raw first dword.  Load 4 of lanes 40..63 repeats that
+    // of lanes 16..39 (same data to the same place), which keeps every lane busy without a branch.
+    int g_tok[SPARSE ? kGather : 1], g_off[SPARSE ? kGather : 1], g_dst[SPARSE ? kGather : 1];
+    bool scale_lane = false;      // load 4 of this lane fetches a scale granule
+    if constexpr (SPARSE) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int kr = 16 * t + l16;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-                kaddr[t][r4] = kr * kRec8Row + (((2 * r4 + (g4 >> 1)) ^ swz8(kr)) << 4) + (g4 & 1) * 8;
+        for (int i = 0; i < kGather; ++i) {
+            const int sl = 64 * i + lane - ((i == kGather - 1 && lane >= 40) ? 24 : 0);
+            const bool scl = sl >= 8 * 36;
+            if (i == kGather - 1) scale_lane = scl;
+            const int tok = 8 * wave + (scl ? sl - 8 * 36 : sl / 36);
+            const int gran = scl ? 36 : sl % 36;
+            g_tok[i] = tok * 4;
+            g_off[i] = gran * 16;
+            g_dst[i] = scl ? kChunk16 + tok * 32
+                     : gran < 32 ? tok * kRowA16 + gran * 32
+                                 : kRegionB16 + tok * 128 + (((2 * (gran - 32)) ^ swzB(tok)) << 4);
         }
-        const int j = l16 >> 1;
-        const int vr = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vaddr[e] = vr * kRec8Row + ((e ^ swz8(vr)) << 4) + (l16 & 1) * 8;
     }
+    // sparse record pool as a raw buffer (offsets past its end read zeros)
+    const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.kv), (short)0, SPARSE ? (int)(unsigned)(a.kv_rows * kRec) : 0, 0x00020000);
 
     bf16x8 qf[18];
     f4 acc[32];
@@ -179,9 +190,13 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         m_run = -INFINITY;
         const int limit = a.causal ? (L - a.s_q + row / a.h_q) : (L - 1);
 
-        // sparse: the split's index list goes to LDS once (no vector loads inside the pipeline)
+        // sparse: the split's index list goes to LDS once, as record byte offsets (kNoRecord for
+        // unused entries and up to the end of the last chunk)
         if constexpr (SPARSE) {
-            for (int e = threadIdx.x; e < t1 - t0; e += kWaves * 64) lidx[e] = a.indices[(size_t)grp * a.topk + t0 + e];
+            for (int e = threadIdx.x; e < nch * kChunk; e += kWaves * 64) {
+                const int v = e < t1 - t0 ? a.indices[(size_t)grp * a.topk + t0 + e] : -1;
+                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)((unsigned)v * kRec) : (int)kNoRecord;
+            }
             __syncthreads();
         }
 
@@ -200,12 +215,11 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             return __builtin_amdgcn_readfirstlane(win[p - bt_base]);
         };
 
-        // ---- copies of one chunk, spread over the waves and over the MFMAs.  Chunks past the
-        // segment's end re-copy its last chunk into their (unused) slot, which keeps the number
+        // ---- paged copies of one chunk, spread over the waves and over the MFMAs.  Chunks past
+        // the segment's end re-copy its last chunk into their (unused) slot, which keeps the number
         // of copies per chunk fixed.
         struct Plan {
-            const char* base;                      // paged: first row of the chunk in HBM
-            int idx[SPARSE ? C::OPS : 1];          // sparse: record of the row this lane fills, per copy
+            const char* base;                      // first row of the chunk in HBM
             char* dst;
             int nrows;
         };
@@ -215,67 +229,61 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             p.dst = ring + (c % DEPTH) * C::BUF;
             const int tb = t0 + cc * kChunk;
             p.nrows = min(kChunk, t1 - tb);
+            p.base = nullptr;
             if constexpr (!SPARSE) {
                 const int page = page_of(cc >> 1);
                 p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
-            } else {
-                p.base = nullptr;
-                // recomputed per chunk on purpose: hoisted, these addresses would not fit in registers
-                int ln = lane;
-                asm volatile("" : "+v"(ln));
-#pragma unroll
-                for (int j = 0; j < C::OPS; ++j) {
-                    const int rr = (64 * (wave + kWaves * j) + ln) / 40;   // row of the granule this lane fills
-                    const int v = lidx[cc * kChunk + rr];     // inside the list; stale past its end
-                    p.idx[j] = rr < p.nrows ? v : -1;
-                }
             }
             return p;
         };
         auto copy_op = [&](const Plan& p, int j) {
-            if constexpr (!SPARSE) {
-                const int q = wave + kWaves * j;
-                if (j < kChunk / kWaves) {   // region A rows
-                    const int rr = min(q, p.nrows - 1);
-                    copy_s(p.base + rr * kRowBytes, (unsigned)lane << 4, p.dst + q * kRowA16);
-                } else {                     // region B: 8 rows of 128 B per copy
-                    const int sl = (q - kChunk) * 64 + lane;
-                    const int br = sl >> 3;
-                    const int rr = min(br, p.nrows - 1);
-                    copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(br))) * 16,
-                         p.dst + kRegionB16 + (q - kChunk) * 1024);
-                }
-            } else {
-                const int gg = 64 * (wave + kWaves * j) + lane;
-                const int rr = gg / 40, slot_g = gg - 40 * rr;
-                const char* rec = p.idx[j] >= 0 ? static_cast<const char*>(a.kv) + (size_t)p.idx[j] * kRec
-                                                : reinterpret_cast<const char*>(kZeroRecord);
-                copy(rec + ((slot_g ^ swz8(rr)) << 4), p.dst + 1024 * (wave + kWaves * j));
+            const int q = wave + kWaves * j;
+            if (j < kChunk / kWaves) {   // region A rows
+                const int rr = min(q, p.nrows - 1);
+                copy_s(p.base + rr * kRowBytes, (unsigned)lane << 4, p.dst + q * kRowA16);
+            } else {                     // region B: 8 rows of 128 B per copy
+                const int sl = (q - kChunk) * 64 + lane;
+                const int br = sl >> 3;
+                const int rr = min(br, p.nrows - 1);
+                copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(br))) * 16,
+                     p.dst + kRegionB16 + (q - kChunk) * 1024);
             }
+        };
+
+        // ---- sparse: load i of chunk c into registers; conversion of those registers into chunk
+        // c's ring slot.  Chunks past the segment's end gather its last chunk again (unused slot).
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 gv[SPARSE ? kGather : 1];
+        unsigned g_rec4 = 0;        // record offset behind load 4 (marks an unused entry's scale)
+        auto gather = [&](int c, int i) {
+            const int cc = min(c, nch - 1);
+            const unsigned rec = *reinterpret_cast<const unsigned*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
+            if (i == kGather - 1) g_rec4 = rec;
+            gv[i] = __builtin_amdgcn_raw_buffer_load_b128(pool, rec + (unsigned)g_off[i], 0, SHARED ? 0 : 2);
+        };
+        auto convert = [&](int c, int i) {
+            char* slot = ring + (c % DEPTH) * C::BUF;
+            const u32x4 r = gv[i];
+            uint4 lo = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.x, r.y));
+            const uint4 hi = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.z, r.w));
+            if (i == kGather - 1) {
+                // scale granule: the raw fp32 scale, NaN for an unused entry (masked off)
+                const unsigned sc = g_rec4 >= kNoRecord ? 0x7fc00000u : r.x;
+                lo.x = scale_lane ? sc : lo.x;
+            }
+            *reinterpret_cast<uint4*>(slot + g_dst[i]) = lo;
+            *reinterpret_cast<uint4*>(slot + (g_dst[i] ^ 16)) = hi;
         };
 
         // ---- LDS fragments
         auto kfrag = [&](const char* buf, int t, int ks) -> bf16x8 {
-            if constexpr (!SPARSE) {
-                const int off = ks < 16 ? kaddr[0][0] + 64 * ks + 16 * kRowA16 * t
-                                        : kaddrB[ks & 1] + 16 * 128 * t;
-                return *reinterpret_cast<const bf16x8*>(buf + off);
-            } else {
-                const uint2 w = *reinterpret_cast<const uint2*>(buf + kaddr[t][ks & 3] + 128 * (ks >> 2));
-                return fp8x8_to_bf16(w.x, w.y);
-            }
+            const int off = ks < 16 ? kaddr + 64 * ks + 16 * kRowA16 * t : kaddrB[ks & 1] + 16 * 128 * t;
+            return *reinterpret_cast<const bf16x8*>(buf + off);
         };
         auto vfrag = [&](const char* buf, int dt) -> bf16x8 {
-            if constexpr (!SPARSE) {
-                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0] + 32 * dt));
-                const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr[0] + 32 * dt + 16 * kRowA16));
-                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-            } else {
-                typedef int v2i __attribute__((ext_vector_type(2)));
-                const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(buf + vaddr[dt & 7] + 128 * (dt >> 3)));
-                return fp8x8_to_bf16((unsigned)w[0], (unsigned)w[1]);
-            }
+            const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr + 32 * dt));
+            const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr + 32 * dt + 16 * kRowA16));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
         };
 
         // S^T of chunk c, tile t (tokens 16t..16t+15) x this wave's 16 rows: s2[t][ks&1], four
@@ -354,9 +362,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                     bool valid;
                     float f = a.scale_log2;
                     if constexpr (SPARSE) {
-                        const int v = lidx[c * kChunk + tok];   // inside the list; stale past its end
-                        const float sc = *reinterpret_cast<const float*>(buf + tok * kRec8Row + ((36 ^ swz8(tok)) << 4));
-                        valid = (tb + tok < t1) & (v >= 0);     // bitwise: no branches
+                        // NaN marks an unused entry or a position past the list
+                        const float sc = *reinterpret_cast<const float*>(buf + kChunk16 + tok * 32);
+                        valid = sc == sc;
                         S.tsc[t][i] = valid ? sc : 0.f;
                         f *= sc;
                     } else {
@@ -432,26 +440,41 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             for (int dt = 0; dt < 32; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
             bool restart = false;
             Scores S;
+            if constexpr (!SPARSE) {
 #pragma unroll
-            for (int c = 0; c < AHEAD; ++c) {
-                const Plan p = plan_for(c);
+                for (int c = 0; c < AHEAD; ++c) {
+                    const Plan p = plan_for(c);
 #pragma unroll
-                for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+                    for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+                }
+                wait_chunk();
+            } else {
+#pragma unroll
+                for (int i = 0; i < kGather; ++i) gather(0, i);
+#pragma unroll
+                for (int i = 0; i < kGather; ++i) convert(0, i);
+#pragma unroll
+                for (int i = 0; i < kGather; ++i) gather(1, i);
             }
-            // chunk 0: Q.K^T (copies of chunk AHEAD spread over it), mask
-            wait_chunk();
+            // chunk 0: Q.K^T (copies of chunk AHEAD, or the conversion of chunk 1 and the gathers
+            // of chunk 2, spread over it), mask
             __syncthreads();
             {
                 const Plan p = plan_for(AHEAD);
                 f4 s2[2][2];
                 qk(0, s2, [&](int ks) {
-                    if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                    if constexpr (!SPARSE) {
+                        if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                    } else if ((ks & 1) == 0 && ks / 2 < kGather) {
+                        convert(1, ks / 2);
+                        gather(2, ks / 2);
+                    }
                 });
 #pragma unroll
                 for (int step = 0; step < 5; ++step) mask_step(step, 0, s2, S);
             }
             for (int k = 1; k < nch; ++k) {
-                wait_chunk();
+                if constexpr (!SPARSE) wait_chunk();
                 // chunk k in LDS; votes of chunk k-1 visible; slot (k-2) % DEPTH free
                 __syncthreads();
                 restart = restart | any_vote(k - 1);
@@ -459,9 +482,14 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 Probs P;
                 f4 s2[2][2];
                 // S^T(k) on the MFMAs while chunk k-1 becomes probabilities and chunk k+AHEAD is
-                // copied
+                // copied (sparse: chunk k+1 is converted and chunk k+2 gathered)
                 qk(k, s2, [&](int ks) {
-                    if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                    if constexpr (!SPARSE) {
+                        if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
+                    } else if ((ks & 1) == 0 && ks / 2 < kGather) {
+                        convert(k + 1, ks / 2);
+                        gather(k + 2, ks / 2);
+                    }
                     if (ks == 3) prob_step(0, S, P);
                     if (ks == 7) prob_step(1, S, P);
                 });

@@ -922,6 +922,8 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     }
     // the row-split kernel applies the scale in the exponent, which needs it positive
     if (!sparse && a.M > 32 && a.scale_log2 > 0.f) return launch_decode_rows(a, false, stream);
+    // sparse: the row-split kernel addresses the record pool with 32-bit buffer offsets
+    if (sparse && a.M > 32 && a.kv_rows * kRec <= kRowsSparseMaxPool) return launch_decode_rows(a, true, stream);
     if (a.M > 16) return launch_decode_big(a, sparse, stream);
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = t.row_groups;

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from mla_inputs import make_config, make_paged, make_sparse
-from mla_inputs.gen import bf16_bits_from_f32, bf16_bits_to_f32
+from mla_inputs.gen import bf16_bits_from_f32, bf16_bits_to_f32, quantize_rows_e4m3
 from oracle import paged_decode, sparse_decode
 from tests.helpers import check_parity, dev_bf16, dev_i32, dev_u8, to_host
 
@@ -160,8 +160,10 @@ def test_sparse_cases(env, case):
     check_parity(o, l, o_ref, l_ref, str(case))
 
 
-def test_sparse_all_skipped_and_duplicates(env):
-    inp = make_sparse(2, 2, 16, 300, 64, 0.0, seed=31)
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_sparse_all_skipped_and_duplicates(env, h_q):
+    _say("sparse skip/dup h_q", h_q)
+    inp = make_sparse(2, 2, h_q, 300, 64, 0.0, seed=31)
     inp.indices[0, 1, :] = -1                         # a query that reads nothing
     inp.indices[1, 0, 10:20] = inp.indices[1, 0, 0]   # repeated rows count repeatedly
     for splits in (0, 1, 2):
@@ -211,6 +213,46 @@ def test_paged_wide_score_range(env, case):
     o, l = run_paged(env, inp, P)
     o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
     check_parity(o, l, o_ref, l_ref, "ramp " + str(case))
+
+
+def _ramp_sparse(inp, top, seed=9):
+    """Sparse input whose scores move linearly along each query's index list, from ~0 to ~`top`
+    nats (falling for top < 0); one query token per sequence, so every record has one position."""
+    assert inp.s_q == 1
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(576)
+    u /= np.linalg.norm(u)
+    sigma_inv = 1.0 / inp.softmax_scale
+    qf = u * sigma_inv + 0.02 * sigma_inv * rng.standard_normal(inp.q.shape)
+    inp.q = bf16_bits_from_f32(qf.astype(np.float32))
+    x = 0.5 * rng.standard_normal((inp.num_tokens, 576))
+    for b in range(inp.batch):
+        lst = inp.indices[b, 0]
+        for e, r in enumerate(lst):
+            if r >= 0:
+                f = (e + 1) / len(lst) if top > 0 else (len(lst) - e) / len(lst)
+                x[r] += abs(top) * f * u
+    inp.kv = quantize_rows_e4m3(x.astype(np.float32))
+    return inp
+
+
+SPARSE_RAMP_CASES = [
+    # batch, h_q, tokens_per_seq, topk, p_invalid, top (nats), splits
+    (2, 64, 3000, 2048, 0.05, 150.0, 0),
+    (2, 64, 3000, 2048, 0.05, -150.0, 0),
+    (2, 128, 2500, 1500, 0.1, 150.0, 2),
+    (2, 32, 2500, 1500, 0.1, 150.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_RAMP_CASES, ids=[str(i) for i in range(len(SPARSE_RAMP_CASES))])
+def test_sparse_wide_score_range(env, case):
+    batch, h_q, T, topk, p, top, splits = case
+    _say("sparse ramp", case)
+    inp = _ramp_sparse(make_sparse(batch, 1, h_q, T, topk, p, seed=800 + h_q), top)
+    o, l = run_sparse(env, inp, splits)
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+    check_parity(o, l, o_ref, l_ref, "sparse ramp " + str(case))
 
 
 @pytest.mark.parametrize("h_q,scale", [(16, 2.5), (64, 2.5), (16, 0.7), (64, 0.7)])
