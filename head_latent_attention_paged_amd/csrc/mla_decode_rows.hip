@@ -1,22 +1,28 @@
 // gfx950 decode kernel for many query rows per KV stream: paged s_q*h_q > 32, sparse h_q > 32.
 //
-// A workgroup holds 64 query rows in four waves (one per SIMD); each wave owns 16 rows end to
-// end: S^T = K Q^T for all 32 tokens of a chunk (tokens on the MFMA M side, "FlashMLA-ETAP:
-// Efficient Transpose Attention Pipeline ...", section 핵심 메커니즘, transposed form), the
-// online softmax of its rows, and O^T += V^T P^T over all 512 value dims.  The two 16-token
-// S^T tiles of a chunk hold, lane by lane, exactly the P^T elements this lane feeds to the
-// 16x16x32 P.V MFMA (with V^T read in the matching token order), so a wave needs no data from
-// another wave: the only workgroup barrier per chunk guards the shared ring of KV chunks.
+// A workgroup holds 64 query rows in eight waves, two per SIMD, so that one wave's LDS, MFMA and
+// barrier latencies overlap with the other's work.  Waves w and w^4 share 16 rows (row block
+// w & 3) and split the work of a 32-token chunk between them: wave half h = w >> 2 computes
+// S^T = K Q^T for tokens 16h..16h+15 (tokens on the MFMA M side, "FlashMLA-ETAP: Efficient
+// Transpose Attention Pipeline ...", section 핵심 메커니즘, transposed form) and the online
+// softmax of that tile, then O^T += V^T P^T for value dims 256h..256h+255 over all 32 tokens.
+// The 16-token S^T tile holds, lane by lane, exactly half of the P^T elements this lane feeds
+// to the 16x16x32 P.V MFMA (with V^T read in the matching token order); the other half comes
+// from the partner wave through LDS.  The two value halves split the output as the pages'
+// design splits it across two warpgroups.
 //
-// The chunk loop is software-pipelined: iteration k multiplies S^T(k) while it turns S^T(k-1)
-// into probabilities and copies a later chunk, then multiplies O^T += V^T(k-1) P^T(k-1) while
-// it masks S^T(k).  Chunks travel HBM -> LDS by direct copies, spread over all four waves.
+// Chunk loop, iteration k: Q.K^T(k) of the own tile (the copies of a later chunk spread over
+// it), then P.V(k-1) with P(k-1) from both waves while S^T(k) is masked and turned into
+// probabilities, which go to LDS for the partner.  One workgroup barrier per chunk guards the
+// shared ring of KV chunks and the exchanged probabilities.
 //
-// Softmax reference: a row's reference is its first finite chunk maximum and never moves inside
-// a pass, so the accumulators are touched only by MFMAs.  p = 2^(s - m) <= 2^kRefSlack keeps
-// bf16 P and the fp32 sums finite; a score that outgrows its row's reference by more (scores
-// spanning over 44 nats) makes the workgroup finish the pass, discard it and run it again with
-// the row's maximum over the whole segment as reference (so at most once per segment).
+// Softmax reference: a row's reference is the maximum of its first chunk (both tiles, which
+// each wave of the pair computes for that chunk, so the two agree bit for bit) and never moves
+// inside a pass, so the accumulators are touched only by MFMAs.  p = 2^(s - m) <= 2^kRefSlack
+// keeps bf16 P and the fp32 sums finite; a score that outgrows its row's reference by more
+// (or a finite score in a row whose first chunk had none) makes the workgroup finish the pass,
+// discard it and run it again with the row's maximum over the whole segment as reference (so
+// at most once per segment).
 //
 // Sparse fp8: a chunk is 32 gathered records ("deepseek-ai/FlashMLA" project summary, section
 // 기술적 세부 사항: fp8 values plus a per-token scale, -1 = unused index).  The workgroup loads
@@ -30,8 +36,8 @@ namespace mla {
 
 namespace rows {
 
-constexpr int kWaves = 4;
-constexpr int kRowsWg = 16 * kWaves;
+constexpr int kWaves = 8;
+constexpr int kRowsWg = 64;
 // LDS fragment prefetch distances (MFMA steps) of the K and the V^T reads
 #ifndef MLA_ROWS_KPF
 #define MLA_ROWS_KPF 4
@@ -53,11 +59,12 @@ constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
 
-// Sparse gathers: a chunk's 32 records are 32 x 36 granules of 16 codes plus 32 scale granules,
-// 8 records per wave = 296 granule loads over 64 lanes x 5.  Index entries become byte offsets
-// into the record pool once per segment; an unused entry (or one past the list) gets kNoRecord,
-// which lies beyond the buffer's range, so its loads return zeros.
-constexpr int kGather = 5;
+// Sparse gathers: a chunk's 32 records are 32 x 36 granules of 16 codes plus 32 scale granules;
+// a wave loads 4 records = 148 granules with 3 loads of 64 lanes (slots 148..191 repeat slots
+// 84..127: same data to the same place).  Index entries become byte offsets into the record
+// pool once per segment; an unused entry (or one past the list) gets kNoRecord, which lies
+// beyond the buffer's range, so its loads return zeros.
+constexpr int kGather = 3;
 constexpr unsigned kNoRecord = 0xFFFFF000u;
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exact
@@ -76,18 +83,19 @@ struct Cfg {
     // chunk k+1, converted while chunk k+2 is gathered into registers
     static constexpr int DEPTH = SPARSE ? 3 : 4;
     static constexpr int AHEAD = DEPTH - 2;
-    // paged copies per wave per chunk: 32 rows of region A + 4 KB of region B
-    static constexpr int OPS = (kChunk + 4) / kWaves;
+    // paged copies per wave per chunk: 32 rows of region A + 4 KB of region B = 36 x 1 KB over
+    // eight waves, the last four repeated
+    static constexpr int OPS = 5;
     static constexpr int RING = DEPTH * BUF;
     static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;        // a split's index list
     static constexpr int PAGES = SPARSE ? 0 : kWaves * 64 * 4;            // per-wave page windows
+    static constexpr int PX = 2 * kWaves * 64 * 8;                        // exchanged P, by chunk parity
     static constexpr int VOTES = 2 * kWaves * 4;                          // restart votes, by chunk parity
-    static constexpr int SINK = kWaves * 64 * 4;                          // targets of masked-off lanes
-    static constexpr int LDS = RING + IDX + PAGES + VOTES + SINK;
+    static constexpr int LDS = RING + IDX + PAGES + PX + VOTES;
 };
 
 template <bool SPARSE, bool SHARED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_rows_kernel(const AttnArgs a) {
     using C = Cfg<SPARSE>;
     constexpr int DEPTH = C::DEPTH;
@@ -96,13 +104,16 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     char* ring = smem;
     int* lidx = reinterpret_cast<int*>(smem + C::RING);
     int* lpages = reinterpret_cast<int*>(smem + C::RING + C::IDX);
-    int* votes = reinterpret_cast<int*>(smem + C::RING + C::IDX + C::PAGES);
-    float* sink = reinterpret_cast<float*>(smem + C::RING + C::IDX + C::PAGES + C::VOTES);
+    uint2* px = reinterpret_cast<uint2*>(smem + C::RING + C::IDX + C::PAGES);
+    int* votes = reinterpret_cast<int*>(smem + C::RING + C::IDX + C::PAGES + C::PX);
+    float* red = reinterpret_cast<float*>(px);      // end-of-pass exchanges (P no longer read)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rb = wave & 3;           // row block
+    const int h = wave >> 2;           // token half of Q.K^T, value half of P.V
+    const int partner = wave ^ 4;
     const int g4 = lane >> 4, l16 = lane & 15;
-    float* my_sink = sink + wave * 64 + lane;
 
     // ---- work item -> (part or sparse split, row group); row groups of one item share an XCD
     const int R = ceil_div(a.M, kRowsWg);
@@ -119,7 +130,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             rg = bid % R;
         }
     }
-    const int row = rg * kRowsWg + 16 * wave + l16;     // this lane's query row (B / C column)
+    const int row = rg * kRowsWg + 16 * rb + l16;     // this lane's query row (B / C column)
     const bool row_ok = row < a.M;
     // row groups that re-read the same KV keep it in L2 (default policy); a single reader
     // streams it (nontemporal)
@@ -133,37 +144,32 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     };
 
     // ---- LDS fragment offsets that do not depend on the chunk
-    // K, token tile t (tokens 16t + l16), step ks: dims 32*ks + 8*g4 (kaddr + 64*ks + tile
-    // offset; region B for ks = 16, 17 via kaddrB)
-    int kaddr, kaddrB[2];
-    // V^T, dims 16*dt + l16 of the A operand: lane supplies token row 4*g4 + l16/4 (+16 for the
-    // second half of the tokens), dims 16*dt + 8*((l16&3)>>1) + 4*(l16&1) (vaddr + 32*dt)
-    int vaddr;
-    kaddr = l16 * kRowA16 + g4 * 16;
+    // K, token tile t (tokens 16t + l16), step ks: dims 32*ks + 8*g4 (kaddr + 64*ks + 16*kRowA16*t;
+    // region B for ks = 16, 17 via kaddrB + 2048*t)
+    const int kaddr = l16 * kRowA16 + g4 * 16;
+    int kaddrB[2];
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-        kaddrB[par] = kRegionB16 + l16 * 128 + (((4 * par + g4) ^ swzB(l16)) << 4);
-    vaddr = (4 * g4 + (l16 >> 2)) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
+    for (int par = 0; par < 2; ++par) kaddrB[par] = kRegionB16 + l16 * 128 + (((4 * par + g4) ^ swzB(l16)) << 4);
+    // V^T, dims 16*dt + l16 of the A operand, dt = 16h + j: lane supplies token row 4*g4 + l16/4
+    // (+16 for the second half of the tokens), dims 16*dt + 8*((l16&3)>>1) + 4*(l16&1)
+    const int vaddr = (4 * g4 + (l16 >> 2)) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8 + 32 * 16 * h;
 
-    // ---- sparse gathers: load i of this lane fetches granule gran of record tok (of the chunk)
-    // and stores it at g_dst[i] of the ring slot: codes as 16 bf16 (32 B, the second half at
-    // g_dst ^ 16), a scale granule as its raw first dword.  Load 4 of lanes 40..63 repeats that
-    // of lanes 16..39 (same data to the same place), which keeps every lane busy without a branch.
+    // ---- sparse gathers: load i of this lane fetches granule g_off/16 of record g_tok/4 of the
+    // chunk and stores it at g_dst of the ring slot: codes as 16 bf16 (32 B, the second half at
+    // g_dst ^ 16), a scale granule as its raw first dword
     int g_tok[SPARSE ? kGather : 1], g_off[SPARSE ? kGather : 1], g_dst[SPARSE ? kGather : 1];
-    bool scale_lane = false;      // load 4 of this lane fetches a scale granule
     if constexpr (SPARSE) {
 #pragma unroll
         for (int i = 0; i < kGather; ++i) {
-            const int sl = 64 * i + lane - ((i == kGather - 1 && lane >= 40) ? 24 : 0);
-            const bool scl = sl >= 8 * 36;
-            if (i == kGather - 1) scale_lane = scl;
-            const int tok = 8 * wave + (scl ? sl - 8 * 36 : sl / 36);
-            const int gran = scl ? 36 : sl % 36;
+            int sl = 64 * i + lane;
+            if (sl >= 4 * 37) sl -= 64;
+            const int tok = 4 * wave + sl / 37;
+            const int gran = sl % 37;
             g_tok[i] = tok * 4;
             g_off[i] = gran * 16;
-            g_dst[i] = scl ? kChunk16 + tok * 32
-                     : gran < 32 ? tok * kRowA16 + gran * 32
-                                 : kRegionB16 + tok * 128 + (((2 * (gran - 32)) ^ swzB(tok)) << 4);
+            g_dst[i] = gran == 36 ? kChunk16 + tok * 32
+                     : gran < 32  ? tok * kRowA16 + gran * 32
+                                  : kRegionB16 + tok * 128 + (((2 * (gran - 32)) ^ swzB(tok)) << 4);
         }
     }
     // sparse record pool as a raw buffer (offsets past its end read zeros)
@@ -171,7 +177,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         const_cast<void*>(a.kv), (short)0, SPARSE ? (int)(unsigned)(a.kv_rows * kRec) : 0, 0x00020000);
 
     bf16x8 qf[18];
-    f4 acc[32];
+    f4 acc[16];
     float m_run, l_run;
     float m_lane;     // largest score this lane has seen in the pass (for a restart's reference)
 
@@ -241,12 +247,13 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             if (j < kChunk / kWaves) {   // region A rows
                 const int rr = min(q, p.nrows - 1);
                 copy_s(p.base + rr * kRowBytes, (unsigned)lane << 4, p.dst + q * kRowA16);
-            } else {                     // region B: 8 rows of 128 B per copy
-                const int sl = (q - kChunk) * 64 + lane;
+            } else {                     // region B: 8 rows of 128 B per copy (parts 0..3, repeated)
+                const int part = (q - kChunk) & 3;
+                const int sl = part * 64 + lane;
                 const int br = sl >> 3;
                 const int rr = min(br, p.nrows - 1);
                 copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(br))) * 16,
-                     p.dst + kRegionB16 + (q - kChunk) * 1024);
+                     p.dst + kRegionB16 + part * 1024);
             }
         };
 
@@ -254,11 +261,11 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // c's ring slot.  Chunks past the segment's end gather its last chunk again (unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         u32x4 gv[SPARSE ? kGather : 1];
-        unsigned g_rec4 = 0;        // record offset behind load 4 (marks an unused entry's scale)
+        unsigned g_rec[SPARSE ? kGather : 1];
         auto gather = [&](int c, int i) {
             const int cc = min(c, nch - 1);
             const unsigned rec = *reinterpret_cast<const unsigned*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
-            if (i == kGather - 1) g_rec4 = rec;
+            g_rec[i] = rec;
             gv[i] = __builtin_amdgcn_raw_buffer_load_b128(pool, rec + (unsigned)g_off[i], 0, SHARED ? 0 : 2);
         };
         auto convert = [&](int c, int i) {
@@ -266,11 +273,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             const u32x4 r = gv[i];
             uint4 lo = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.x, r.y));
             const uint4 hi = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.z, r.w));
-            if (i == kGather - 1) {
-                // scale granule: the raw fp32 scale, NaN for an unused entry (masked off)
-                const unsigned sc = g_rec4 >= kNoRecord ? 0x7fc00000u : r.x;
-                lo.x = scale_lane ? sc : lo.x;
-            }
+            // scale granule: the raw fp32 scale, NaN for an unused entry (masked off)
+            const unsigned sc = g_rec[i] >= kNoRecord ? 0x7fc00000u : r.x;
+            lo.x = g_off[i] == 36 * 16 ? sc : lo.x;
             *reinterpret_cast<uint4*>(slot + g_dst[i]) = lo;
             *reinterpret_cast<uint4*>(slot + (g_dst[i] ^ 16)) = hi;
         };
@@ -280,143 +285,92 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             const int off = ks < 16 ? kaddr + 64 * ks + 16 * kRowA16 * t : kaddrB[ks & 1] + 16 * 128 * t;
             return *reinterpret_cast<const bf16x8*>(buf + off);
         };
-        auto vfrag = [&](const char* buf, int dt) -> bf16x8 {
-            const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr + 32 * dt));
-            const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr + 32 * dt + 16 * kRowA16));
+        auto vfrag = [&](const char* buf, int j) -> bf16x8 {
+            const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr + 32 * j));
+            const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr + 32 * j + 16 * kRowA16));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
         };
 
-        // S^T of chunk c, tile t (tokens 16t..16t+15) x this wave's 16 rows: s2[t][ks&1], four
-        // independent MFMA chains.  side(ks) runs between the steps; fragments are read kPF steps
-        // ahead, since one wave per SIMD leaves nothing else to hide the LDS latency.
-        auto qk = [&](int c, f4 (&s2)[2][2], auto&& side) {
+        // S^T of chunk c, tile t x this wave's 16 rows: two MFMA chains s2[ks&1] (the other wave
+        // of the SIMD fills the MFMA latency).  side(ks) runs between the steps.
+        auto qk = [&](int c, int t, f4 (&s2)[2], auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
+            s2[0] = s2[1] = f4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 kf[kPF];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) s2[t][0] = s2[t][1] = f4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 kf[kPF][2];
-#pragma unroll
-            for (int i = 0; i < kPF - 1; ++i)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) kf[i][t] = kfrag(buf, t, i);
+            for (int i = 0; i < kPF - 1; ++i) kf[i] = kfrag(buf, t, i);
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                if (ks + kPF - 1 < 18)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) kf[(ks + kPF - 1) % kPF][t] = kfrag(buf, t, ks + kPF - 1);
-#pragma unroll
-                for (int t = 0; t < 2; ++t) s2[t][ks & 1] = mfma16(kf[ks % kPF][t], qf[ks], s2[t][ks & 1]);
+                if (ks + kPF - 1 < 18) kf[(ks + kPF - 1) % kPF] = kfrag(buf, t, ks + kPF - 1);
+                s2[ks & 1] = mfma16(kf[ks % kPF], qf[ks], s2[ks & 1]);
                 side(ks);
             }
         };
-        // O^T[16dt..16dt+15][rows] += V^T P^T over chunk c's 32 tokens, dt = 0..31; side(dt)
+        // O^T[256h + 16j .. +15][rows] += V^T P^T over chunk c's 32 tokens, j = 0..15; side(j)
         auto pv = [&](int c, bf16x8 pT, auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             bf16x8 vf[kVPF];
 #pragma unroll
             for (int i = 0; i < kVPF - 1; ++i) vf[i] = vfrag(buf, i);
 #pragma unroll
-            for (int dt = 0; dt < 32; ++dt) {
-                if (dt + kVPF - 1 < 32) vf[(dt + kVPF - 1) % kVPF] = vfrag(buf, dt + kVPF - 1);
-                acc[dt] = mfma16(vf[dt % kVPF], pT, acc[dt]);
-                side(dt);
+            for (int j = 0; j < 16; ++j) {
+                if (j + kVPF - 1 < 16) vf[(j + kVPF - 1) % kVPF] = vfrag(buf, j + kVPF - 1);
+                acc[j] = mfma16(vf[j % kVPF], pT, acc[j]);
+                side(j);
             }
         };
 
-        // ---- softmax of one chunk, in steps that can be spread over MFMAs
-        struct Scores {
-            f4 s[2];        // masked S^T of tiles 0 and 1: sparse scaled (log2 units), paged raw
-            float mxs;      // paged: this lane's largest scaled score of the chunk
-            float tsc[2][4];  // sparse: token scales
-            bool outgrown;  // a score exceeds its row's reference by more than kRefSlack
+        // ---- masking of tile t of chunk c: masked scores in log2 units (paged: raw, scaled
+        // later; sparse: scaled), the tile's largest scaled score, and token scales
+        struct Tile {
+            f4 s;
+            float mx;       // largest scaled score of the tile in this lane
+            float tsc[4];   // sparse: token scales (0 for masked tokens)
         };
-        // step 0: sum the chains; 1/2: mask and scale tile t, compare with the reference;
-        // 3: rows without a reference take the chunk maximum (cross-lane, wave-local); 4: vote
-        auto mask_step = [&](int step, int c, const f4 (&s2)[2][2], Scores& S) {
+        auto mask_tile = [&](int c, int t, f4 s, Tile& T) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             const int tb = t0 + c * kChunk;
-            if (step == 0) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) S.s[t] = s2[t][0] + s2[t][1];
-                S.outgrown = false;
-            } else if (!SPARSE && (step == 1 || step == 2)) {
+            if constexpr (!SPARSE) {
                 // raw scores; a positive scale commutes with the maximum and is applied in the
                 // exponent (the launcher sends other scales to another kernel)
-                const int t = step - 1;
                 const int bnd = min(t1, limit + 1) - tb - 16 * t - 4 * g4;    // valid: i < bnd
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S.s[t][i] = i < bnd ? S.s[t][i] : -INFINITY;
-                const float mt = fmaxf(fmaxf(S.s[t][0], S.s[t][1]), fmaxf(S.s[t][2], S.s[t][3]));
-                if (t == 0) {
-                    S.mxs = mt;
-                } else {
-                    S.mxs = fmaxf(S.mxs, mt) * a.scale_log2;
-                    S.outgrown = (m_run != -INFINITY) & (S.mxs > m_run + kRefSlack);
-                    m_lane = fmaxf(m_lane, S.mxs);
-                }
-            } else if (step == 1 || step == 2) {
-                const int t = step - 1;
-                const float cap = m_run + kRefSlack;      // -inf while the row has no reference
+                for (int i = 0; i < 4; ++i) T.s[i] = i < bnd ? s[i] : -INFINITY;
+                T.mx = fmaxf(fmaxf(T.s[0], T.s[1]), fmaxf(T.s[2], T.s[3])) * a.scale_log2;
+            } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = 16 * t + 4 * g4 + i;
-                    bool valid;
-                    float f = a.scale_log2;
-                    if constexpr (SPARSE) {
-                        // NaN marks an unused entry or a position past the list
-                        const float sc = *reinterpret_cast<const float*>(buf + kChunk16 + tok * 32);
-                        valid = sc == sc;
-                        S.tsc[t][i] = valid ? sc : 0.f;
-                        f *= sc;
-                    } else {
-                        valid = (tb + tok < t1) & (tb + tok <= limit);
-                    }
-                    S.s[t][i] = valid ? S.s[t][i] * f : -INFINITY;
-                    S.outgrown = S.outgrown | ((m_run != -INFINITY) & (S.s[t][i] > cap));
+                    // NaN marks an unused entry or a position past the list
+                    const float sc = *reinterpret_cast<const float*>(buf + kChunk16 + tok * 32);
+                    const bool valid = sc == sc;
+                    T.tsc[i] = valid ? sc : 0.f;
+                    T.s[i] = valid ? s[i] * (a.scale_log2 * sc) : -INFINITY;
                 }
-                m_lane = fmaxf(m_lane, fmaxf(fmaxf(S.s[t][0], S.s[t][1]), fmaxf(S.s[t][2], S.s[t][3])));
-            } else if (step == 3) {
-                if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
-                    float mx;
-                    if constexpr (SPARSE)
-                        mx = fmaxf(fmaxf(fmaxf(S.s[0][0], S.s[0][1]), fmaxf(S.s[0][2], S.s[0][3])),
-                                   fmaxf(fmaxf(S.s[1][0], S.s[1][1]), fmaxf(S.s[1][2], S.s[1][3])));
-                    else
-                        mx = S.mxs;
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    if (m_run == -INFINITY) m_run = mx;       // acc and l are still exactly 0
-                }
-            } else if (step == 4) {
-                const bool v = __builtin_amdgcn_ballot_w64(S.outgrown) != 0;
-                *(lane == 0 ? reinterpret_cast<float*>(&votes[(c & 1) * kWaves + wave]) : my_sink) = __int_as_float(v ? 1 : 0);
+                T.mx = fmaxf(fmaxf(T.s[0], T.s[1]), fmaxf(T.s[2], T.s[3]));
             }
         };
-        // step 0/1: probabilities of tile t; 2: P^T operand
-        struct Probs {
-            unsigned pk[4];
-        };
-        auto prob_step = [&](int step, const Scores& S, Probs& P) {
-            if (step == 0 || step == 1) {
-                const int t = step;
-                const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-                float p[4];
+        // probabilities of the own tile under the row's reference: 4 bf16 in two dwords
+        auto probs = [&](const Tile& T) -> uint2 {
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if constexpr (SPARSE) p[i] = exp2_fast(S.s[t][i] - m_use);
-                    else p[i] = exp2_fast(__builtin_fmaf(S.s[t][i], a.scale_log2, -m_use));
-                    l_run += p[i];
-                    if constexpr (SPARSE) p[i] *= S.tsc[t][i];
-                }
-                P.pk[2 * t] = pack_bf16x2(p[0], p[1]);
-                P.pk[2 * t + 1] = pack_bf16x2(p[2], p[3]);
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (SPARSE) p[i] = exp2_fast(T.s[i] - m_use);
+                else p[i] = exp2_fast(__builtin_fmaf(T.s[i], a.scale_log2, -m_use));
+                l_run += p[i];
+                if constexpr (SPARSE) p[i] *= T.tsc[i];
             }
+            return make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         };
         // B operand element j of lane (l16, g4) is token (j < 4 ? 4*g4 + j : 16 + 4*g4 + j - 4):
-        // tile 0's then tile 1's S^T values of this lane
-        auto p_operand = [&](const Probs& P) {
-            return __builtin_bit_cast(bf16x8, make_uint4(P.pk[0], P.pk[1], P.pk[2], P.pk[3]));
+        // tile 0's then tile 1's probabilities of this lane's row
+        auto p_operand = [&](uint2 own, uint2 other) {
+            const uint4 v = h == 0 ? make_uint4(own.x, own.y, other.x, other.y)
+                                   : make_uint4(other.x, other.y, own.x, own.y);
+            return __builtin_bit_cast(bf16x8, v);
         };
-        // after the barrier that follows mask_step 4 of chunk c: any vote in the workgroup?
+        // after the barrier that follows the vote of chunk c: any vote in the workgroup?
         auto any_vote = [&](int c) {
             int any = 0;
 #pragma unroll
@@ -437,9 +391,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             l_run = 0.f;
             m_lane = -INFINITY;
 #pragma unroll
-            for (int dt = 0; dt < 32; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 16; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
             bool restart = false;
-            Scores S;
+            uint2 p_own;
             if constexpr (!SPARSE) {
 #pragma unroll
                 for (int c = 0; c < AHEAD; ++c) {
@@ -456,93 +410,118 @@ void mla_decode_rows_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int i = 0; i < kGather; ++i) gather(1, i);
             }
-            // chunk 0: Q.K^T (copies of chunk AHEAD, or the conversion of chunk 1 and the gathers
-            // of chunk 2, spread over it), mask
+            // chunk 0: Q.K^T of both tiles (the row's reference needs all 32 tokens; the copies of
+            // chunk AHEAD, or the conversion of chunk 1 and the gathers of chunk 2, spread over
+            // it), reference, probabilities of the own tile
             __syncthreads();
             {
                 const Plan p = plan_for(AHEAD);
-                f4 s2[2][2];
-                qk(0, s2, [&](int ks) {
+                auto side0 = [&](int ks) {
                     if constexpr (!SPARSE) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
                     } else if ((ks & 1) == 0 && ks / 2 < kGather) {
                         convert(1, ks / 2);
                         gather(2, ks / 2);
                     }
-                });
-#pragma unroll
-                for (int step = 0; step < 5; ++step) mask_step(step, 0, s2, S);
+                };
+                f4 s0[2], s1[2];
+                qk(0, 0, s0, side0);
+                qk(0, 1, s1, no_side);
+                Tile T0, T1;
+                mask_tile(0, 0, s0[0] + s0[1], T0);
+                mask_tile(0, 1, s1[0] + s1[1], T1);
+                float mx = fmaxf(T0.mx, T1.mx);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                m_lane = fmaxf(m_lane, mx);
+                if (m_run == -INFINITY) m_run = mx;     // a restart pass keeps its reference
+                p_own = probs(h == 0 ? T0 : T1);
+                px[(0 * kWaves + wave) * 64 + lane] = p_own;
+                if (lane == 0) votes[wave] = 0;
             }
             for (int k = 1; k < nch; ++k) {
                 if constexpr (!SPARSE) wait_chunk();
-                // chunk k in LDS; votes of chunk k-1 visible; slot (k-2) % DEPTH free
+                // chunk k in LDS; probabilities and votes of chunk k-1 visible; slot (k-2) % DEPTH free
                 __syncthreads();
                 restart = restart | any_vote(k - 1);
+                const uint2 p_other = px[(((k - 1) & 1) * kWaves + partner) * 64 + lane];
                 const Plan p = plan_for(k + AHEAD);
-                Probs P;
-                f4 s2[2][2];
-                // S^T(k) on the MFMAs while chunk k-1 becomes probabilities and chunk k+AHEAD is
-                // copied (sparse: chunk k+1 is converted and chunk k+2 gathered)
-                qk(k, s2, [&](int ks) {
+                f4 s2[2];
+                // S^T(k) of the own tile on the MFMAs while chunk k+AHEAD is copied (sparse:
+                // chunk k+1 is converted and chunk k+2 gathered)
+                qk(k, h, s2, [&](int ks) {
                     if constexpr (!SPARSE) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
                     } else if ((ks & 1) == 0 && ks / 2 < kGather) {
                         convert(k + 1, ks / 2);
                         gather(k + 2, ks / 2);
                     }
-                    if (ks == 3) prob_step(0, S, P);
-                    if (ks == 7) prob_step(1, S, P);
                 });
-                // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked
-                pv(k - 1, p_operand(P), [&](int dt) {
-                    if (dt == 1) mask_step(0, k, s2, S);
-                    if (dt == 3) mask_step(1, k, s2, S);
-                    if (dt == 5) mask_step(2, k, s2, S);
-                    if (dt == 7) mask_step(4, k, s2, S);
+                // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked and turned into
+                // probabilities
+                Tile T;
+                bool outgrown = false;
+                uint2 p_next;
+                pv(k - 1, p_operand(p_own, p_other), [&](int j) {
+                    if (j == 3) {
+                        mask_tile(k, h, s2[0] + s2[1], T);
+                        m_lane = fmaxf(m_lane, T.mx);
+                        // also true for a finite score in a row without a reference
+                        outgrown = T.mx > m_run + kRefSlack;
+                    }
+                    if (j == 7) p_next = probs(T);
                 });
-                mask_step(3, k, s2, S);        // rare: rows still without a reference
+                p_own = p_next;
+                px[((k & 1) * kWaves + wave) * 64 + lane] = p_own;
+                const bool v = __builtin_amdgcn_ballot_w64(outgrown) != 0;
+                if (lane == 0) votes[(k & 1) * kWaves + wave] = v ? 1 : 0;
             }
-            __syncthreads();                   // votes of the last chunk visible
+            __syncthreads();                   // votes and probabilities of the last chunk visible
             restart = restart | any_vote(nch - 1);
             if (!restart) {
-                Probs P;
-                prob_step(0, S, P);
-                prob_step(1, S, P);
-                pv(nch - 1, p_operand(P), no_side);
+                const uint2 p_other = px[(((nch - 1) & 1) * kWaves + partner) * 64 + lane];
+                pv(nch - 1, p_operand(p_own, p_other), no_side);
             }
             // the copies past the segment's end land first
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (!restart) break;
-            // run the pass again with each row's maximum over the segment as reference
+            // run the pass again with each row's maximum over the segment (both tiles) as reference
             float mx = m_lane;
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            m_run = mx;
+            __syncthreads();                   // exchanged probabilities no longer read
+            red[wave * 64 + lane] = mx;
+            __syncthreads();
+            m_run = fmaxf(mx, red[partner * 64 + lane]);
             __syncthreads();
         }
 
-        // ---- row sums across the four lanes of a row, then the output
+        // ---- row sums: the four lanes of a row, then the partner wave's tile
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
+        __syncthreads();                    // exchanged probabilities no longer read
+        red[wave * 64 + lane] = l_run;
+        __syncthreads();
+        l_run += red[partner * 64 + lane];
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
         if (row_ok) {
             if (final_out) {
-                __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + row) * kDv + 4 * g4;
+                __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + row) * kDv + 256 * h + 4 * g4;
 #pragma unroll
-                for (int dt = 0; dt < 32; ++dt) {
-                    const f4 v = acc[dt] * inv;
-                    *reinterpret_cast<uint2*>(orow + dt * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                for (int j = 0; j < 16; ++j) {
+                    const f4 v = acc[j] * inv;
+                    *reinterpret_cast<uint2*>(orow + j * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
-                if (g4 == 0) a.lse[(size_t)grp * a.M + row] = lse_v;
+                if (g4 == 0 && h == 0) a.lse[(size_t)grp * a.M + row] = lse_v;
             } else {
-                float* prow = a.part_o + ((size_t)slot * a.M + row) * kDv + 4 * g4;
+                float* prow = a.part_o + ((size_t)slot * a.M + row) * kDv + 256 * h + 4 * g4;
 #pragma unroll
-                for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f4*>(prow + dt * 16) = acc[dt] * inv;
-                if (g4 == 0) a.part_lse[(size_t)slot * a.M + row] = lse_v;
+                for (int j = 0; j < 16; ++j) *reinterpret_cast<f4*>(prow + j * 16) = acc[j] * inv;
+                if (g4 == 0 && h == 0) a.part_lse[(size_t)slot * a.M + row] = lse_v;
             }
         }
-        __syncthreads();                    // LDS (ring, index list, votes) free for the next segment
+        __syncthreads();                    // LDS (ring, index list, exchanges) free for the next segment
     };
 
     if constexpr (!SPARSE) {
