@@ -241,6 +241,25 @@ def cpu_baseline(inp, kind, counts_fn, min_s=10.0, max_s=30.0):
             "sample": sample, "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
 
 
+def run_calls(k, n):
+    """Workload k's decode call n times with nothing else timed around it (profiler passes)."""
+    import torch
+
+    import head_latent_attention_paged_amd as mla
+    from mla_inputs import CONFIGS, make_config
+
+    dev = torch.device("cuda:0")
+    inp = make_config(k, poison=False)
+    if CONFIGS[k]["kind"] == "paged":
+        _, fn = setup_paged(torch, mla, inp, dev)
+    else:
+        _, fn = setup_sparse(torch, mla, inp, dev)
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    print("ran %d decode calls of workload %d" % (n, k), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,9 +269,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration) and exit")
+    ap.add_argument("--calls-of", type=int, default=0, metavar="K",
+                    help="only run workload K's decode call --steps times, untimed (for counter passes), and exit")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.calls_of:
+        run_calls(args.calls_of, args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)

@@ -31,7 +31,10 @@ int sparse_auto_splits(int batch, int s_q, int h_q, int topk) {
     const long long sets = (long long)batch * s_q;
     const Tiling t = mla::choose_tiling(h_q);
     const long long per_set = sets * t.row_groups;
-    long long want = (mla::kSparseTargetItems + per_set - 1) / per_set;
+    // as many splits as fit in one round of work items: a second, partly filled round costs as
+    // much as it saves, and every split adds partial traffic and a combine
+    long long want = mla::kSparseTargetItems / per_set;
+    if (want < 1) want = 1;
     const int max_splits = (topk + mla::kChunk - 1) / mla::kChunk;
     if (want < sparse_min_splits(topk)) want = sparse_min_splits(topk);
     if (want > max_splits) want = max_splits;

@@ -65,6 +65,8 @@ __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
 // pool once per segment; an unused entry (or one past the list) gets kNoRecord, which lies
 // beyond the buffer's range, so its loads return zeros.
 constexpr int kGather = 3;
+// output staging: a wave's 16 rows x 256 values (fp32 1 KB, bf16 512 B per row) at this row pitch
+constexpr int kOutPitch = 1040;
 constexpr unsigned kNoRecord = 0xFFFFF000u;
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exact
@@ -101,6 +103,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     constexpr int DEPTH = C::DEPTH;
     constexpr int AHEAD = C::AHEAD;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    static_assert(C::LDS >= kWaves * 16 * kOutPitch, "output staging must fit in LDS");
     char* ring = smem;
     int* lidx = reinterpret_cast<int*>(smem + C::RING);
     int* lpages = reinterpret_cast<int*>(smem + C::RING + C::IDX);
@@ -505,20 +508,39 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         l_run += red[partner * 64 + lane];
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
-        if (row_ok) {
-            if (final_out) {
-                __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + row) * kDv + 256 * h + 4 * g4;
+        if (row_ok && g4 == 0 && h == 0) {
+            if (final_out) a.lse[(size_t)grp * a.M + row] = lse_v;
+            else a.part_lse[(size_t)slot * a.M + row] = lse_v;
+        }
+        // ---- output through LDS, so that every store instruction writes whole 128-byte lines:
+        // the wave's 16 rows x 256 values go to its own LDS area (rows padded by 16 B), then out
+        // again as 16 contiguous bytes per lane
+        __syncthreads();                    // the exchange area is read: all of LDS is free
+        char* stg = smem + wave * (16 * kOutPitch);
+        const int row0 = rg * kRowsWg + 16 * rb;
+        if (final_out) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const f4 v = acc[j] * inv;
-                    *reinterpret_cast<uint2*>(orow + j * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-                if (g4 == 0 && h == 0) a.lse[(size_t)grp * a.M + row] = lse_v;
-            } else {
-                float* prow = a.part_o + ((size_t)slot * a.M + row) * kDv + 256 * h + 4 * g4;
+            for (int j = 0; j < 16; ++j) {
+                const f4 v = acc[j] * inv;
+                *reinterpret_cast<uint2*>(stg + l16 * kOutPitch + j * 32 + g4 * 8) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+            char* obase = static_cast<char*>(a.out) + ((size_t)grp * a.M + row0) * (kDv * 2) + 512 * h;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) *reinterpret_cast<f4*>(prow + j * 16) = acc[j] * inv;
-                if (g4 == 0 && h == 0) a.part_lse[(size_t)slot * a.M + row] = lse_v;
+            for (int i = 0; i < 8; ++i) {
+                const int r = 2 * i + (lane >> 5), cgr = lane & 31;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kOutPitch + cgr * 16);
+                if (row0 + r < a.M) *reinterpret_cast<uint4*>(obase + (size_t)r * (kDv * 2) + cgr * 16) = v;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                *reinterpret_cast<f4*>(stg + l16 * kOutPitch + j * 64 + g4 * 16) = acc[j] * inv;
+            char* pbase = reinterpret_cast<char*>(a.part_o) + ((size_t)slot * a.M + row0) * (kDv * 4) + 1024 * h;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kOutPitch + lane * 16);
+                if (row0 + r < a.M) *reinterpret_cast<uint4*>(pbase + (size_t)r * (kDv * 4) + lane * 16) = v;
             }
         }
         __syncthreads();                    // LDS (ring, index list, exchanges) free for the next segment

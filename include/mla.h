@@ -128,7 +128,10 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
 
 /*
  * Number of topk splits mla_decode_sparse uses per query token for a given
- * shape when called with splits = 0, and the workspace it then needs.
+ * shape when called with splits = 0, and the workspace it then needs.  The
+ * rule: as many splits as keep the work items (query tokens x row groups x
+ * splits) within one round of 256, at least one, at most topk / 32, and at
+ * least topk / 2048.
  */
 int mla_sparse_splits(int batch, int s_q, int h_q, int topk);
 size_t mla_workspace_size_sparse(int batch, int s_q, int h_q, int topk, int splits);

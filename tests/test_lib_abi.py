@@ -44,7 +44,11 @@ def test_num_parts_and_workspace(mla):
     ws = mla.workspace_size(128, 1, 16, 256)
     assert ws >= (128 + 256) * 16 * 513 * 4
     assert mla.workspace_size(0, 1, 16, 8) == 0
-    assert mla.sparse_splits(32, 6, 64, 2048) >= 1
+    # enough work items (query tokens x 64-row groups) for one round: no split
+    assert mla.sparse_splits(32, 6, 64, 2048) == 1
+    # few query tokens: as many splits as fit one round of 256 items, at most topk / 32
+    assert mla.sparse_splits(2, 1, 64, 2048) == 64
+    assert mla.sparse_splits(8, 1, 64, 2048) == 32
     assert mla.workspace_size_sparse(1, 1, 16, 32, 1) == 0          # one split needs no workspace
 
 
