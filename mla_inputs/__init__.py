@@ -8,7 +8,7 @@ oracle and the GPU path can take their inputs from it.
 
 from .gen import (  # noqa: F401
     D_QK, D_V, PAGE, REC_BYTES,
-    PagedInputs, SparseInputs,
+    PagedInputs, PagedFp8Inputs, SparseInputs,
     bf16_bits_from_f32, bf16_bits_to_f32,
-    make_paged, make_sparse, make_config, config_info, CONFIGS,
+    make_paged, make_paged_fp8, make_sparse, make_config, config_info, CONFIGS,
 )

@@ -143,6 +143,83 @@ def make_paged(batch: int, s_q: int, h_q: int,
                        causal=bool(causal), softmax_scale=scale, poison_page=poison_page)
 
 
+@dataclasses.dataclass
+class PagedFp8Inputs:
+    q: np.ndarray               # uint16 bf16 bits [batch, s_q, h_q, 576]
+    kcache: np.ndarray          # uint8 [num_pages, 64, 640] fp8 records (codes, scale, pad)
+    block_table: np.ndarray     # int32 [batch, max_blocks]
+    seqlens: np.ndarray         # int32 [batch]
+    s_q: int
+    h_q: int
+    causal: bool
+    softmax_scale: float        # an fp32 value, stored as a Python float
+    poison_page: int            # index of the all-NaN page, or -1
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kcache.shape[0])
+
+
+def make_paged_fp8(batch: int, s_q: int, h_q: int,
+                   seqlens: Union[Sequence[int], tuple],
+                   causal: bool, seed: int, poison: bool = True,
+                   softmax_scale: Optional[float] = None) -> PagedFp8Inputs:
+    """Draw one paged decode input set over an fp8 cache.
+
+    Same draws and page permutation as ``make_paged``; the cached rows are
+    drawn in fp32 and quantised per token into 640-byte records (e4m3 codes
+    and an fp32 scale, as for the sparse cache), stored in 64-token pages:
+    the fp8 KV cache layout of the decode path ("deepseek-ai/FlashMLA"
+    project summary, sections "사용 방법" step 3 and "기술적 세부 사항").
+    Poisoned records (unused pages, rows past a sequence's end) hold NaN codes
+    and a NaN scale.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if isinstance(seqlens, tuple) and len(seqlens) == 3 and seqlens[0] == "uniform":
+        L = rng.integers(int(seqlens[1]), int(seqlens[2]) + 1, size=batch).astype(np.int32)
+    else:
+        L = np.asarray(seqlens, dtype=np.int32)
+        if L.shape != (batch,):
+            raise ValueError("seqlens must have one entry per sequence")
+    if (L < 0).any():
+        raise ValueError("sequence lengths must be >= 0")
+    nblk = (L.astype(np.int64) + PAGE - 1) // PAGE
+    total = int(nblk.sum())
+    max_blocks = max(1, int(nblk.max()) if batch else 1)
+    perm = rng.permutation(total).astype(np.int32)
+    fill = total if poison else 0
+    bt = np.full((batch, max_blocks), fill, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        n = int(nblk[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = _normal_bf16(rng, (batch, s_q, h_q, D_QK))
+    n_rows = total * PAGE
+    kc = np.empty((n_rows, REC_BYTES), dtype=np.uint8)
+    for r0 in range(0, n_rows, _KV_CHUNK_ROWS):
+        r1 = min(n_rows, r0 + _KV_CHUNK_ROWS)
+        kc[r0:r1] = quantize_rows_e4m3(rng.standard_normal((r1 - r0, D_QK), dtype=np.float32))
+    kc = kc.reshape(total, PAGE, REC_BYTES)
+    poison_page = -1
+    if poison:
+        bad = np.zeros((PAGE, REC_BYTES), dtype=np.uint8)
+        bad[:, :D_QK] = 0x7F
+        bad[:, SCALE_OFF:SCALE_OFF + 4] = np.full(PAGE, np.nan, dtype="<f4").view(np.uint8).reshape(PAGE, 4)
+        kc = np.concatenate([kc, bad[None]], axis=0)
+        poison_page = total
+        for b in range(batch):
+            if L[b] % PAGE:
+                kc[bt[b, L[b] // PAGE], L[b] % PAGE:] = bad[L[b] % PAGE:]
+    scale = _fp32(D_QK ** -0.5 if softmax_scale is None else softmax_scale)
+    return PagedFp8Inputs(q=q, kcache=kc, block_table=bt, seqlens=L, s_q=s_q, h_q=h_q,
+                          causal=bool(causal), softmax_scale=scale, poison_page=poison_page)
+
+
 # --------------------------------------------------------------------------
 # Sparse fp8 inputs
 # --------------------------------------------------------------------------
@@ -238,6 +315,9 @@ CONFIGS = {
             batch=16, s_q=1, h_q=16, seqlens=[65536] * 16, causal=False),
     5: dict(kind="sparse", name="sparse fp8 decode: b=32 s_q=6 h_q=64 topk=2048 pool=32768/seq p(-1)=0.05",
             batch=32, s_q=6, h_q=64, tokens_per_seq=32768, topk=2048, p_invalid=0.05),
+    # fp8 KV cache for the dense paged path: the memory-bound shape over 640-byte records
+    6: dict(kind="paged_fp8", name="memory-bound paged decode, fp8 KV: b=128 s_q=1 h_q=16 L=4096",
+            batch=128, s_q=1, h_q=16, seqlens=[4096] * 128, causal=False),
 }
 
 
@@ -246,9 +326,11 @@ def config_info(k: int) -> dict:
 
 
 def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
-    """Inputs for workload ``k`` (1..5) with seed 1000 + k unless given."""
+    """Inputs for workload ``k`` (1..6) with seed 1000 + k unless given."""
     c = CONFIGS[k]
     seed = 1000 + k if seed is None else seed
     if c["kind"] == "paged":
         return make_paged(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison)
+    if c["kind"] == "paged_fp8":
+        return make_paged_fp8(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison)
     return make_sparse(c["batch"], c["s_q"], c["h_q"], c["tokens_per_seq"], c["topk"], c["p_invalid"], seed)

@@ -5,6 +5,6 @@ leg use it.  It shares no code with the GPU library.
 """
 
 from .mla_oracle import (  # noqa: F401
-    E4M3_TABLE, attend, bf16_to_f64, e4m3_value, gather_paged_rows,
-    lse_combine, paged_decode, sparse_decode, sparse_rows_f64, visible_count,
+    E4M3_TABLE, attend, bf16_to_f64, e4m3_value, gather_paged_records, gather_paged_rows,
+    lse_combine, paged_decode, paged_decode_fp8, sparse_decode, sparse_rows_f64, visible_count,
 )

@@ -152,6 +152,41 @@ def paged_decode(q_bits: np.ndarray, kcache_bits: np.ndarray, block_table: np.nd
     return O, LSE
 
 
+def gather_paged_records(kcache_records: np.ndarray, block_table_row: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Dequantised rows of logical tokens 0..n_tokens-1 of one sequence from an fp8 paged cache
+    ([pages, 64, 640] records), gathered through its block table."""
+    out = np.empty((n_tokens, D_QK), dtype=np.float64)
+    for t in range(0, n_tokens, PAGE):
+        page = int(block_table_row[t // PAGE])
+        n = min(PAGE, n_tokens - t)
+        out[t:t + n] = sparse_rows_f64(kcache_records[page], np.arange(n))
+    return out
+
+
+def paged_decode_fp8(q_bits: np.ndarray, kcache_records: np.ndarray, block_table: np.ndarray,
+                     seqlens: np.ndarray, softmax_scale: float, causal: bool,
+                     batches: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Paged MLA decode over an fp8 cache: 64-token pages of 640-byte records (e4m3 codes of the
+    576 dims and the token's fp32 scale), the fp8 KV cache layout of the decode path
+    ("deepseek-ai/FlashMLA" project summary, sections "사용 방법" step 3 and "기술적 세부 사항").
+    Row value = e4m3(code) * scale, exactly; otherwise the definition of ``paged_decode``.
+
+    kcache_records [pages, 64, 640] uint8.  Returns O [B, s_q, h_q, 512] and LSE [B, s_q, h_q]
+    in float64 (sequences outside ``batches`` stay NaN).
+    """
+    B, s_q, h_q, _ = q_bits.shape
+    sigma = float(np.float32(softmax_scale))
+    O = np.full((B, s_q, h_q, D_V), np.nan)
+    LSE = np.full((B, s_q, h_q), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seqlens[b])
+        rows = gather_paged_records(kcache_records, block_table[b], L)
+        for s in range(s_q):
+            n = visible_count(L, s_q, s, causal)
+            O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows[:n], sigma)
+    return O, LSE
+
+
 def sparse_decode(q_bits: np.ndarray, kv_records: np.ndarray, indices: np.ndarray,
                   softmax_scale: float,
                   sets: Optional[Iterable[Tuple[int, int]]] = None) -> Tuple[np.ndarray, np.ndarray]:

@@ -72,6 +72,27 @@ def test_sparse_generator_indices():
 
 
 def test_config_table():
-    assert set(CONFIGS) == {1, 2, 3, 4, 5}
+    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6}
     assert CONFIGS[2]["batch"] == 128 and CONFIGS[4]["seqlens"][0] == 65536
     assert CONFIGS[5]["topk"] == 2048
+    # the fp8-cache workload is the memory-bound shape over fp8 records
+    assert CONFIGS[6]["kind"] == "paged_fp8"
+    assert all(CONFIGS[6][k] == CONFIGS[2][k] for k in ("batch", "s_q", "h_q", "seqlens", "causal"))
+
+
+def test_paged_fp8_generator():
+    from mla_inputs import make_paged_fp8
+    inp = make_paged_fp8(3, 2, 16, [100, 64, 5], True, seed=5)
+    assert inp.kcache.shape == (2 + 1 + 1 + 1, 64, 640) and inp.kcache.dtype == np.uint8
+    assert inp.poison_page == 4
+    # pages handed out once, unused slots on the poison page
+    used = np.concatenate([inp.block_table[0, :2], inp.block_table[1, :1], inp.block_table[2, :1]])
+    assert sorted(used.tolist()) == [0, 1, 2, 3]
+    assert inp.block_table[1, 1] == 4 and inp.block_table[2, 1] == 4
+    # records past a sequence's end carry NaN codes and a NaN scale
+    last = inp.kcache[inp.block_table[0, 1], 100 - 64:]
+    assert np.all(last[:, :576] == 0x7F)
+    assert np.isnan(last[:, 576:580].copy().view("<f4")).all()
+    # in-range records: finite positive scales
+    sc = inp.kcache[inp.block_table[1, 0], :, 576:580].copy().view("<f4")
+    assert np.all(np.isfinite(sc)) and np.all(sc > 0)

@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from mla_inputs import bf16_bits_from_f32, make_paged, make_sparse
-from oracle import (E4M3_TABLE, attend, bf16_to_f64, lse_combine, paged_decode,
+from mla_inputs import bf16_bits_from_f32, make_paged, make_paged_fp8, make_sparse
+from oracle import (E4M3_TABLE, attend, bf16_to_f64, lse_combine, paged_decode, paged_decode_fp8,
                     sparse_decode, sparse_rows_f64, visible_count)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -309,6 +309,59 @@ def test_sparse_equals_paged_on_the_same_rows():
     idx[0, 1, :] = np.arange(T)
     Os, Ls = sparse_decode(q, rec, idx, SIGMA)
     assert np.allclose(Op, Os, rtol=0, atol=1e-13) and np.allclose(Lp, Ls, rtol=0, atol=1e-13)
+
+
+def _exact_records(rng, n):
+    """fp8 records whose dequantised values are bf16 values: no NaN codes, power-of-two scales."""
+    rec = np.zeros((n, 640), dtype=np.uint8)
+    codes = rng.integers(0, 256, size=(n, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    rec[:, :576] = codes
+    rec[:, 576:580] = (2.0 ** rng.integers(-4, 3, size=n)).astype("<f4").view(np.uint8).reshape(n, 4)
+    return rec
+
+
+def test_paged_fp8_equals_bf16_paged_on_the_same_values():
+    """An fp8 paged cache and a bf16 paged cache holding the same values, through the same block
+    tables (permuted pages, ragged lengths, causal with two queries), give the same result."""
+    rng = np.random.default_rng(31)
+    L = np.array([150, 70], dtype=np.int32)
+    pages = 3 + 2
+    rec = _exact_records(rng, pages * 64).reshape(pages, 64, 640)
+    vals = sparse_rows_f64(rec.reshape(-1, 640), np.arange(pages * 64))
+    kc = _bf16(vals.astype(np.float32)).reshape(pages, 64, 1, 576)
+    assert np.array_equal(bf16_to_f64(kc).reshape(-1, 576), vals)
+    perm = rng.permutation(pages).astype(np.int32)
+    bt = np.array([perm[:3], np.r_[perm[3:], 0]], dtype=np.int32)
+    q = _bf16(rng.standard_normal((2, 2, 16, 576)))
+    Ob, Lb = paged_decode(q, kc, bt, L, SIGMA, causal=True)
+    Of, Lf = paged_decode_fp8(q, rec, bt, L, SIGMA, causal=True)
+    assert np.allclose(Ob, Of, rtol=0, atol=1e-13) and np.allclose(Lb, Lf, rtol=0, atol=1e-13)
+
+
+def test_paged_fp8_equals_sparse_over_the_page_rows():
+    """Paged fp8 decode == sparse decode whose index list names the same rows of the flattened
+    pool (row = page * 64 + position in the page), in token order."""
+    inp = make_paged_fp8(2, 1, 16, [130, 64], False, seed=41, poison=False)
+    O, LSE = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    flat = inp.kcache.reshape(-1, 640)
+    topk = int(inp.seqlens.max())
+    idx = np.full((2, 1, topk), -1, dtype=np.int32)
+    for b in range(2):
+        t = np.arange(int(inp.seqlens[b]))
+        idx[b, 0, :len(t)] = inp.block_table[b, t // 64] * 64 + t % 64
+    Os, Ls = sparse_decode(inp.q, flat, idx, inp.softmax_scale)
+    assert np.allclose(O, Os, rtol=0, atol=1e-13) and np.allclose(LSE, Ls, rtol=0, atol=1e-13)
+
+
+def test_paged_fp8_never_reads_poisoned_records():
+    """NaN records in unused block-table slots and past each sequence's end change nothing."""
+    inp = make_paged_fp8(3, 2, 16, [100, 64, 5], True, seed=43, poison=True)
+    O, LSE = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    assert np.isfinite(O).all() and np.isfinite(LSE).all()
+    clean = make_paged_fp8(3, 2, 16, [100, 64, 5], True, seed=43, poison=False)
+    Oc, Lc = paged_decode_fp8(clean.q, clean.kcache, clean.block_table, clean.seqlens, clean.softmax_scale, True)
+    assert np.array_equal(O, Oc) and np.array_equal(LSE, Lc)
 
 
 def test_visible_count():
