@@ -31,13 +31,14 @@ D_QK, D_V = 576, 512
 def paged_counts(inp):
     """Algorithmic bytes and flops of one paged decode step.
 
-    Bytes: every visible KV row once per sequence (1152 B; V lies inside K), Q, O (bf16),
-    LSE (fp32), the used block-table entries and the sequence lengths.  Flops:
-    2 * (576 + 512) per (query row, visible token)."""
+    Bytes: every visible KV row once per sequence (bf16 1152 B; an fp8 record's 576 codes and
+    its fp32 scale, 580 B; V lies inside K), Q, O (bf16), LSE (fp32), the used block-table
+    entries and the sequence lengths.  Flops: 2 * (576 + 512) per (query row, visible token)."""
     L = inp.seqlens.astype(np.int64)
     b, s_q, h_q = inp.batch, inp.s_q, inp.h_q
     M = s_q * h_q
-    kv = int(L.sum()) * D_QK * 2
+    row_bytes = 580 if inp.kcache.dtype == np.uint8 else D_QK * 2
+    kv = int(L.sum()) * row_bytes
     nblk = int(((L + 63) // 64).sum())
     byts = kv + b * M * D_QK * 2 + b * M * D_V * 2 + b * M * 4 + nblk * 4 + b * 4
     vis = 0
@@ -164,9 +165,10 @@ def time_back_to_back(torch, fn, n):
 
 
 def setup_paged(torch, mla, inp, dev):
-    from tests.helpers import dev_bf16, dev_i32
+    from tests.helpers import dev_bf16, dev_i32, dev_u8
 
-    q, kc = dev_bf16(inp.q, dev), dev_bf16(inp.kcache, dev)
+    q = dev_bf16(inp.q, dev)
+    kc = dev_u8(inp.kcache, dev) if inp.kcache.dtype == np.uint8 else dev_bf16(inp.kcache, dev)
     bt, sl = dev_i32(inp.block_table, dev), dev_i32(inp.seqlens, dev)
     P = mla.num_parts(inp.h_q, inp.s_q)
     out = torch.empty((inp.batch, inp.s_q, inp.h_q, D_V), dtype=torch.bfloat16, device=dev)
@@ -250,7 +252,7 @@ def run_calls(k, n):
 
     dev = torch.device("cuda:0")
     inp = make_config(k, poison=False)
-    if CONFIGS[k]["kind"] == "paged":
+    if CONFIGS[k]["kind"] in ("paged", "paged_fp8"):
         _, fn = setup_paged(torch, mla, inp, dev)
     else:
         _, fn = setup_sparse(torch, mla, inp, dev)
@@ -338,10 +340,10 @@ def main():
     if args.extra:
         flush = Flusher(torch, dev)
         extra = {}
-        for k in (2, 3, 4, 5):
+        for k in (2, 3, 4, 5, 6):
             print("[bench] workload %d" % k, file=sys.stderr, flush=True)
             ik = inp if k == 2 else make_config(k, poison=False)
-            if CONFIGS[k]["kind"] == "paged":
+            if CONFIGS[k]["kind"] in ("paged", "paged_fp8"):
                 _, fn = setup_paged(torch, mla, ik, dev)
                 b_k, f_k = paged_counts(ik)
             else:

@@ -22,8 +22,8 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP
 
 EXPORTS = (
     "mla_status_string", "mla_num_parts", "mla_get_metadata", "mla_get_metadata_host",
-    "mla_workspace_size", "mla_decode_paged", "mla_sparse_splits", "mla_workspace_size_sparse",
-    "mla_decode_sparse",
+    "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_sparse_splits",
+    "mla_workspace_size_sparse", "mla_decode_sparse",
 )
 
 
@@ -54,6 +54,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32,
                                      vp, vp, i32, vp, sz, vp, vp, vp]
     lib.mla_decode_paged.restype = i32
+    lib.mla_decode_paged_fp8.argtypes = lib.mla_decode_paged.argtypes
+    lib.mla_decode_paged_fp8.restype = i32
     lib.mla_sparse_splits.argtypes = [i32, i32, i32, i32]
     lib.mla_sparse_splits.restype = i32
     lib.mla_workspace_size_sparse.argtypes = [i32, i32, i32, i32, i32]
@@ -137,14 +139,24 @@ def decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tenso
                  softmax_scale: float = D_QK ** -0.5, causal: bool = False,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Paged MLA decode; returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q])."""
+    """Paged MLA decode; returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q]).
+
+    kcache is bf16 [num_blocks, 64, 1, 576], or uint8 [num_blocks, 64, 640] fp8 records (e4m3
+    codes of the 576 dims, the token's fp32 scale at byte 576), which calls mla_decode_paged_fp8.
+    """
     batch, s_q, h_q, d = q.shape
     if d != D_QK:
         raise ValueError("q must have 576 dims per head")
     _require(q, "q", torch.bfloat16)
-    _require(kcache, "kcache", torch.bfloat16)
-    if kcache.dim() != 4 or tuple(kcache.shape[1:]) != (PAGE, 1, D_QK):
-        raise ValueError("kcache must be [num_blocks, 64, 1, 576]")
+    fp8 = kcache.dtype == torch.uint8
+    if fp8:
+        _require(kcache, "kcache", torch.uint8)
+        if kcache.dim() != 3 or tuple(kcache.shape[1:]) != (PAGE, SPARSE_REC):
+            raise ValueError("an fp8 kcache must be [num_blocks, 64, 640] uint8 records")
+    else:
+        _require(kcache, "kcache", torch.bfloat16)
+        if kcache.dim() != 4 or tuple(kcache.shape[1:]) != (PAGE, 1, D_QK):
+            raise ValueError("kcache must be [num_blocks, 64, 1, 576]")
     _require(block_table, "block_table", torch.int32)
     _require(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
     tile_meta, num_splits = metadata
@@ -159,7 +171,8 @@ def decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tenso
     need = workspace_size(batch, s_q, h_q, P)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    _check("mla_decode_paged", lib.mla_decode_paged(
+    name = "mla_decode_paged_fp8" if fp8 else "mla_decode_paged"
+    _check(name, getattr(lib, name)(
         q.data_ptr(), kcache.data_ptr(), kcache.shape[0], block_table.data_ptr(), block_table.shape[1],
         cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
         tile_meta.data_ptr(), num_splits.data_ptr(), P,

@@ -25,6 +25,7 @@ SOURCES = {
     "mla_kernels.hip": VGPR_FORM,
     "mla_decode_big.hip": VGPR_FORM,
     "mla_decode_rows.hip": [],
+    "mla_decode_fp8.hip": VGPR_FORM,
     "mla_api.cpp": [],
 }
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -132,13 +132,13 @@ mla_status_t mla_get_metadata_host(const int32_t* cache_seqlens, int batch, int 
     return MLA_OK;
 }
 
-mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blocks,
-                              const int32_t* block_table, int max_blocks,
-                              const int32_t* cache_seqlens, int batch, int s_q, int h_q,
-                              float softmax_scale, int causal,
-                              const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
-                              void* workspace, size_t workspace_bytes,
-                              void* out, float* lse, void* stream) {
+static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t num_blocks,
+                                      const int32_t* block_table, int max_blocks,
+                                      const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                      float softmax_scale, int causal,
+                                      const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* out, float* lse, void* stream, bool fp8) {
     if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0 || max_blocks <= 0 || num_blocks <= 0)
@@ -150,8 +150,10 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
     const size_t need = mla_workspace_size(batch, s_q, h_q, num_parts);
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
     if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
-
     const int M = s_q * h_q;
+    // fp8 pages with more than 16 rows go through 32-bit buffer offsets
+    if (fp8 && M > 16 && num_blocks * mla::kPage * mla::kRec > mla::kRowsSparseMaxPool) return MLA_ERR_UNSUPPORTED;
+
     const long long slots = (long long)batch + num_parts;
     mla::AttnArgs a{};
     a.q = q;
@@ -173,11 +175,37 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
     a.causal = causal ? 1 : 0;
     a.num_parts = num_parts;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.kv_fp8 = fp8 ? 1 : 0;
+    a.kv_rows = num_blocks * mla::kPage;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (mla::launch_decode(a, false, s) != hipSuccess) return MLA_ERR_HIP;
     if (mla::launch_combine(a.part_o, a.part_lse, num_splits, 0, batch, M, out, lse, s) != hipSuccess)
         return MLA_ERR_HIP;
     return MLA_OK;
+}
+
+mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blocks,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                              float softmax_scale, int causal,
+                              const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                              void* workspace, size_t workspace_bytes,
+                              void* out, float* lse, void* stream) {
+    return decode_paged_impl(q, kcache, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                             softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
+                             workspace_bytes, out, lse, stream, false);
+}
+
+mla_status_t mla_decode_paged_fp8(const void* q, const void* kcache, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  float softmax_scale, int causal,
+                                  const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, void* stream) {
+    return decode_paged_impl(q, kcache, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                             softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
+                             workspace_bytes, out, lse, stream, true);
 }
 
 mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens,

@@ -51,19 +51,10 @@ constexpr int kRowA16 = 1056;
 constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
 
 // An all-zero record: unused index entries are copied from it, so a chunk always costs the same
 // copies (exact s_waitcnt accounting) and its zero-weight V rows are finite.
 __device__ __attribute__((aligned(16))) const unsigned char kZeroRecord[kRec8Row] = {0};
-
-// 8 e4m3 codes (two dwords) -> 8 bf16, exact
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
-#define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))
-    const uint4 v = make_uint4(MLA_CVT(lo, false), MLA_CVT(lo, true), MLA_CVT(hi, false), MLA_CVT(hi, true));
-#undef MLA_CVT
-    return __builtin_bit_cast(bf16x8, v);
-}
 
 // Workgroup: PAIRS pairs of waves sharing one stream of chunks.  A pair owns 32 query rows;
 // in each 32-token chunk wave h (0/1) of the pair computes S^T for tokens 16h..16h+15 and

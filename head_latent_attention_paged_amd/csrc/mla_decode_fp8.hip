@@ -1,0 +1,273 @@
+// gfx950 decode kernel for an fp8 paged cache and one 16-row tile (s_q * h_q <= 16), the
+// memory-bound shape over 64-token pages of 640-byte records (e4m3 codes of the 576 dims and the
+// token's fp32 scale: the fp8 KV cache layout of the decode path, "deepseek-ai/FlashMLA" project
+// summary, sections 사용 방법 step 3 and 기술적 세부 사항).
+//
+// Four independent token streams per workgroup (one per wave, one wave per SIMD) double-buffer
+// 32-token chunks (half a page, 20 KB of records) that go HBM -> LDS by direct copies.  Per chunk
+// a wave computes S^T = K Q^T for two 16-token tiles (tokens on the MFMA M side, "FlashMLA-ETAP:
+// Efficient Transpose Attention Pipeline ...", section 핵심 메커니즘), converting the K fragments
+// exactly from e4m3 to bf16 as they are read; the two S^T tiles hold, lane by lane, the P^T B
+// operand of one 16x16x32 MFMA per 16 value dims, whose V^T operand comes from a transposing
+// 8-bit LDS read in the matching token order.  The token scale multiplies the score and the
+// probability before P.V.  Online softmax with a lagging reference, as in the bf16 kernel; the
+// four streams merge at the end.
+#include "mla_device.h"
+
+namespace mla {
+
+namespace m16f8 {
+
+constexpr int kChunk8 = 32;                    // tokens per chunk: half a page
+constexpr int kBuf = kChunk8 * kRec;           // 20 KB of records
+constexpr int kOps = kBuf / 1024;              // 20 copies of 64 lanes x 16 B per chunk
+constexpr int kStreams = 4;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_m16_fp8_kernel(const AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[kStreams * 2 * kBuf];   // 160 KB
+    const int lane = threadIdx.x & 63;
+    const int ts = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);       // stream = wave
+    const int g4 = lane >> 4, l16 = lane & 15;
+    char* bufs = smem + ts * 2 * kBuf;
+    const int item = blockIdx.x;
+
+    // K fragment (A operand of S^T), tile t, step ks: dims 32*ks + 8*g4 of token 16t + l16 =
+    // granule 2*ks + g4/2, half g4&1 (kaddr[t][ks&3] + 128*(ks/4): the XOR only touches the low
+    // three granule bits)
+    int kaddr[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int kr = 16 * t + l16;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) kaddr[t][r4] = kr * kRec + (((2 * r4 + (g4 >> 1)) ^ swz8(kr)) << 4) + (g4 & 1) * 8;
+    }
+    // V^T fragment (A operand of O^T), dims 16*dt + l16: the transposing read gives this lane 8
+    // tokens of granule dt; B operand element j of lane (l16, g4) is token (j < 4 ? 4*g4 + j :
+    // 16 + 4*g4 + j - 4), so lane l16 reads rows 4*g4 + l16/2 (l16 < 8) or 16 + 4*g4 + l16/2 - 4
+    int vaddr[8];
+    {
+        const int j = l16 >> 1;
+        const int vr = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vaddr[e] = vr * kRec + ((e ^ swz8(vr)) << 4) + (l16 & 1) * 8;
+    }
+    // copies: op j, lane: LDS byte 1024*j + 16*lane = record row rr, slot s, filled from granule
+    // s ^ swz8(rr) of the row
+    int c_row[kOps], c_gran[kOps];
+#pragma unroll
+    for (int j = 0; j < kOps; ++j) {
+        const int gg = 64 * j + lane;
+        c_row[j] = gg / 40;
+        c_gran[j] = ((gg % 40) ^ swz8(gg / 40)) << 4;
+    }
+
+    bf16x8 qf[18];
+    f4 acc[32];
+    float m_run, l_run;
+
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
+        const int r = l16;
+        {
+            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (r < a.M ? r : 0)) * (kDqk * 2);
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
+                if (r >= a.M) v = make_uint4(0, 0, 0, 0);
+                qf[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+        const int limit = a.causal ? (L - a.s_q + r / a.h_q) : (L - 1);
+        const int nch = ceil_div(t1 - t0, kChunk8);
+
+        // Wave ts handles chunks c = ts + 4k: half c & 1 of page (c >> 1) of the segment.  The
+        // page numbers come 64 at a time into one register of the wave (lane i: page base + i).
+        const int lo_page = t0 >> 6;
+        int bt_base = -1000000, win = 0;
+        auto page_of = [&](int p) {
+            if (p - bt_base >= 64 || p < bt_base) {
+                bt_base = p;
+                const int np = ceil_div(t1, kPage) - lo_page;
+                win = (lane < np - p) ? a.block_table[(size_t)grp * a.max_blocks + lo_page + p + lane] : 0;
+            }
+            return __builtin_amdgcn_readlane(win, p - bt_base);
+        };
+        // copy chunk c = ts + 4k (32 records, contiguous in HBM) into buffer b; rows past the
+        // end repeat the last row (weight 0, finite)
+        auto issue = [&](int k, int b) {
+            const int c = ts + 4 * k;
+            const int tb = t0 + c * kChunk8;
+            const int nrows = min(kChunk8, t1 - tb);
+            const int page = page_of(c >> 1);
+            const char* base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRec;
+            char* dst = bufs + b * kBuf;
+#pragma unroll
+            for (int j = 0; j < kOps; ++j) {
+                const int rr = min(c_row[j], nrows - 1);
+                dma16_s(base, (unsigned)(rr * kRec + c_gran[j]), dst + 1024 * j);
+            }
+        };
+
+        if (ts < nch) issue(0, 0);
+        int k = 0;
+        for (int c = ts; c < nch; c += kStreams, ++k) {
+            const char* buf = bufs + (k & 1) * kBuf;
+            if (c + kStreams < nch) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the other buffer done
+                issue(k + 1, (k + 1) & 1);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOps) : "memory");   // chunk c landed, c+4 in flight
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            const int tb = t0 + c * kChunk8;
+            // S^T of the two tiles over 576 dims: four independent chains
+            f4 s2[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) s2[t][0] = s2[t][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(buf + kaddr[t][ks & 3] + 128 * (ks >> 2));
+                    s2[t][ks & 1] = mfma16(fp8x8_to_bf16(w.x, w.y), qf[ks], s2[t][ks & 1]);
+                }
+            }
+            // mask and scale: token scale * softmax scale (log2 units)
+            float x[2][4], tsc[2][4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f4 sv = s2[t][0] + s2[t][1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = 16 * t + 4 * g4 + i;
+                    const float sc = *reinterpret_cast<const float*>(buf + tok * kRec + ((36 ^ swz8(tok)) << 4));
+                    const int tt = tb + tok;
+                    const bool valid = (tt < t1) & (tt <= limit);
+                    tsc[t][i] = valid ? sc : 0.f;
+                    x[t][i] = valid ? sv[i] * (a.scale_log2 * sc) : -INFINITY;
+                    mx = fmaxf(mx, x[t][i]);
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.f : m_new));
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            unsigned pk[4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = exp2_fast(x[t][i] - m_use);
+                    l_run += p[i];
+                    p[i] *= tsc[t][i];
+                }
+                pk[2 * t] = pack_bf16x2(p[0], p[1]);
+                pk[2 * t + 1] = pack_bf16x2(p[2], p[3]);
+            }
+            const bf16x8 pT = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            typedef int v2i __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) {
+                const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(buf + vaddr[dt & 7] + 128 * (dt >> 3)));
+                acc[dt] = mfma16(fp8x8_to_bf16((unsigned)w[0], (unsigned)w[1]), pT, acc[dt]);
+            }
+        }
+
+        // row sums, merge the 4 streams (stream 0 keeps the result), write
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        f4* macc = reinterpret_cast<f4*>(smem);
+        float* mml = reinterpret_cast<float*>(smem + 3 * 32 * 64 * 16);
+        __syncthreads();
+        if (ts > 0) {
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) macc[((ts - 1) * 32 + dt) * 64 + lane] = acc[dt];
+            mml[((ts - 1) * 64 + lane) * 2 + 0] = m_run;
+            mml[((ts - 1) * 64 + lane) * 2 + 1] = l_run;
+        }
+        __syncthreads();
+        if (ts == 0) {
+            float mk[4], lk[4];
+            mk[0] = m_run;
+            lk[0] = l_run;
+            float m_new = m_run;
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                mk[w] = mml[((w - 1) * 64 + lane) * 2 + 0];
+                lk[w] = mml[((w - 1) * 64 + lane) * 2 + 1];
+                m_new = fmaxf(m_new, mk[w]);
+            }
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            float al[4], l_new = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                al[w] = exp2_fast(mk[w] - m_use);
+                l_new += al[w] * lk[w];
+            }
+            const float inv = l_new > 0.f ? 1.f / l_new : 0.f;
+            const float lse_v = l_new > 0.f ? (m_new + __log2f(l_new)) * kLn2 : -INFINITY;
+            if (r < a.M) {
+                if (final_out) {
+                    __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + r) * kDv + 4 * g4;
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) {
+                        f4 v = acc[dt] * al[0];
+#pragma unroll
+                        for (int w = 1; w < 4; ++w) v += macc[((w - 1) * 32 + dt) * 64 + lane] * al[w];
+                        v *= inv;
+                        *reinterpret_cast<uint2*>(orow + dt * 16) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    }
+                    if (g4 == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
+                } else {
+                    float* prow = a.part_o + ((size_t)slot * a.M + r) * kDv + 4 * g4;
+#pragma unroll
+                    for (int dt = 0; dt < 32; ++dt) {
+                        f4 v = acc[dt] * al[0];
+#pragma unroll
+                        for (int w = 1; w < 4; ++w) v += macc[((w - 1) * 32 + dt) * 64 + lane] * al[w];
+                        *reinterpret_cast<f4*>(prow + dt * 16) = v * inv;
+                    }
+                    if (g4 == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    const int* meta = a.tile_meta + (size_t)item * kMetaInts;
+    const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
+    for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
+        const int L = a.seqlens[bb];
+        const int nb = ceil_div(L, kPage);
+        const int lo = (bb == b0) ? blk0 : 0;
+        const int hi = (bb == b1) ? blk1 : nb;
+        if (lo >= hi) continue;
+        const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
+        const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
+        run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+    }
+}
+
+}  // namespace m16f8
+
+hipError_t launch_decode_m16_fp8(const AttnArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(m16f8::mla_decode_m16_fp8_kernel, dim3(a.num_parts), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mla

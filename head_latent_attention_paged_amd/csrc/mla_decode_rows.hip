@@ -69,37 +69,37 @@ constexpr int kGather = 3;
 constexpr int kOutPitch = 1040;
 constexpr unsigned kNoRecord = 0xFFFFF000u;
 
-// 8 e4m3 codes (two dwords) -> 8 bf16, exact
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
-#define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))
-    const uint4 v = make_uint4(MLA_CVT(lo, false), MLA_CVT(lo, true), MLA_CVT(hi, false), MLA_CVT(hi, true));
-#undef MLA_CVT
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-template <bool SPARSE>
+template <bool GATHER>
 struct Cfg {
     // a ring slot holds a bf16 chunk; sparse adds the 32 token scales (32-byte stride)
-    static constexpr int BUF = kChunk16 + (SPARSE ? kChunk * 32 : 0);
+    static constexpr int BUF = kChunk16 + (GATHER ? kChunk * 32 : 0);
     // ring slots: chunk k-1 (P.V), chunk k (Q.K^T) and, paged, AHEAD chunks in flight; sparse,
     // chunk k+1, converted while chunk k+2 is gathered into registers
-    static constexpr int DEPTH = SPARSE ? 3 : 4;
+    static constexpr int DEPTH = GATHER ? 3 : 4;
     static constexpr int AHEAD = DEPTH - 2;
     // paged copies per wave per chunk: 32 rows of region A + 4 KB of region B = 36 x 1 KB over
     // eight waves, the last four repeated
     static constexpr int OPS = 5;
     static constexpr int RING = DEPTH * BUF;
-    static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;        // a split's index list
-    static constexpr int PAGES = SPARSE ? 0 : kWaves * 64 * 4;            // per-wave page windows
+    static constexpr int IDX = GATHER ? kMaxSparseSplit * 4 : 0;        // a segment's index list
+    static constexpr int PAGES = GATHER ? 0 : kWaves * 64 * 4;            // per-wave page windows
     static constexpr int PX = 2 * kWaves * 64 * 8;                        // exchanged P, by chunk parity
     static constexpr int VOTES = 2 * kWaves * 4;                          // restart votes, by chunk parity
     static constexpr int LDS = RING + IDX + PAGES + PX + VOTES;
 };
 
-template <bool SPARSE, bool SHARED>
+// kernel modes: bf16 pages (direct copies), sparse fp8 records through an index list, fp8 pages
+// (their records gathered through an index list built from the block table)
+constexpr int kPagedBf16 = 0, kSparseFp8 = 1, kPagedFp8 = 2;
+
+template <int MODE, bool SHARED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_rows_kernel(const AttnArgs a) {
-    using C = Cfg<SPARSE>;
+    constexpr bool SPARSE = MODE == kSparseFp8;
+    constexpr bool GATHER = MODE != kPagedBf16;     // fp8 records gathered through the index list
+    using C = Cfg<GATHER>;
+    constexpr int PF = kPF;
+    constexpr int VPF = kVPF;
     constexpr int DEPTH = C::DEPTH;
     constexpr int AHEAD = C::AHEAD;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -160,8 +160,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     // ---- sparse gathers: load i of this lane fetches granule g_off/16 of record g_tok/4 of the
     // chunk and stores it at g_dst of the ring slot: codes as 16 bf16 (32 B, the second half at
     // g_dst ^ 16), a scale granule as its raw first dword
-    int g_tok[SPARSE ? kGather : 1], g_off[SPARSE ? kGather : 1], g_dst[SPARSE ? kGather : 1];
-    if constexpr (SPARSE) {
+    int g_tok[GATHER ? kGather : 1], g_off[GATHER ? kGather : 1], g_dst[GATHER ? kGather : 1];
+    if constexpr (GATHER) {
 #pragma unroll
         for (int i = 0; i < kGather; ++i) {
             int sl = 64 * i + lane;
@@ -177,7 +177,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     }
     // sparse record pool as a raw buffer (offsets past its end read zeros)
     const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.kv), (short)0, SPARSE ? (int)(unsigned)(a.kv_rows * kRec) : 0, 0x00020000);
+        const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * kRec) : 0, 0x00020000);
 
     bf16x8 qf[18];
     f4 acc[16];
@@ -200,10 +200,19 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         const int limit = a.causal ? (L - a.s_q + row / a.h_q) : (L - 1);
 
         // sparse: the split's index list goes to LDS once, as record byte offsets (kNoRecord for
-        // unused entries and up to the end of the last chunk)
-        if constexpr (SPARSE) {
+        // unused entries and up to the end of the last chunk); fp8 pages: the record offsets of
+        // the segment's tokens through the block table
+        if constexpr (GATHER) {
             for (int e = threadIdx.x; e < nch * kChunk; e += kWaves * 64) {
-                const int v = e < t1 - t0 ? a.indices[(size_t)grp * a.topk + t0 + e] : -1;
+                long long v = -1;
+                if (e < t1 - t0) {
+                    if constexpr (SPARSE) {
+                        v = a.indices[(size_t)grp * a.topk + t0 + e];
+                    } else {
+                        const int t = t0 + e;
+                        v = (long long)a.block_table[(size_t)grp * a.max_blocks + (t >> 6)] * kPage + (t & 63);
+                    }
+                }
                 lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)((unsigned)v * kRec) : (int)kNoRecord;
             }
             __syncthreads();
@@ -239,7 +248,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             const int tb = t0 + cc * kChunk;
             p.nrows = min(kChunk, t1 - tb);
             p.base = nullptr;
-            if constexpr (!SPARSE) {
+            if constexpr (!GATHER) {
                 const int page = page_of(cc >> 1);
                 p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
             }
@@ -263,8 +272,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // ---- sparse: load i of chunk c into registers; conversion of those registers into chunk
         // c's ring slot.  Chunks past the segment's end gather its last chunk again (unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 gv[SPARSE ? kGather : 1];
-        unsigned g_rec[SPARSE ? kGather : 1];
+        u32x4 gv[GATHER ? kGather : 1];
+        unsigned g_rec[GATHER ? kGather : 1];
         auto gather = [&](int c, int i) {
             const int cc = min(c, nch - 1);
             const unsigned rec = *reinterpret_cast<const unsigned*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
@@ -299,26 +308,26 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         auto qk = [&](int c, int t, f4 (&s2)[2], auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             s2[0] = s2[1] = f4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 kf[kPF];
+            bf16x8 kf[PF];
 #pragma unroll
-            for (int i = 0; i < kPF - 1; ++i) kf[i] = kfrag(buf, t, i);
+            for (int i = 0; i < PF - 1; ++i) kf[i] = kfrag(buf, t, i);
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                if (ks + kPF - 1 < 18) kf[(ks + kPF - 1) % kPF] = kfrag(buf, t, ks + kPF - 1);
-                s2[ks & 1] = mfma16(kf[ks % kPF], qf[ks], s2[ks & 1]);
+                if (ks + PF - 1 < 18) kf[(ks + PF - 1) % PF] = kfrag(buf, t, ks + PF - 1);
+                s2[ks & 1] = mfma16(kf[ks % PF], qf[ks], s2[ks & 1]);
                 side(ks);
             }
         };
         // O^T[256h + 16j .. +15][rows] += V^T P^T over chunk c's 32 tokens, j = 0..15; side(j)
         auto pv = [&](int c, bf16x8 pT, auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
-            bf16x8 vf[kVPF];
+            bf16x8 vf[VPF];
 #pragma unroll
-            for (int i = 0; i < kVPF - 1; ++i) vf[i] = vfrag(buf, i);
+            for (int i = 0; i < VPF - 1; ++i) vf[i] = vfrag(buf, i);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                if (j + kVPF - 1 < 16) vf[(j + kVPF - 1) % kVPF] = vfrag(buf, j + kVPF - 1);
-                acc[j] = mfma16(vf[j % kVPF], pT, acc[j]);
+                if (j + VPF - 1 < 16) vf[(j + VPF - 1) % VPF] = vfrag(buf, j + VPF - 1);
+                acc[j] = mfma16(vf[j % VPF], pT, acc[j]);
                 side(j);
             }
         };
@@ -333,7 +342,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         auto mask_tile = [&](int c, int t, f4 s, Tile& T) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             const int tb = t0 + c * kChunk;
-            if constexpr (!SPARSE) {
+            if constexpr (!GATHER) {
                 // raw scores; a positive scale commutes with the maximum and is applied in the
                 // exponent (the launcher sends other scales to another kernel)
                 const int bnd = min(t1, limit + 1) - tb - 16 * t - 4 * g4;    // valid: i < bnd
@@ -341,12 +350,15 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 for (int i = 0; i < 4; ++i) T.s[i] = i < bnd ? s[i] : -INFINITY;
                 T.mx = fmaxf(fmaxf(T.s[0], T.s[1]), fmaxf(T.s[2], T.s[3])) * a.scale_log2;
             } else {
+                // fp8 pages also apply the row's causal limit: token i of the lane is visible
+                // while i <= lim
+                const int lim = SPARSE ? 3 : limit - tb - 16 * t - 4 * g4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = 16 * t + 4 * g4 + i;
                     // NaN marks an unused entry or a position past the list
                     const float sc = *reinterpret_cast<const float*>(buf + kChunk16 + tok * 32);
-                    const bool valid = sc == sc;
+                    const bool valid = (sc == sc) & (i <= lim);
                     T.tsc[i] = valid ? sc : 0.f;
                     T.s[i] = valid ? s[i] * (a.scale_log2 * sc) : -INFINITY;
                 }
@@ -359,10 +371,10 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (SPARSE) p[i] = exp2_fast(T.s[i] - m_use);
+                if constexpr (GATHER) p[i] = exp2_fast(T.s[i] - m_use);
                 else p[i] = exp2_fast(__builtin_fmaf(T.s[i], a.scale_log2, -m_use));
                 l_run += p[i];
-                if constexpr (SPARSE) p[i] *= T.tsc[i];
+                if constexpr (GATHER) p[i] *= T.tsc[i];
             }
             return make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         };
@@ -397,7 +409,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             for (int j = 0; j < 16; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
             bool restart = false;
             uint2 p_own;
-            if constexpr (!SPARSE) {
+            if constexpr (!GATHER) {
 #pragma unroll
                 for (int c = 0; c < AHEAD; ++c) {
                     const Plan p = plan_for(c);
@@ -420,7 +432,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             {
                 const Plan p = plan_for(AHEAD);
                 auto side0 = [&](int ks) {
-                    if constexpr (!SPARSE) {
+                    if constexpr (!GATHER) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
                     } else if ((ks & 1) == 0 && ks / 2 < kGather) {
                         convert(1, ks / 2);
@@ -443,7 +455,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 if (lane == 0) votes[wave] = 0;
             }
             for (int k = 1; k < nch; ++k) {
-                if constexpr (!SPARSE) wait_chunk();
+                if constexpr (!GATHER) wait_chunk();
                 // chunk k in LDS; probabilities and votes of chunk k-1 visible; slot (k-2) % DEPTH free
                 __syncthreads();
                 restart = restart | any_vote(k - 1);
@@ -453,7 +465,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 // S^T(k) of the own tile on the MFMAs while chunk k+AHEAD is copied (sparse:
                 // chunk k+1 is converted and chunk k+2 gathered)
                 qk(k, h, s2, [&](int ks) {
-                    if constexpr (!SPARSE) {
+                    if constexpr (!GATHER) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
                     } else if ((ks & 1) == 0 && ks / 2 < kGather) {
                         convert(k + 1, ks / 2);
@@ -518,6 +530,10 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         __syncthreads();                    // the exchange area is read: all of LDS is free
         char* stg = smem + wave * (16 * kOutPitch);
         const int row0 = rg * kRowsWg + 16 * rb;
+        // computed here, not hoisted out of the segment and pass loops, where they would hold
+        // registers through the chunk loop
+        int ln = lane, nrow = a.M - row0;
+        asm volatile("" : "+v"(ln), "+s"(nrow));
         if (final_out) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -528,9 +544,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             char* obase = static_cast<char*>(a.out) + ((size_t)grp * a.M + row0) * (kDv * 2) + 512 * h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int r = 2 * i + (lane >> 5), cgr = lane & 31;
+                const int r = 2 * i + (ln >> 5), cgr = ln & 31;
                 const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kOutPitch + cgr * 16);
-                if (row0 + r < a.M) *reinterpret_cast<uint4*>(obase + (size_t)r * (kDv * 2) + cgr * 16) = v;
+                if (r < nrow) *reinterpret_cast<uint4*>(obase + (size_t)r * (kDv * 2) + cgr * 16) = v;
             }
         } else {
 #pragma unroll
@@ -539,8 +555,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             char* pbase = reinterpret_cast<char*>(a.part_o) + ((size_t)slot * a.M + row0) * (kDv * 4) + 1024 * h;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kOutPitch + lane * 16);
-                if (row0 + r < a.M) *reinterpret_cast<uint4*>(pbase + (size_t)r * (kDv * 4) + lane * 16) = v;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kOutPitch + ln * 16);
+                if (r < nrow) *reinterpret_cast<uint4*>(pbase + (size_t)r * (kDv * 4) + ln * 16) = v;
             }
         }
         __syncthreads();                    // LDS (ring, index list, exchanges) free for the next segment
@@ -574,13 +590,17 @@ hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = (a.M + rows::kRowsWg - 1) / rows::kRowsWg;
     const dim3 grid(items * R), block(rows::kWaves * 64);
+#define MLA_ROWS_LAUNCH(MODE_)                                                                                     \
+    if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, true>), grid, block, 0, stream, a);      \
+    else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, false>), grid, block, 0, stream, a);
     if (sparse) {
-        if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<true, false>), grid, block, 0, stream, a);
+        MLA_ROWS_LAUNCH(rows::kSparseFp8)
+    } else if (a.kv_fp8) {
+        MLA_ROWS_LAUNCH(rows::kPagedFp8)
     } else {
-        if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<false, false>), grid, block, 0, stream, a);
+        MLA_ROWS_LAUNCH(rows::kPagedBf16)
     }
+#undef MLA_ROWS_LAUNCH
     return hipGetLastError();
 }
 

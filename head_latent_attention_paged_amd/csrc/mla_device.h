@@ -92,6 +92,19 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(unsigned, v);
 }
 
+// 8 e4m3 codes (two dwords) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
+#define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))
+    const uint4 v = make_uint4(MLA_CVT(lo, false), MLA_CVT(lo, true), MLA_CVT(hi, false), MLA_CVT(hi, true));
+#undef MLA_CVT
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// fp8 record rows in LDS (640 B = 40 granules of 16 B): granule g of row r sits at slot
+// g ^ swz8(r), an XOR on the low three granule bits that keeps the 16 rows of a K fragment read
+// (ds_read_b64) and of a V^T transposing read (ds_read_b64_tr_b8) on distinct banks (measured)
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 2); }
+
 // 16 e4m3 codes -> 16 bf16 (exact: every finite e4m3 value is a bf16 value)
 __device__ __forceinline__ void fp8x16_to_bf16(uint4 c, uint4& lo, uint4& hi) {
 #define MLA_CVT(w, h) __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, h))

@@ -56,7 +56,8 @@ struct AttnArgs {
     int causal;
     int num_parts;              // paged parts; sparse: splits per query token
     int split_len;              // sparse entries per split (multiple of kChunk)
-    int64_t kv_rows;            // sparse: records in the pool
+    int64_t kv_rows;            // sparse: records in the pool; paged fp8: pages * 64
+    int kv_fp8;                 // paged: 1 = 64-token pages of 640-byte fp8 records
     float scale_log2;           // softmax_scale * log2(e)
 };
 
@@ -67,6 +68,7 @@ void metadata_host(const int32_t* seqlens, int batch, int num_parts,
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_big(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream);
+hipError_t launch_decode_m16_fp8(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream);

@@ -916,6 +916,11 @@ static hipError_t launch_decode_t(const AttnArgs& a, int items, int R, hipStream
 
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const Tiling t = choose_tiling(a.M);
+    if (!sparse && a.kv_fp8) {
+        // fp8 pages: the 16-row streaming kernel, or the row-split kernel's fp8 gathers
+        if (a.M <= 16) return launch_decode_m16_fp8(a, stream);
+        return launch_decode_rows(a, false, stream);
+    }
     if (!sparse && a.M <= 16) {
         hipLaunchKernelGGL(mla_decode_m16_kernel, dim3(a.num_parts), dim3(256), 0, stream, a);
         return hipGetLastError();

@@ -127,6 +127,31 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
                               void* out, float* lse, void* stream);
 
 /*
+ * Paged MLA decode over an fp8 cache: the same call as mla_decode_paged with
+ * the cache in the fp8 layout of the decode path ("deepseek-ai/FlashMLA"
+ * project summary, section 사용 방법 step 3: flash_mla_with_kvcache on the
+ * FP8 KV cache; section 기술적 세부 사항: raw e4m3 values plus a per-token
+ * scale).
+ *
+ *   kcache   [device] uint8[num_blocks, 64, 640]: 64-token pages of records,
+ *            bytes [0,576) the OCP E4M3FN codes of the row's 576 dims,
+ *            bytes [576,580) the token's fp32 scale (little endian),
+ *            bytes [580,640) unused.  Row value = e4m3(code) * scale.
+ *
+ * Every other argument, the workspace size and the result are as for
+ * mla_decode_paged.  With s_q * h_q > 16 the cache must be at most
+ * 3.75 GiB (num_blocks * 64 * 640 bytes); larger caches return
+ * MLA_ERR_UNSUPPORTED.
+ */
+mla_status_t mla_decode_paged_fp8(const void* q, const void* kcache, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  float softmax_scale, int causal,
+                                  const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, void* stream);
+
+/*
  * Number of topk splits mla_decode_sparse uses per query token for a given
  * shape when called with splits = 0, and the workspace it then needs.  The
  * rule: as many splits as keep the work items (query tokens x row groups x

@@ -10,9 +10,9 @@ import sys
 import numpy as np
 import pytest
 
-from mla_inputs import make_config, make_paged, make_sparse
+from mla_inputs import make_config, make_paged, make_paged_fp8, make_sparse
 from mla_inputs.gen import bf16_bits_from_f32, bf16_bits_to_f32, quantize_rows_e4m3
-from oracle import paged_decode, sparse_decode
+from oracle import paged_decode, paged_decode_fp8, sparse_decode
 from tests.helpers import check_parity, dev_bf16, dev_i32, dev_u8, to_host
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +40,20 @@ def run_paged(env, inp, num_parts=None):
     mla, dev = env
     q = dev_bf16(inp.q, dev)
     kc = dev_bf16(inp.kcache, dev)
+    bt = dev_i32(inp.block_table, dev)
+    sl = dev_i32(inp.seqlens, dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
+    out, lse = mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal)
+    torch.cuda.synchronize()
+    return to_host(out, lse)
+
+
+def run_paged_fp8(env, inp, num_parts=None):
+    import torch
+
+    mla, dev = env
+    q = dev_bf16(inp.q, dev)
+    kc = dev_u8(inp.kcache, dev)
     bt = dev_i32(inp.block_table, dev)
     sl = dev_i32(inp.seqlens, dev)
     meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
@@ -135,6 +149,65 @@ def test_block_table_permutation_is_bitwise_invariant(env):
     inp.block_table = perm[inp.block_table].astype(np.int32)
     o2, l2 = run_paged(env, inp, 8)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------- paged, fp8 cache
+FP8_PAGED_CASES = [
+    # batch, s_q, h_q, seqlens, causal, num_parts
+    (3, 1, 16, [1, 64, 65], False, None),
+    (4, 1, 16, [63, 128, 129, 300], False, 1),
+    (2, 1, 16, [1000, 777], False, 64),
+    (3, 2, 8, [2, 100, 257], True, None),
+    (2, 4, 4, [3, 200], True, 5),
+    (3, 1, 16, [0, 50, 0], False, None),
+    (2, 2, 32, [130, 700], True, None),
+    (2, 2, 64, [1, 2], True, 4),
+    (2, 1, 48, [77, 300], False, None),
+    (2, 1, 32, [500, 64], False, 3),
+    (1, 2, 64, [4000], False, 16),
+    (3, 3, 16, [40, 96, 1], True, 3),
+]
+
+
+@pytest.mark.parametrize("case", FP8_PAGED_CASES, ids=[str(i) for i in range(len(FP8_PAGED_CASES))])
+def test_paged_fp8_cases(env, case):
+    batch, s_q, h_q, L, causal, P = case
+    _say("paged fp8 case", case)
+    inp = make_paged_fp8(batch, s_q, h_q, L, causal, seed=300 + sum(L) + h_q, poison=True)
+    o, l = run_paged_fp8(env, inp, P)
+    o_ref, l_ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
+    check_parity(o, l, o_ref, l_ref, "fp8 " + str(case))
+
+
+@pytest.mark.parametrize("h_q,scale", [(16, 2.5), (64, 2.5), (16, 0.0), (64, 0.0), (16, -0.05), (64, -0.05)])
+def test_paged_fp8_softmax_scales(env, h_q, scale):
+    """Large, zero and negative softmax scales over an fp8 cache (16-row and many-row kernels)."""
+    _say("paged fp8 scale", h_q, scale)
+    inp = make_paged_fp8(2, 1, h_q, [1800, 900], False, seed=450 + h_q, poison=True, softmax_scale=scale)
+    o, l = run_paged_fp8(env, inp)
+    o_ref, l_ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    check_parity(o, l, o_ref, l_ref, "fp8 scale %g h_q %d" % (scale, h_q))
+
+
+def test_paged_fp8_forced_splits(env):
+    inp = make_paged_fp8(3, 1, 16, [900, 1500, 64], False, seed=15, poison=True)
+    o_ref, l_ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    for P in (1, 2, 8, 64, 256):
+        _say("fp8 split", P)
+        o, l = run_paged_fp8(env, inp, P)
+        check_parity(o, l, o_ref, l_ref, "fp8 P=%d" % P)
+
+
+def test_full_size_paged_fp8_sampled(env):
+    _say("full-size fp8 paged (memory-bound shape)")
+    inp = make_config(6, poison=False)
+    o, l = run_paged_fp8(env, inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    sample = sorted(np.random.default_rng(6).choice(inp.batch, size=6, replace=False).tolist())
+    o_ref, l_ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale,
+                                    inp.causal, batches=sample)
+    err, rmse = _sampled(o, l, o_ref, l_ref, sample, "config 6")
+    _say("config 6 sampled max err", err, "rmse", rmse)
 
 
 # ----------------------------------------------------------------- sparse

@@ -20,7 +20,7 @@ def mla():
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "mla.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_function_is_exported(mla):
@@ -52,11 +52,12 @@ def test_num_parts_and_workspace(mla):
     assert mla.workspace_size_sparse(1, 1, 16, 32, 1) == 0          # one split needs no workspace
 
 
-def _paged_call(mla, **kw):
+def _paged_call(mla, fp8=False, **kw):
     args = dict(q=16, kc=16, nb=4, bt=16, maxb=1, sl=16, batch=1, s_q=1, h_q=16, scale=0.04, causal=0,
                 meta=16, ns=16, P=8, ws=16, wsb=1 << 30, out=16, lse=16)
     args.update(kw)
-    return mla.lib.mla_decode_paged(args["q"], args["kc"], args["nb"], args["bt"], args["maxb"], args["sl"],
+    f = mla.lib.mla_decode_paged_fp8 if fp8 else mla.lib.mla_decode_paged
+    return f(args["q"], args["kc"], args["nb"], args["bt"], args["maxb"], args["sl"],
                                     args["batch"], args["s_q"], args["h_q"], args["scale"], args["causal"],
                                     args["meta"], args["ns"], args["P"], args["ws"], args["wsb"],
                                     args["out"], args["lse"], None)
@@ -73,6 +74,17 @@ def test_paged_validation_before_launch(mla):
     assert _paged_call(mla, s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
     assert _paged_call(mla, wsb=100) == mla.MLA_ERR_WORKSPACE
     assert _paged_call(mla, ws=None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_paged_fp8_validation_before_launch(mla):
+    # the same host checks as the bf16 call, plus the 32-bit offset limit of the many-row path
+    assert _paged_call(mla, fp8=True, kc=None) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, fp8=True, nb=0) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, fp8=True, scale=float("inf")) == mla.MLA_ERR_INVALID_ARG
+    assert _paged_call(mla, fp8=True, wsb=100) == mla.MLA_ERR_WORKSPACE
+    assert _paged_call(mla, fp8=True, s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
+    # more than 16 rows over a cache beyond 3.75 GiB (100000 pages x 40 KiB)
+    assert _paged_call(mla, fp8=True, h_q=64, nb=100000) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_sparse_validation_before_launch(mla):
