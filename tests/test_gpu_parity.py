@@ -288,6 +288,45 @@ def test_paged_wide_score_range(env, case):
     check_parity(o, l, o_ref, l_ref, "ramp " + str(case))
 
 
+def _ramp_fp8(inp, top, seed=8):
+    """The score ramp of _ramp on an fp8 page cache: rows rebuilt along each sequence and
+    quantised per token into records (poisoned records stay as they are)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(576)
+    u /= np.linalg.norm(u)
+    sigma_inv = 1.0 / inp.softmax_scale
+    qf = u * sigma_inv + 0.02 * sigma_inv * rng.standard_normal(inp.q.shape)
+    inp.q = bf16_bits_from_f32(qf.astype(np.float32))
+    for b, L in enumerate(inp.seqlens):
+        rows = np.empty((int(L), 576))
+        for t in range(int(L)):
+            f = (t + 1) / L if top > 0 else (L - t) / L
+            rows[t] = abs(top) * f * u + 0.5 * rng.standard_normal(576)
+        rec = quantize_rows_e4m3(rows.astype(np.float32))
+        for t in range(int(L)):
+            inp.kcache[inp.block_table[b, t // 64], t % 64] = rec[t]
+    return inp
+
+
+FP8_RAMP_CASES = [
+    # batch, s_q, h_q, seqlens, causal, top (nats), num_parts
+    (2, 1, 16, [1500, 700], False, 150.0, None),
+    (2, 1, 16, [1500, 700], False, -150.0, None),
+    (2, 1, 64, [1500, 700], False, 150.0, None),
+    (2, 2, 32, [1200, 333], True, -150.0, 8),
+]
+
+
+@pytest.mark.parametrize("case", FP8_RAMP_CASES, ids=[str(i) for i in range(len(FP8_RAMP_CASES))])
+def test_paged_fp8_wide_score_range(env, case):
+    batch, s_q, h_q, L, causal, top, P = case
+    _say("paged fp8 ramp case", case)
+    inp = _ramp_fp8(make_paged_fp8(batch, s_q, h_q, L, causal, seed=320 + h_q, poison=True), top)
+    o, l = run_paged_fp8(env, inp, P)
+    o_ref, l_ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
+    check_parity(o, l, o_ref, l_ref, "fp8 ramp " + str(case))
+
+
 def _ramp_sparse(inp, top, seed=9):
     """Sparse input whose scores move linearly along each query's index list, from ~0 to ~`top`
     nats (falling for top < 0); one query token per sequence, so every record has one position."""
