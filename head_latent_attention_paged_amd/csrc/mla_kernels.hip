@@ -776,22 +776,35 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
 // --------------------------------------------------------------------------
 // K0: tile-scheduler metadata (one workgroup; integer only, same partition as the host twin)
 // --------------------------------------------------------------------------
-constexpr int kMetaThreads = 1024;
+constexpr int kMetaThreads = 256;
 
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp) {
-    // exclusive scan of v over the 1024 threads; tmp holds 1024 ints
-    const int t = threadIdx.x;
-    tmp[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kMetaThreads; off <<= 1) {
-        const int add = (t >= off) ? tmp[t - off] : 0;
-        __syncthreads();
-        tmp[t] += add;
-        __syncthreads();
+// exclusive scan of v over the workgroup's threads, and the workgroup total: a shuffle scan in
+// each wave, then one over the wave totals (tmp holds kMetaThreads / 64 ints)
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
+    constexpr int kWavesMeta = kMetaThreads / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int incl = tmp[t];
+    if (lane == 63) tmp[w] = x;
     __syncthreads();
-    return incl - v;
+    if (w == 0) {
+        int s = lane < kWavesMeta ? tmp[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kWavesMeta; off <<= 1) {
+            const int y = __shfl_up(s, off);
+            if (lane >= off) s += y;
+        }
+        if (lane < kWavesMeta) tmp[lane] = s;
+    }
+    __syncthreads();
+    const int before = w > 0 ? tmp[w - 1] : 0;
+    total = tmp[kWavesMeta - 1];
+    __syncthreads();
+    return before + x - v;
 }
 
 __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_t* __restrict__ seqlens, int batch,
@@ -799,7 +812,7 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
                                                                     int32_t* __restrict__ num_splits) {
     __shared__ int cpre[kMaxBatchMeta + 1];   // cost prefix C_b
     __shared__ int spre[kMaxBatchMeta + 1];   // split prefix
-    __shared__ int tmp[kMetaThreads];
+    __shared__ int tmp[kMetaThreads / 64];
     __shared__ int s_payload;
     const int t = threadIdx.x;
     // cost prefix
@@ -812,13 +825,10 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
             const int nb = L > 0 ? (L + kPage - 1) / kPage : 0;
             cost = nb > 0 ? nb + kMetaOverheadBlocks : 0;
         }
-        const int ex = block_excl_scan(cost, tmp);
+        int tot;
+        const int ex = block_excl_scan(cost, tmp, tot);
         if (b < batch) cpre[b] = carry + ex;
-        __syncthreads();
-        if (t == kMetaThreads - 1) tmp[0] = ex + cost;
-        __syncthreads();
-        carry += tmp[0];
-        __syncthreads();
+        carry += tot;
     }
     if (t == 0) cpre[batch] = carry;
     const int total = carry;
@@ -838,13 +848,10 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
                 sp = (u0 + nb - 1) / payload - u0 / payload + 1;
             }
         }
-        const int ex = block_excl_scan(sp, tmp);
+        int tot;
+        const int ex = block_excl_scan(sp, tmp, tot);
         if (b < batch) spre[b] = carry + ex;
-        __syncthreads();
-        if (t == kMetaThreads - 1) tmp[0] = ex + sp;
-        __syncthreads();
-        carry += tmp[0];
-        __syncthreads();
+        carry += tot;
     }
     if (t == 0) spre[batch] = carry;
     __syncthreads();
