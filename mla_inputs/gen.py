@@ -81,6 +81,7 @@ class PagedInputs:
     causal: bool
     softmax_scale: float        # an fp32 value, stored as a Python float
     poison_page: int            # index of the all-NaN page, or -1
+    sinks: Optional[np.ndarray] = None   # fp32 [h_q] per-head attention sinks, or None
 
     @property
     def batch(self) -> int:
@@ -90,6 +91,10 @@ class PagedInputs:
     def num_pages(self) -> int:
         return int(self.kcache.shape[0])
 
+    @property
+    def d_qk(self) -> int:
+        return int(self.kcache.shape[-1])
+
 
 def _fp32(x: float) -> float:
     return float(np.float32(x))
@@ -98,7 +103,8 @@ def _fp32(x: float) -> float:
 def make_paged(batch: int, s_q: int, h_q: int,
                seqlens: Union[Sequence[int], tuple],
                causal: bool, seed: int, poison: bool = True,
-               softmax_scale: Optional[float] = None) -> PagedInputs:
+               softmax_scale: Optional[float] = None,
+               d_qk: int = D_QK, sinks: bool = False) -> PagedInputs:
     """Draw one paged decode input set.
 
     ``seqlens`` is either an explicit list of ``batch`` lengths or
@@ -108,6 +114,11 @@ def make_paged(batch: int, s_q: int, h_q: int,
     all-NaN page is appended, every unused block-table slot points at it, and
     the rows past each sequence's end inside its last page are set to NaN, so
     any read outside the visible tokens shows up in the result.
+
+    ``d_qk = 512`` draws the DeepSeek-V4 geometry's latent-only rows (both K and V, no RoPE
+    part; "[flashinfer] ...", README), with the default scale 512^-0.5.  ``sinks`` draws one
+    attention-sink logit per head after everything else, ln(mean L) + U[-2, 2], so that a sink
+    and the cached tokens carry comparable weight.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     if isinstance(seqlens, tuple) and len(seqlens) == 3 and seqlens[0] == "uniform":
@@ -118,6 +129,8 @@ def make_paged(batch: int, s_q: int, h_q: int,
             raise ValueError("seqlens must have one entry per sequence")
     if (L < 0).any():
         raise ValueError("sequence lengths must be >= 0")
+    if d_qk not in (D_QK, D_V):
+        raise ValueError("d_qk must be 576 or 512")
     nblk = (L.astype(np.int64) + PAGE - 1) // PAGE
     total = int(nblk.sum())
     max_blocks = max(1, int(nblk.max()) if batch else 1)
@@ -129,18 +142,22 @@ def make_paged(batch: int, s_q: int, h_q: int,
         n = int(nblk[b])
         bt[b, :n] = perm[off:off + n]
         off += n
-    q = _normal_bf16(rng, (batch, s_q, h_q, D_QK))
-    kc = _normal_bf16(rng, (total, PAGE, 1, D_QK))
+    q = _normal_bf16(rng, (batch, s_q, h_q, d_qk))
+    kc = _normal_bf16(rng, (total, PAGE, 1, d_qk))
     poison_page = -1
     if poison:
-        kc = np.concatenate([kc, np.full((1, PAGE, 1, D_QK), BF16_NAN, dtype=np.uint16)], axis=0)
+        kc = np.concatenate([kc, np.full((1, PAGE, 1, d_qk), BF16_NAN, dtype=np.uint16)], axis=0)
         poison_page = total
         for b in range(batch):
             if L[b] % PAGE:
                 kc[bt[b, L[b] // PAGE], L[b] % PAGE:, 0, :] = BF16_NAN
-    scale = _fp32(D_QK ** -0.5 if softmax_scale is None else softmax_scale)
+    scale = _fp32(d_qk ** -0.5 if softmax_scale is None else softmax_scale)
+    sk = None
+    if sinks:
+        sk = (np.log(max(1.0, float(L.mean()) if batch else 1.0)) +
+              rng.uniform(-2.0, 2.0, size=h_q)).astype(np.float32)
     return PagedInputs(q=q, kcache=kc, block_table=bt, seqlens=L, s_q=s_q, h_q=h_q,
-                       causal=bool(causal), softmax_scale=scale, poison_page=poison_page)
+                       causal=bool(causal), softmax_scale=scale, poison_page=poison_page, sinks=sk)
 
 
 @dataclasses.dataclass
@@ -318,6 +335,10 @@ CONFIGS = {
     # fp8 KV cache for the dense paged path: the memory-bound shape over 640-byte records
     6: dict(kind="paged_fp8", name="memory-bound paged decode, fp8 KV: b=128 s_q=1 h_q=16 L=4096",
             batch=128, s_q=1, h_q=16, seqlens=[4096] * 128, causal=False),
+    # DeepSeek-V4 decode geometry: 512-wide latent rows that are K and V, six causal query
+    # tokens per request, 64 heads, per-head attention sinks
+    7: dict(kind="paged_v4", name="V4-geometry paged decode: b=64 s_q=6 causal h_q=64 L=4096 d=512 + sinks",
+            batch=64, s_q=6, h_q=64, seqlens=[4096] * 64, causal=True),
 }
 
 
@@ -326,11 +347,14 @@ def config_info(k: int) -> dict:
 
 
 def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
-    """Inputs for workload ``k`` (1..6) with seed 1000 + k unless given."""
+    """Inputs for workload ``k`` (1..7) with seed 1000 + k unless given."""
     c = CONFIGS[k]
     seed = 1000 + k if seed is None else seed
     if c["kind"] == "paged":
         return make_paged(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison)
     if c["kind"] == "paged_fp8":
         return make_paged_fp8(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison)
+    if c["kind"] == "paged_v4":
+        return make_paged(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison,
+                          d_qk=D_V, sinks=True)
     return make_sparse(c["batch"], c["s_q"], c["h_q"], c["tokens_per_seq"], c["topk"], c["p_invalid"], seed)

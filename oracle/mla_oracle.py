@@ -35,6 +35,11 @@ online softmax and no splitting:
   values times a per-token scale (same section, KV cache format), decoded
   exactly in float64 from the OCP E4M3FN encoding.
 * An empty visible set gives O = 0 and LSE = -inf.
+* DeepSeek-V4 decode geometry ("[flashinfer] ...", README): the cached row is 512 wide and is
+  both K and V (no RoPE part), and each head may have an attention sink: one more logit in its
+  softmax denominator that carries no value.  Reading: the sink is in the units of the scaled
+  scores (natural log, not multiplied by softmax_scale), and the returned LSE is the log of the
+  whole denominator, sink included; with no visible token O = 0 and LSE = the sink.
 
 The split-KV combine used by the GPU path is, mathematically, the same
 definition evaluated on a partition of the visible set; ``lse_combine`` states
@@ -96,25 +101,37 @@ def sparse_rows_f64(kv_records: np.ndarray, rows: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # The attention definition
 # --------------------------------------------------------------------------
-def attend(q: np.ndarray, rows: np.ndarray, sigma: float) -> Tuple[np.ndarray, np.ndarray]:
+def attend(q: np.ndarray, rows: np.ndarray, sigma: float,
+           sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """softmax(sigma * q rows^T) rows[:, :512] and its natural-log LSE, for every query row.
 
-    q: [H, 576] float64, rows: [T, 576] float64.  Returns O [H, 512], LSE [H].
+    q: [H, D] float64, rows: [T, D] float64 (D = 576, or 512 for the latent-only row that is
+    both K and V).  Returns O [H, 512], LSE [H].
+
+    ``sink`` [H] (natural-log logits, or None) is the per-head attention sink of the DeepSeek-V4
+    decode geometry ("[flashinfer] ...", README: an optional per-head attention sink): one more
+    logit in each head's softmax denominator that carries no value, compared with the scaled
+    scores as it is.  LSE is the log of that whole denominator.
     """
     H = q.shape[0]
-    if rows.shape[0] == 0:
+    T = rows.shape[0]
+    if T == 0 and sink is None:
         return np.zeros((H, D_V)), np.full(H, -np.inf)
     z = sigma * (rows @ q.T)                  # [T, H] scaled scores
-    m = z.max(axis=0)                         # [H]
+    m = z.max(axis=0) if T > 0 else np.full(H, -np.inf)    # [H]
+    if sink is not None:
+        m = np.maximum(m, sink)
     e = np.exp(z - m)                         # [T, H]
     denom = e.sum(axis=0)                     # [H]
+    if sink is not None:
+        denom = denom + np.exp(sink - m)
     o = (e.T @ rows[:, :D_V]) / denom[:, None]
     return o, m + np.log(denom)
 
 
 def gather_paged_rows(kcache_bits: np.ndarray, block_table_row: np.ndarray, n_tokens: int) -> np.ndarray:
     """Rows of logical tokens 0..n_tokens-1 of one sequence, gathered through its block table."""
-    out = np.empty((n_tokens, D_QK), dtype=np.float64)
+    out = np.empty((n_tokens, kcache_bits.shape[-1]), dtype=np.float64)
     for t in range(0, n_tokens, PAGE):
         page = int(block_table_row[t // PAGE])
         n = min(PAGE, n_tokens - t)
@@ -131,13 +148,15 @@ def visible_count(L: int, s_q: int, s: int, causal: bool) -> int:
 
 def paged_decode(q_bits: np.ndarray, kcache_bits: np.ndarray, block_table: np.ndarray,
                  seqlens: np.ndarray, softmax_scale: float, causal: bool,
-                 batches: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                 batches: Optional[Iterable[int]] = None,
+                 sinks: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Paged MLA decode.
 
-    q_bits [B, s_q, h_q, 576] bf16 bits; kcache_bits [pages, 64, 1, 576] bf16 bits;
-    block_table [B, max_blocks] int32; seqlens [B] int32; softmax_scale is an
-    fp32 value.  Returns O [B, s_q, h_q, 512] and LSE [B, s_q, h_q] in float64.
-    With ``batches`` only those sequences are computed (the rest stay NaN).
+    q_bits [B, s_q, h_q, D] bf16 bits; kcache_bits [pages, 64, 1, D] bf16 bits (D = 576, or 512
+    for the DeepSeek-V4 latent row that is both K and V); block_table [B, max_blocks] int32;
+    seqlens [B] int32; softmax_scale is an fp32 value; sinks [h_q] fp32 or None (see
+    ``attend``).  Returns O [B, s_q, h_q, 512] and LSE [B, s_q, h_q] in float64.  With
+    ``batches`` only those sequences are computed (the rest stay NaN).
     """
     B, s_q, h_q, _ = q_bits.shape
     sigma = float(np.float32(softmax_scale))
@@ -148,7 +167,8 @@ def paged_decode(q_bits: np.ndarray, kcache_bits: np.ndarray, block_table: np.nd
         rows = gather_paged_rows(kcache_bits, block_table[b], L)
         for s in range(s_q):
             n = visible_count(L, s_q, s, causal)
-            O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows[:n], sigma)
+            O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows[:n], sigma,
+                                        None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64))
     return O, LSE
 
 

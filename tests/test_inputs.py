@@ -72,12 +72,24 @@ def test_sparse_generator_indices():
 
 
 def test_config_table():
-    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6}
+    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7}
     assert CONFIGS[2]["batch"] == 128 and CONFIGS[4]["seqlens"][0] == 65536
     assert CONFIGS[5]["topk"] == 2048
     # the fp8-cache workload is the memory-bound shape over fp8 records
     assert CONFIGS[6]["kind"] == "paged_fp8"
     assert all(CONFIGS[6][k] == CONFIGS[2][k] for k in ("batch", "s_q", "h_q", "seqlens", "causal"))
+
+
+def test_v4_geometry_generator():
+    inp = make_paged(3, 6, 8, [100, 64, 5], True, seed=5, d_qk=512, sinks=True)
+    assert inp.q.shape == (3, 6, 8, 512) and inp.kcache.shape[1:] == (64, 1, 512)
+    assert abs(inp.softmax_scale - float(np.float32(512 ** -0.5))) == 0
+    assert inp.sinks.shape == (8,) and inp.sinks.dtype == np.float32
+    mean_l = np.log(np.mean([100, 64, 5]))
+    assert np.all(np.abs(inp.sinks - mean_l) <= 2.0 + 1e-6)
+    # the draws before the sinks are those of the same call without sinks
+    plain = make_paged(3, 6, 8, [100, 64, 5], True, seed=5, d_qk=512)
+    assert np.array_equal(plain.kcache, inp.kcache) and plain.sinks is None
 
 
 def test_paged_fp8_generator():

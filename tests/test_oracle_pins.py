@@ -364,6 +364,64 @@ def test_paged_fp8_never_reads_poisoned_records():
     assert np.array_equal(O, Oc) and np.array_equal(LSE, Lc)
 
 
+# ----------------------------------------------------------------- V4 geometry: 512-wide rows, sinks
+def test_512_wide_rows_equal_576_with_zero_rope_dims():
+    """A 512-wide latent row (K and V) scores like a 576-wide row whose 64 RoPE dims are zero in
+    both q and k, and its value is the same 512 dims."""
+    inp = make_paged(2, 2, 16, [150, 70], True, seed=51, poison=True, d_qk=512)
+    O5, L5 = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    zq = np.zeros(inp.q.shape[:-1] + (64,), dtype=np.uint16)
+    zk = np.zeros(inp.kcache.shape[:-1] + (64,), dtype=np.uint16)
+    q576 = np.concatenate([inp.q, zq], axis=-1)
+    k576 = np.concatenate([inp.kcache, zk], axis=-1)
+    k576[inp.poison_page] = 0x7FC0
+    O6, L6 = paged_decode(q576, k576, inp.block_table, inp.seqlens, inp.softmax_scale, True)
+    assert np.allclose(O5, O6, rtol=0, atol=1e-12) and np.allclose(L5, L6, rtol=0, atol=1e-12)
+
+
+def test_sink_of_minus_infinity_is_no_sink():
+    inp = make_paged(2, 1, 16, [100, 3], False, seed=52, d_qk=512)
+    O, LSE = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False)
+    Os, Ls = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, False,
+                          sinks=np.full(16, -np.inf, dtype=np.float32))
+    assert np.array_equal(O, Os) and np.array_equal(LSE, Ls)
+
+
+def test_sink_closed_forms():
+    """Equal scores z = 0 over n tokens with sink s: O = mean(V) * n / (n + e^s), LSE = ln(n + e^s).
+    One token with score z0: O = v / (1 + e^(s - z0)), LSE = logaddexp(z0, s).  No tokens:
+    O = 0, LSE = s."""
+    rng = np.random.default_rng(53)
+    n = 37
+    rows = bf16_to_f64(_bf16(rng.standard_normal((n, 512))))
+    s = np.array([-3.0, 0.0, 2.5, 9.0])
+    o, lse = attend(np.zeros((4, 512)), rows, SIGMA, sink=s)
+    for h in range(4):
+        assert np.allclose(o[h], rows.mean(axis=0) * n / (n + math.exp(s[h])), rtol=0, atol=1e-13)
+        assert abs(lse[h] - math.log(n + math.exp(s[h]))) < 1e-12
+    q = bf16_to_f64(_bf16(rng.standard_normal((4, 512))))
+    o1, l1 = attend(q, rows[:1], SIGMA, sink=s)
+    z0 = SIGMA * rows[0] @ q.T
+    for h in range(4):
+        assert np.allclose(o1[h], rows[0] / (1 + math.exp(s[h] - z0[h])), rtol=1e-12, atol=1e-14)
+        assert abs(l1[h] - np.logaddexp(z0[h], s[h])) < 1e-12
+    o0, l0 = attend(q, rows[:0], SIGMA, sink=s)
+    assert np.all(o0 == 0) and np.array_equal(l0, s)
+
+
+def test_sink_is_a_valueless_part_in_the_split_combine():
+    """Attention with a sink == lse_combine of the sink-free result and a part with O = 0 and
+    LSE = sink (the identity the GPU combine uses for split rows)."""
+    rng = np.random.default_rng(54)
+    rows = bf16_to_f64(_bf16(rng.standard_normal((200, 512))))
+    q = bf16_to_f64(_bf16(rng.standard_normal((8, 512))))
+    s = rng.uniform(-2, 6, size=8)
+    o, lse = attend(q, rows, SIGMA, sink=s)
+    o_t, l_t = attend(q, rows, SIGMA)
+    oc, lc = lse_combine(np.stack([o_t, np.zeros_like(o_t)]), np.stack([l_t, s]))
+    assert np.allclose(o, oc, rtol=0, atol=1e-13) and np.allclose(lse, lc, rtol=0, atol=1e-12)
+
+
 def test_visible_count():
     assert visible_count(10, 1, 0, False) == 10
     assert visible_count(10, 1, 0, True) == 10
