@@ -37,17 +37,19 @@ def paged_counts(inp):
     L = inp.seqlens.astype(np.int64)
     b, s_q, h_q = inp.batch, inp.s_q, inp.h_q
     M = s_q * h_q
-    row_bytes = 580 if inp.kcache.dtype == np.uint8 else D_QK * 2
+    d = D_QK if inp.kcache.dtype == np.uint8 else inp.kcache.shape[-1]    # 576, or 512-wide latent rows
+    row_bytes = 580 if inp.kcache.dtype == np.uint8 else d * 2
     kv = int(L.sum()) * row_bytes
     nblk = int(((L + 63) // 64).sum())
-    byts = kv + b * M * D_QK * 2 + b * M * D_V * 2 + b * M * 4 + nblk * 4 + b * 4
+    sinks = 0 if getattr(inp, "sinks", None) is None else h_q * 4
+    byts = kv + b * M * d * 2 + b * M * D_V * 2 + b * M * 4 + nblk * 4 + b * 4 + sinks
     vis = 0
     for s in range(s_q):
         if inp.causal:
             vis += int(np.clip(L - s_q + s + 1, 0, None).sum())
         else:
             vis += int(L.sum())
-    flops = 2 * (D_QK + D_V) * h_q * vis
+    flops = 2 * (d + D_V) * h_q * vis
     return byts, flops
 
 
@@ -168,7 +170,13 @@ def setup_paged(torch, mla, inp, dev):
     from tests.helpers import dev_bf16, dev_i32, dev_u8
 
     q = dev_bf16(inp.q, dev)
-    kc = dev_u8(inp.kcache, dev) if inp.kcache.dtype == np.uint8 else dev_bf16(inp.kcache, dev)
+    if inp.kcache.dtype == np.uint8:
+        kc = dev_u8(inp.kcache, dev)
+    elif inp.kcache.shape[-1] == D_V:        # 512-wide latent rows (K and V)
+        kc = dev_bf16(inp.kcache.reshape(inp.kcache.shape[0], 64, D_V), dev)
+    else:
+        kc = dev_bf16(inp.kcache, dev)
+    sk = None if getattr(inp, "sinks", None) is None else torch.from_numpy(inp.sinks).to(dev)
     bt, sl = dev_i32(inp.block_table, dev), dev_i32(inp.seqlens, dev)
     P = mla.num_parts(inp.h_q, inp.s_q)
     out = torch.empty((inp.batch, inp.s_q, inp.h_q, D_V), dtype=torch.bfloat16, device=dev)
@@ -177,11 +185,11 @@ def setup_paged(torch, mla, inp, dev):
     meta = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
 
     def decode():
-        mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws)
+        mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws, sinks=sk)
 
     def step():
         m = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
-        mla.decode_paged(q, kc, bt, sl, m, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws)
+        mla.decode_paged(q, kc, bt, sl, m, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws, sinks=sk)
 
     return step, decode
 
@@ -252,7 +260,7 @@ def run_calls(k, n):
 
     dev = torch.device("cuda:0")
     inp = make_config(k, poison=False)
-    if CONFIGS[k]["kind"] in ("paged", "paged_fp8"):
+    if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4"):
         _, fn = setup_paged(torch, mla, inp, dev)
     else:
         _, fn = setup_sparse(torch, mla, inp, dev)
@@ -340,10 +348,10 @@ def main():
     if args.extra:
         flush = Flusher(torch, dev)
         extra = {}
-        for k in (2, 3, 4, 5, 6):
+        for k in (2, 3, 4, 5, 6, 7):
             print("[bench] workload %d" % k, file=sys.stderr, flush=True)
             ik = inp if k == 2 else make_config(k, poison=False)
-            if CONFIGS[k]["kind"] in ("paged", "paged_fp8"):
+            if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4"):
                 _, fn = setup_paged(torch, mla, ik, dev)
                 b_k, f_k = paged_counts(ik)
             else:

@@ -22,7 +22,8 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP
 
 EXPORTS = (
     "mla_status_string", "mla_num_parts", "mla_get_metadata", "mla_get_metadata_host",
-    "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_sparse_splits",
+    "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_decode_paged_latent512",
+    "mla_sparse_splits",
     "mla_workspace_size_sparse", "mla_decode_sparse",
 )
 
@@ -56,6 +57,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged.restype = i32
     lib.mla_decode_paged_fp8.argtypes = lib.mla_decode_paged.argtypes
     lib.mla_decode_paged_fp8.restype = i32
+    lib.mla_decode_paged_latent512.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp,
+                                               vp, vp, i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_paged_latent512.restype = i32
     lib.mla_sparse_splits.argtypes = [i32, i32, i32, i32]
     lib.mla_sparse_splits.restype = i32
     lib.mla_workspace_size_sparse.argtypes = [i32, i32, i32, i32, i32]
@@ -138,16 +142,25 @@ def decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tenso
                  cache_seqlens: torch.Tensor, metadata: Tuple[torch.Tensor, torch.Tensor],
                  softmax_scale: float = D_QK ** -0.5, causal: bool = False,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 workspace: Optional[torch.Tensor] = None,
+                 sinks: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MLA decode; returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q]).
 
-    kcache is bf16 [num_blocks, 64, 1, 576], or uint8 [num_blocks, 64, 640] fp8 records (e4m3
-    codes of the 576 dims, the token's fp32 scale at byte 576), which calls mla_decode_paged_fp8.
+    kcache is bf16 [num_blocks, 64, 1, 576]; or uint8 [num_blocks, 64, 640] fp8 records (e4m3
+    codes of the 576 dims, the token's fp32 scale at byte 576), which calls mla_decode_paged_fp8;
+    or, with q of 512 dims, bf16 [num_blocks, 64, 512] latent rows that are K and V (the
+    DeepSeek-V4 geometry), which calls mla_decode_paged_latent512 with the optional per-head
+    ``sinks`` (fp32 [h_q]).
     """
     batch, s_q, h_q, d = q.shape
-    if d != D_QK:
-        raise ValueError("q must have 576 dims per head")
+    if d not in (D_QK, D_V):
+        raise ValueError("q must have 576 (or 512) dims per head")
     _require(q, "q", torch.bfloat16)
+    if d == D_V:
+        return _decode_paged_latent512(q, kcache, block_table, cache_seqlens, metadata, softmax_scale,
+                                       causal, out, lse, workspace, sinks)
+    if sinks is not None:
+        raise ValueError("attention sinks come with the 512-wide latent rows")
     fp8 = kcache.dtype == torch.uint8
     if fp8:
         _require(kcache, "kcache", torch.uint8)
@@ -175,6 +188,38 @@ def decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tenso
     _check(name, getattr(lib, name)(
         q.data_ptr(), kcache.data_ptr(), kcache.shape[0], block_table.data_ptr(), block_table.shape[1],
         cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
+        tile_meta.data_ptr(), num_splits.data_ptr(), P,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, lse
+
+
+def _decode_paged_latent512(q, kcache, block_table, cache_seqlens, metadata, softmax_scale, causal,
+                            out, lse, workspace, sinks):
+    batch, s_q, h_q, _ = q.shape
+    _require(kcache, "kcache", torch.bfloat16)
+    if kcache.dim() != 3 or tuple(kcache.shape[1:]) != (PAGE, D_V):
+        raise ValueError("kcache must be [num_blocks, 64, 512] for 512-wide latent rows")
+    _require(block_table, "block_table", torch.int32)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
+    if sinks is not None:
+        _require(sinks, "sinks", torch.float32, (h_q,))
+    tile_meta, num_splits = metadata
+    P = tile_meta.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, (batch, s_q, h_q, D_V))
+    _require(lse, "lse", torch.float32, (batch, s_q, h_q))
+    need = workspace_size(batch, s_q, h_q, P)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_paged_latent512", lib.mla_decode_paged_latent512(
+        q.data_ptr(), kcache.data_ptr(), kcache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
+        None if sinks is None else sinks.data_ptr(),
         tile_meta.data_ptr(), num_splits.data_ptr(), P,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))

@@ -138,7 +138,8 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
                                       float softmax_scale, int causal,
                                       const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
                                       void* workspace, size_t workspace_bytes,
-                                      void* out, float* lse, void* stream, bool fp8) {
+                                      void* out, float* lse, void* stream, bool fp8,
+                                      int d_qk = mla::kDqk, const float* sinks = nullptr) {
     if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0 || max_blocks <= 0 || num_blocks <= 0)
@@ -177,9 +178,11 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.kv_fp8 = fp8 ? 1 : 0;
     a.kv_rows = num_blocks * mla::kPage;
+    a.d_qk = d_qk;
+    a.sinks = sinks;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (mla::launch_decode(a, false, s) != hipSuccess) return MLA_ERR_HIP;
-    if (mla::launch_combine(a.part_o, a.part_lse, num_splits, 0, batch, M, out, lse, s) != hipSuccess)
+    if (mla::launch_combine(a.part_o, a.part_lse, num_splits, 0, batch, M, out, lse, s, sinks, h_q) != hipSuccess)
         return MLA_ERR_HIP;
     return MLA_OK;
 }
@@ -194,6 +197,18 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
     return decode_paged_impl(q, kcache, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
                              softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
                              workspace_bytes, out, lse, stream, false);
+}
+
+mla_status_t mla_decode_paged_latent512(const void* q, const void* kcache, int64_t num_blocks,
+                                       const int32_t* block_table, int max_blocks,
+                                       const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                       float softmax_scale, int causal, const float* sinks,
+                                       const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* out, float* lse, void* stream) {
+    return decode_paged_impl(q, kcache, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                             softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
+                             workspace_bytes, out, lse, stream, false, mla::kDv, sinks);
 }
 
 mla_status_t mla_decode_paged_fp8(const void* q, const void* kcache, int64_t num_blocks,
@@ -246,6 +261,7 @@ mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens
     a.M = h_q;
     a.topk = topk;
     a.kv_rows = num_tokens;
+    a.d_qk = mla::kDqk;
     a.num_parts = eff;
     a.split_len = sparse_split_len(topk, req);
     a.scale_log2 = softmax_scale * 1.4426950408889634f;

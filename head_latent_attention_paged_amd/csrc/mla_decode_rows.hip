@@ -69,7 +69,7 @@ constexpr int kGather = 3;
 constexpr int kOutPitch = 1040;
 constexpr unsigned kNoRecord = 0xFFFFF000u;
 
-template <bool GATHER>
+template <bool GATHER, int D>
 struct Cfg {
     // a ring slot holds a bf16 chunk; sparse adds the 32 token scales (32-byte stride)
     static constexpr int BUF = kChunk16 + (GATHER ? kChunk * 32 : 0);
@@ -78,8 +78,8 @@ struct Cfg {
     static constexpr int DEPTH = GATHER ? 3 : 4;
     static constexpr int AHEAD = DEPTH - 2;
     // paged copies per wave per chunk: 32 rows of region A + 4 KB of region B = 36 x 1 KB over
-    // eight waves, the last four repeated
-    static constexpr int OPS = 5;
+    // eight waves, the last four repeated; 512-wide rows have no region B: 32 x 1 KB
+    static constexpr int OPS = D == kDqk ? 5 : 4;
     static constexpr int RING = DEPTH * BUF;
     static constexpr int IDX = GATHER ? kMaxSparseSplit * 4 : 0;        // a segment's index list
     static constexpr int PAGES = GATHER ? 0 : kWaves * 64 * 4;            // per-wave page windows
@@ -92,12 +92,20 @@ struct Cfg {
 // (their records gathered through an index list built from the block table)
 constexpr int kPagedBf16 = 0, kSparseFp8 = 1, kPagedFp8 = 2;
 
-template <int MODE, bool SHARED>
+// D: width of a cached row, 576 (512 latent + 64 RoPE dims) or 512 (the DeepSeek-V4 latent row
+// that is both K and V, bf16 pages only)
+template <int MODE, bool SHARED, int D = kDqk>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_rows_kernel(const AttnArgs a) {
     constexpr bool SPARSE = MODE == kSparseFp8;
     constexpr bool GATHER = MODE != kPagedBf16;     // fp8 records gathered through the index list
-    using C = Cfg<GATHER>;
+    static_assert(D == kDqk || (D == kDv && MODE == kPagedBf16), "512-wide rows: bf16 pages only");
+    constexpr int KS = D / 32;                      // Q.K^T MFMA steps (32 dims each)
+    constexpr int ROWB = D * 2;                     // bytes of a bf16 row in HBM
+    // raw masked scores with the scale in the exponent (576-wide bf16 pages, positive scales);
+    // otherwise the scores are scaled before masking, which takes any scale
+    constexpr bool RAWMAX = !GATHER && D == kDqk;
+    using C = Cfg<GATHER, D>;
     constexpr int PF = kPF;
     constexpr int VPF = kVPF;
     constexpr int DEPTH = C::DEPTH;
@@ -179,7 +187,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * kRec) : 0, 0x00020000);
 
-    bf16x8 qf[18];
+    bf16x8 qf[KS];
     f4 acc[16];
     float m_run, l_run;
     float m_lane;     // largest score this lane has seen in the pass (for a restart's reference)
@@ -188,9 +196,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         const int nch = ceil_div(t1 - t0, kChunk);
         // ---- Q fragments (B operand of S^T): dims 32*ks + 8*g4 .. +7 of this lane's row
         {
-            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (row_ok ? row : 0)) * (kDqk * 2);
+            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (row_ok ? row : 0)) * ROWB;
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
                 if (!row_ok) v = make_uint4(0, 0, 0, 0);
                 qf[ks] = __builtin_bit_cast(bf16x8, v);
@@ -250,7 +258,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             p.base = nullptr;
             if constexpr (!GATHER) {
                 const int page = page_of(cc >> 1);
-                p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRowBytes;
+                p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * ROWB;
             }
             return p;
         };
@@ -258,13 +266,13 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             const int q = wave + kWaves * j;
             if (j < kChunk / kWaves) {   // region A rows
                 const int rr = min(q, p.nrows - 1);
-                copy_s(p.base + rr * kRowBytes, (unsigned)lane << 4, p.dst + q * kRowA16);
+                copy_s(p.base + rr * ROWB, (unsigned)lane << 4, p.dst + q * kRowA16);
             } else {                     // region B: 8 rows of 128 B per copy (parts 0..3, repeated)
                 const int part = (q - kChunk) & 3;
                 const int sl = part * 64 + lane;
                 const int br = sl >> 3;
                 const int rr = min(br, p.nrows - 1);
-                copy(p.base + rr * kRowBytes + (64 + ((sl & 7) ^ swzB(br))) * 16,
+                copy(p.base + rr * ROWB + (64 + ((sl & 7) ^ swzB(br))) * 16,
                      p.dst + kRegionB16 + part * 1024);
             }
         };
@@ -312,8 +320,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < PF - 1; ++i) kf[i] = kfrag(buf, t, i);
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
-                if (ks + PF - 1 < 18) kf[(ks + PF - 1) % PF] = kfrag(buf, t, ks + PF - 1);
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + PF - 1 < KS) kf[(ks + PF - 1) % PF] = kfrag(buf, t, ks + PF - 1);
                 s2[ks & 1] = mfma16(kf[ks % PF], qf[ks], s2[ks & 1]);
                 side(ks);
             }
@@ -342,13 +350,19 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         auto mask_tile = [&](int c, int t, f4 s, Tile& T) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             const int tb = t0 + c * kChunk;
-            if constexpr (!GATHER) {
+            if constexpr (RAWMAX) {
                 // raw scores; a positive scale commutes with the maximum and is applied in the
                 // exponent (the launcher sends other scales to another kernel)
                 const int bnd = min(t1, limit + 1) - tb - 16 * t - 4 * g4;    // valid: i < bnd
 #pragma unroll
                 for (int i = 0; i < 4; ++i) T.s[i] = i < bnd ? s[i] : -INFINITY;
                 T.mx = fmaxf(fmaxf(T.s[0], T.s[1]), fmaxf(T.s[2], T.s[3])) * a.scale_log2;
+            } else if constexpr (!GATHER) {
+                // scaled scores (log2 units), masked
+                const int bnd = min(t1, limit + 1) - tb - 16 * t - 4 * g4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) T.s[i] = i < bnd ? s[i] * a.scale_log2 : -INFINITY;
+                T.mx = fmaxf(fmaxf(T.s[0], T.s[1]), fmaxf(T.s[2], T.s[3]));
             } else {
                 // fp8 pages also apply the row's causal limit: token i of the lane is visible
                 // while i <= lim
@@ -371,7 +385,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (GATHER) p[i] = exp2_fast(T.s[i] - m_use);
+                if constexpr (!RAWMAX) p[i] = exp2_fast(T.s[i] - m_use);
                 else p[i] = exp2_fast(__builtin_fmaf(T.s[i], a.scale_log2, -m_use));
                 l_run += p[i];
                 if constexpr (GATHER) p[i] *= T.tsc[i];
@@ -518,8 +532,16 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         red[wave * 64 + lane] = l_run;
         __syncthreads();
         l_run += red[partner * 64 + lane];
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        if (final_out && a.sinks) {
+            // the head's attention sink joins the denominator (a split row gets it in the combine)
+            const float sk = a.sinks[(row_ok ? row : 0) % a.h_q];
+            const float hi = fmaxf(lse_v, sk), lo = fminf(lse_v, sk);
+            const float tot = lo == -INFINITY ? hi : hi + log1pf(expf(lo - hi));
+            inv *= l_run > 0.f ? expf(lse_v - tot) : 0.f;
+            lse_v = tot;
+        }
         if (row_ok && g4 == 0 && h == 0) {
             if (final_out) a.lse[(size_t)grp * a.M + row] = lse_v;
             else a.part_lse[(size_t)slot * a.M + row] = lse_v;
@@ -590,15 +612,17 @@ hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
     const int R = (a.M + rows::kRowsWg - 1) / rows::kRowsWg;
     const dim3 grid(items * R), block(rows::kWaves * 64);
-#define MLA_ROWS_LAUNCH(MODE_)                                                                                     \
-    if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, true>), grid, block, 0, stream, a);      \
-    else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, false>), grid, block, 0, stream, a);
+#define MLA_ROWS_LAUNCH(MODE_, D_)                                                                                 \
+    if (R > 1) hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, true, D_>), grid, block, 0, stream, a);  \
+    else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, false, D_>), grid, block, 0, stream, a);
     if (sparse) {
-        MLA_ROWS_LAUNCH(rows::kSparseFp8)
+        MLA_ROWS_LAUNCH(rows::kSparseFp8, kDqk)
     } else if (a.kv_fp8) {
-        MLA_ROWS_LAUNCH(rows::kPagedFp8)
+        MLA_ROWS_LAUNCH(rows::kPagedFp8, kDqk)
+    } else if (a.d_qk == kDv) {
+        MLA_ROWS_LAUNCH(rows::kPagedBf16, kDv)
     } else {
-        MLA_ROWS_LAUNCH(rows::kPagedBf16)
+        MLA_ROWS_LAUNCH(rows::kPagedBf16, kDqk)
     }
 #undef MLA_ROWS_LAUNCH
     return hipGetLastError();

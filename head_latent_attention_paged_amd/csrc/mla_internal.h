@@ -58,6 +58,8 @@ struct AttnArgs {
     int split_len;              // sparse entries per split (multiple of kChunk)
     int64_t kv_rows;            // sparse: records in the pool; paged fp8: pages * 64
     int kv_fp8;                 // paged: 1 = 64-token pages of 640-byte fp8 records
+    int d_qk;                   // paged bf16: row width, 576 or 512 (latent row that is K and V)
+    const float* sinks;         // per-head attention sinks [h_q] (natural log), or null
     float scale_log2;           // softmax_scale * log2(e)
 };
 
@@ -71,6 +73,6 @@ hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream
 hipError_t launch_decode_m16_fp8(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
-                          hipStream_t stream);
+                          hipStream_t stream, const float* sinks = nullptr, int h_q = 1);
 
 }  // namespace mla

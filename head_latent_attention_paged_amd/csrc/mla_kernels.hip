@@ -739,7 +739,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ prefix,
                                                           int uniform_splits, int rows,
-                                                          __bf16* __restrict__ out, float* __restrict__ lse) {
+                                                          __bf16* __restrict__ out, float* __restrict__ lse,
+                                                          const float* __restrict__ sinks, int h_q) {
     const int grp = blockIdx.x;
     const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
     const int d4 = threadIdx.x & 127;
@@ -754,11 +755,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
     }
     if (n == 1) return;   // the decode kernel wrote this row directly
     __bf16* orow = out + ((size_t)grp * rows + r) * kDv + d4 * 4;
-    float mu = -INFINITY;
+    // an attention sink is one more term of the denominator, with LSE = the sink and no value
+    const float sk = sinks ? sinks[r % h_q] : -INFINITY;
+    float mu = sk;
     for (int i = 0; i < n; ++i) mu = fmaxf(mu, part_lse[(size_t)(base + i) * rows + r]);
     f4 o = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (mu != -INFINITY) {
+        if (sk != -INFINITY) wsum = expf(sk - mu);
         for (int i = 0; i < n; ++i) {
             const float li = part_lse[(size_t)(base + i) * rows + r];
             const float w = (li == -INFINITY) ? 0.f : expf(li - mu);
@@ -923,6 +927,8 @@ static hipError_t launch_decode_t(const AttnArgs& a, int items, int R, hipStream
 
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const Tiling t = choose_tiling(a.M);
+    // 512-wide rows (K and V): the row-split kernel, whatever the rows and the scale
+    if (!sparse && a.d_qk == kDv) return launch_decode_rows(a, false, stream);
     if (!sparse && a.kv_fp8) {
         // fp8 pages: the 16-row streaming kernel, or the row-split kernel's fp8 gathers
         if (a.M <= 16) return launch_decode_m16_fp8(a, stream);
@@ -950,9 +956,10 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
-                          hipStream_t stream) {
+                          hipStream_t stream, const float* sinks, int h_q) {
     hipLaunchKernelGGL(mla_combine_kernel, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
-                       part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse);
+                       part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
+                       sinks, h_q);
     return hipGetLastError();
 }
 

@@ -127,6 +127,34 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
                               void* out, float* lse, void* stream);
 
 /*
+ * Paged decode in the DeepSeek-V4 main-attention geometry ("[flashinfer]
+ * FlashInfer, NVFP4를 활용한 DeepSeek-V4 디코딩 성능 최적화", README: paged MQA over
+ * one 512-wide latent row per token that is both K and V, 64-token pages,
+ * q_len query tokens per request with the causal mask against the request's
+ * last tokens, an optional per-head attention sink, bf16 output, natural-log
+ * fp32 LSE), here over a bf16 cache.
+ *
+ *   q        [device] bf16 [batch, s_q, h_q, 512]
+ *   kcache   [device] bf16 [num_blocks, 64, 512]; the row is K, and V
+ *   sinks    [device] fp32 [h_q] or NULL: one more logit per head in the
+ *            softmax denominator, carrying no value, in the units of the
+ *            scaled scores (not multiplied by softmax_scale); the returned
+ *            LSE is the log of the whole denominator (a row that sees no
+ *            token gets O = 0, LSE = its sink)
+ *
+ * Metadata, block table, lengths, causal rule, workspace size
+ * (mla_workspace_size) and outputs are as for mla_decode_paged; any finite
+ * softmax_scale (e.g. 512^-0.5).
+ */
+mla_status_t mla_decode_paged_latent512(const void* q, const void* kcache, int64_t num_blocks,
+                                       const int32_t* block_table, int max_blocks,
+                                       const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                       float softmax_scale, int causal, const float* sinks,
+                                       const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* out, float* lse, void* stream);
+
+/*
  * Paged MLA decode over an fp8 cache: the same call as mla_decode_paged with
  * the cache in the fp8 layout of the decode path ("deepseek-ai/FlashMLA"
  * project summary, section 사용 방법 step 3: flash_mla_with_kvcache on the

@@ -48,6 +48,22 @@ def run_paged(env, inp, num_parts=None):
     return to_host(out, lse)
 
 
+def run_paged_v4(env, inp, num_parts=None):
+    """512-wide latent rows (K and V) with optional sinks: mla_decode_paged_latent512."""
+    import torch
+
+    mla, dev = env
+    q = dev_bf16(inp.q, dev)
+    kc = dev_bf16(inp.kcache.reshape(inp.num_pages, 64, 512), dev)
+    bt = dev_i32(inp.block_table, dev)
+    sl = dev_i32(inp.seqlens, dev)
+    sk = None if inp.sinks is None else torch.from_numpy(inp.sinks).to(dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
+    out, lse = mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal, sinks=sk)
+    torch.cuda.synchronize()
+    return to_host(out, lse)
+
+
 def run_paged_fp8(env, inp, num_parts=None):
     import torch
 
@@ -208,6 +224,53 @@ def test_full_size_paged_fp8_sampled(env):
                                     inp.causal, batches=sample)
     err, rmse = _sampled(o, l, o_ref, l_ref, sample, "config 6")
     _say("config 6 sampled max err", err, "rmse", rmse)
+
+
+# ----------------------------------------------------------------- V4 geometry: 512-wide rows, sinks
+V4_CASES = [
+    # batch, s_q, h_q, seqlens, causal, sinks, num_parts
+    (2, 6, 64, [300, 70], True, True, None),
+    (2, 6, 64, [300, 70], True, False, None),
+    (3, 1, 16, [1, 64, 65], False, True, None),
+    (3, 2, 32, [500, 0, 3], True, True, 3),
+    (1, 6, 64, [2000], True, True, 16),
+    (1, 6, 128, [700], True, True, None),
+    (4, 6, 8, [5, 6, 7, 129], True, True, 2),
+]
+
+
+@pytest.mark.parametrize("case", V4_CASES, ids=[str(i) for i in range(len(V4_CASES))])
+def test_paged_v4_geometry_cases(env, case):
+    batch, s_q, h_q, L, causal, sinks, P = case
+    _say("paged v4 case", case)
+    inp = make_paged(batch, s_q, h_q, L, causal, seed=600 + sum(L) + h_q, poison=True, d_qk=512, sinks=sinks)
+    o, l = run_paged_v4(env, inp, P)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal,
+                                sinks=inp.sinks)
+    check_parity(o, l, o_ref, l_ref, "v4 " + str(case))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.5])
+def test_paged_v4_softmax_scales(env, scale):
+    _say("paged v4 scale", scale)
+    inp = make_paged(2, 6, 64, [900, 300], True, seed=650, poison=True, softmax_scale=scale, d_qk=512,
+                     sinks=True)
+    o, l = run_paged_v4(env, inp)
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, True,
+                                sinks=inp.sinks)
+    check_parity(o, l, o_ref, l_ref, "v4 scale %g" % scale)
+
+
+def test_full_size_v4_geometry_sampled(env):
+    _say("full-size V4 geometry")
+    inp = make_config(7, poison=False)
+    o, l = run_paged_v4(env, inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    sample = sorted(np.random.default_rng(7).choice(inp.batch, size=4, replace=False).tolist())
+    o_ref, l_ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale,
+                                inp.causal, batches=sample, sinks=inp.sinks)
+    err, rmse = _sampled(o, l, o_ref, l_ref, sample, "config 7")
+    _say("config 7 sampled max err", err, "rmse", rmse)
 
 
 # ----------------------------------------------------------------- sparse
