@@ -238,6 +238,127 @@ def make_paged_fp8(batch: int, s_q: int, h_q: int,
 
 
 # --------------------------------------------------------------------------
+# FP4 (E2M1) paged inputs, DeepSeek-V4 geometry
+# --------------------------------------------------------------------------
+FP4_ROW_BYTES = 256     # 512 E2M1 codes, two per byte (low nibble = even element)
+FP4_SCALE_BYTES = 32    # one UE4M3 scale byte per block of 16 values
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def quantize_rows_nvfp4(x: np.ndarray):
+    """Block-16 FP4 quantisation of 512-wide rows: (codes [N, 256] uint8, scales [N, 32] uint8).
+
+    Per block of 16 values: scale = amax / 6 cast to E4M3 (torch ``float8_e4m3fn``, nearest-even;
+    always non-negative, so it is a UE4M3 byte); each value divided by the cast scale is
+    clamped to +-6 and replaced by the nearest E2M1 magnitude (ties to the smaller one) with
+    its sign; an all-zero block gets scale 0 and zero codes.  Element 2j goes to the low
+    nibble of byte j, element 2j+1 to the high nibble.
+    """
+    import torch  # local import: only the fp8/fp4 generators need torch's e4m3 cast
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n, d = x.shape
+    if d % 32:
+        raise ValueError("row width must be a multiple of 32")
+    blk = x.reshape(n, d // 16, 16)
+    amax = np.abs(blk).max(axis=2)
+    sc8 = torch.from_numpy((amax / np.float32(6.0)).astype(np.float32)).to(torch.float8_e4m3fn)
+    scales = sc8.view(torch.uint8).numpy().copy()
+    sval = sc8.to(torch.float32).numpy()
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(sval[:, :, None] > 0, blk / sval[:, :, None], np.float32(0.0))
+    y = np.clip(y, np.float32(-6.0), np.float32(6.0))
+    mag = np.abs(y)
+    idx = np.argmin(np.abs(mag[..., None] - _E2M1_GRID), axis=-1).astype(np.uint8)
+    nib = idx | np.where((y < 0) & (idx > 0), np.uint8(8), np.uint8(0)).astype(np.uint8)
+    nib = nib.reshape(n, d)
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return codes, scales
+
+
+@dataclasses.dataclass
+class PagedFp4Inputs:
+    q: np.ndarray               # uint16 bf16 bits [batch, s_q, h_q, 512]
+    kv_codes: np.ndarray        # uint8 [num_pages, 64, 256] packed E2M1
+    kv_scales: np.ndarray       # uint8 [num_pages, 64, 32] UE4M3 block-16 scales
+    block_table: np.ndarray     # int32 [batch, max_blocks]
+    seqlens: np.ndarray         # int32 [batch]
+    s_q: int
+    h_q: int
+    causal: bool
+    softmax_scale: float        # an fp32 value, stored as a Python float
+    poison_page: int            # index of the poisoned page, or -1
+    sinks: Optional[np.ndarray] = None   # fp32 [h_q], or None
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv_codes.shape[0])
+
+
+def make_paged_fp4(batch: int, s_q: int, h_q: int,
+                   seqlens: Union[Sequence[int], tuple],
+                   causal: bool, seed: int, poison: bool = True,
+                   softmax_scale: Optional[float] = None, sinks: bool = False) -> PagedFp4Inputs:
+    """Draw one DeepSeek-V4-geometry decode input set over an FP4 paged cache.
+
+    Same draws and page permutation as ``make_paged`` with ``d_qk = 512``; the latent rows are
+    drawn in fp32 and quantised by ``quantize_rows_nvfp4`` into the FP4 cache tensors of the
+    V4 decode call ("[flashinfer] ...", README tensor table: ``kv_cache [num_pages, 64, 256]``,
+    ``kv_scale [num_pages, 64, 32]``).  The query stays bf16.  Poisoned rows (unused pages,
+    rows past a sequence's end) hold NaN scale bytes (0x7F), so any read of them shows up.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if isinstance(seqlens, tuple) and len(seqlens) == 3 and seqlens[0] == "uniform":
+        L = rng.integers(int(seqlens[1]), int(seqlens[2]) + 1, size=batch).astype(np.int32)
+    else:
+        L = np.asarray(seqlens, dtype=np.int32)
+        if L.shape != (batch,):
+            raise ValueError("seqlens must have one entry per sequence")
+    if (L < 0).any():
+        raise ValueError("sequence lengths must be >= 0")
+    nblk = (L.astype(np.int64) + PAGE - 1) // PAGE
+    total = int(nblk.sum())
+    max_blocks = max(1, int(nblk.max()) if batch else 1)
+    perm = rng.permutation(total).astype(np.int32)
+    fill = total if poison else 0
+    bt = np.full((batch, max_blocks), fill, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        n = int(nblk[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = _normal_bf16(rng, (batch, s_q, h_q, D_V))
+    n_rows = total * PAGE
+    codes = np.empty((n_rows, FP4_ROW_BYTES), dtype=np.uint8)
+    scales = np.empty((n_rows, FP4_SCALE_BYTES), dtype=np.uint8)
+    for r0 in range(0, n_rows, _KV_CHUNK_ROWS):
+        r1 = min(n_rows, r0 + _KV_CHUNK_ROWS)
+        codes[r0:r1], scales[r0:r1] = quantize_rows_nvfp4(rng.standard_normal((r1 - r0, D_V), dtype=np.float32))
+    codes = codes.reshape(total, PAGE, FP4_ROW_BYTES)
+    scales = scales.reshape(total, PAGE, FP4_SCALE_BYTES)
+    poison_page = -1
+    if poison:
+        codes = np.concatenate([codes, np.full((1, PAGE, FP4_ROW_BYTES), 0x77, dtype=np.uint8)], axis=0)
+        scales = np.concatenate([scales, np.full((1, PAGE, FP4_SCALE_BYTES), 0x7F, dtype=np.uint8)], axis=0)
+        poison_page = total
+        for b in range(batch):
+            if L[b] % PAGE:
+                scales[bt[b, L[b] // PAGE], L[b] % PAGE:] = 0x7F
+    scale = _fp32(D_V ** -0.5 if softmax_scale is None else softmax_scale)
+    sk = None
+    if sinks:
+        sk = (np.log(max(1.0, float(L.mean()) if batch else 1.0)) +
+              rng.uniform(-2.0, 2.0, size=h_q)).astype(np.float32)
+    return PagedFp4Inputs(q=q, kv_codes=codes, kv_scales=scales, block_table=bt, seqlens=L, s_q=s_q,
+                          h_q=h_q, causal=bool(causal), softmax_scale=scale, poison_page=poison_page,
+                          sinks=sk)
+
+
+# --------------------------------------------------------------------------
 # Sparse fp8 inputs
 # --------------------------------------------------------------------------
 @dataclasses.dataclass
@@ -319,7 +440,7 @@ def make_sparse(batch: int, s_q: int, h_q: int, tokens_per_seq: int, topk: int,
 
 
 # --------------------------------------------------------------------------
-# The five named workloads
+# The named workloads
 # --------------------------------------------------------------------------
 CONFIGS = {
     1: dict(kind="paged", name="tiny paged decode: b=2 s_q=1 h_q=16 L={37,130}",
@@ -339,6 +460,9 @@ CONFIGS = {
     # tokens per request, 64 heads, per-head attention sinks
     7: dict(kind="paged_v4", name="V4-geometry paged decode: b=64 s_q=6 causal h_q=64 L=4096 d=512 + sinks",
             batch=64, s_q=6, h_q=64, seqlens=[4096] * 64, causal=True),
+    # the same geometry over an FP4 cache (E2M1 codes, UE4M3 block-16 scales)
+    8: dict(kind="paged_v4_fp4", name="V4-geometry paged decode, FP4 KV: b=64 s_q=6 causal h_q=64 L=4096 d=512 + sinks",
+            batch=64, s_q=6, h_q=64, seqlens=[4096] * 64, causal=True),
 }
 
 
@@ -347,7 +471,7 @@ def config_info(k: int) -> dict:
 
 
 def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
-    """Inputs for workload ``k`` (1..7) with seed 1000 + k unless given."""
+    """Inputs for workload ``k`` (1..8) with seed 1000 + k unless given."""
     c = CONFIGS[k]
     seed = 1000 + k if seed is None else seed
     if c["kind"] == "paged":
@@ -357,4 +481,7 @@ def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
     if c["kind"] == "paged_v4":
         return make_paged(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison,
                           d_qk=D_V, sinks=True)
+    if c["kind"] == "paged_v4_fp4":
+        return make_paged_fp4(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison,
+                              sinks=True)
     return make_sparse(c["batch"], c["s_q"], c["h_q"], c["tokens_per_seq"], c["topk"], c["p_invalid"], seed)

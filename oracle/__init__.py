@@ -5,6 +5,7 @@ leg use it.  It shares no code with the GPU library.
 """
 
 from .mla_oracle import (  # noqa: F401
-    E4M3_TABLE, attend, bf16_to_f64, e4m3_value, gather_paged_records, gather_paged_rows,
-    lse_combine, paged_decode, paged_decode_fp8, sparse_decode, sparse_rows_f64, visible_count,
+    E2M1_TABLE, E4M3_TABLE, attend, bf16_to_f64, e2m1_value, e4m3_value, fp4_rows_f64,
+    gather_paged_fp4, gather_paged_records, gather_paged_rows, lse_combine, paged_decode,
+    paged_decode_fp4, paged_decode_fp8, sparse_decode, sparse_rows_f64, visible_count,
 )

@@ -40,6 +40,12 @@ online softmax and no splitting:
   softmax denominator that carries no value.  Reading: the sink is in the units of the scaled
   scores (natural log, not multiplied by softmax_scale), and the returned LSE is the log of the
   whole denominator, sink included; with no visible token O = 0 and LSE = the sink.
+* FP4 KV for that geometry ("[flashinfer] ...", README: E2M1 values two per byte, 256 bytes
+  per 512-wide row, UE4M3 scales for blocks of 16 values, 32 bytes per row; "deepseek-ai/
+  FlashMLA" project summary, "기술적 세부 사항": e2m1 caches).  Readings: element 2j of a row
+  is the low nibble of byte j and element 2j+1 the high nibble; scale byte b covers elements
+  16b..16b+15; a UE4M3 byte is decoded like an E4M3FN byte (its sign bit is never set by a
+  valid cache); there is no further per-tensor scale.  Row value = e2m1 * scale, exactly.
 
 The split-KV combine used by the GPU path is, mathematically, the same
 definition evaluated on a partition of the visible set; ``lse_combine`` states
@@ -88,6 +94,25 @@ def e4m3_value(code: int) -> float:
 
 
 E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e2m1_value(nibble: int) -> float:
+    """Value of one FP4 E2M1 nibble (OCP microscaling FP4): 1 sign, 2 exponent bits (bias 1),
+    1 mantissa bit.  Exponent field 0 is subnormal (m/2); there is no infinity or NaN, so the
+    largest magnitude is 1.5 * 2^2 = 6.
+    """
+    sign = -1.0 if nibble & 0x8 else 1.0
+    e = (nibble >> 1) & 0x3
+    m = nibble & 0x1
+    if e == 0:
+        return sign * m / 2.0
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+E2M1_TABLE = np.array([e2m1_value(n) for n in range(16)], dtype=np.float64)
+FP4_ROW_BYTES = 256      # 512 E2M1 codes, two per byte
+FP4_SCALE_BYTES = 32     # one UE4M3 scale per 16 values
+FP4_BLOCK = 16
 
 
 def sparse_rows_f64(kv_records: np.ndarray, rows: np.ndarray) -> np.ndarray:
@@ -204,6 +229,58 @@ def paged_decode_fp8(q_bits: np.ndarray, kcache_records: np.ndarray, block_table
         for s in range(s_q):
             n = visible_count(L, s_q, s, causal)
             O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows[:n], sigma)
+    return O, LSE
+
+
+def fp4_rows_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantise FP4 rows: codes [N, 256] uint8 (two E2M1 values per byte, low nibble first),
+    scales [N, 32] uint8 (UE4M3, one per block of 16 values).  Returns [N, 512] float64 with
+    value = e2m1(code) * scale of its block, exactly.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    n = codes.shape[0]
+    vals = np.empty((n, 2 * codes.shape[1]), dtype=np.float64)
+    vals[:, 0::2] = E2M1_TABLE[codes & 0x0F]
+    vals[:, 1::2] = E2M1_TABLE[codes >> 4]
+    block_scale = E4M3_TABLE[scales]                               # [N, 32]
+    return vals * np.repeat(block_scale, FP4_BLOCK, axis=1)
+
+
+def gather_paged_fp4(kv_codes: np.ndarray, kv_scales: np.ndarray, block_table_row: np.ndarray,
+                     n_tokens: int) -> np.ndarray:
+    """Dequantised 512-wide rows of logical tokens 0..n_tokens-1 of one sequence from an FP4
+    paged cache (codes [pages, 64, 256], scales [pages, 64, 32]), through its block table."""
+    out = np.empty((n_tokens, D_V), dtype=np.float64)
+    for t in range(0, n_tokens, PAGE):
+        page = int(block_table_row[t // PAGE])
+        n = min(PAGE, n_tokens - t)
+        out[t:t + n] = fp4_rows_f64(kv_codes[page, :n], kv_scales[page, :n])
+    return out
+
+
+def paged_decode_fp4(q_bits: np.ndarray, kv_codes: np.ndarray, kv_scales: np.ndarray,
+                     block_table: np.ndarray, seqlens: np.ndarray, softmax_scale: float,
+                     causal: bool, batches: Optional[Iterable[int]] = None,
+                     sinks: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """DeepSeek-V4 decode geometry over an FP4 paged cache ("[flashinfer] ...", README tensor
+    table: ``kv_cache [num_pages, 64, 256]`` packed E2M1 and ``kv_scale [num_pages, 64, 32]``
+    UE4M3): each token's dequantised 512-wide row is both K and V; otherwise the definition of
+    ``paged_decode`` (causal rule, optional per-head sinks).  q_bits [B, s_q, h_q, 512] bf16 bits.
+    Returns O [B, s_q, h_q, 512] and LSE [B, s_q, h_q] in float64 (sequences outside
+    ``batches`` stay NaN).
+    """
+    B, s_q, h_q, _ = q_bits.shape
+    sigma = float(np.float32(softmax_scale))
+    sk = None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
+    O = np.full((B, s_q, h_q, D_V), np.nan)
+    LSE = np.full((B, s_q, h_q), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seqlens[b])
+        rows = gather_paged_fp4(kv_codes, kv_scales, block_table[b], L)
+        for s in range(s_q):
+            n = visible_count(L, s_q, s, causal)
+            O[b, s], LSE[b, s] = attend(bf16_to_f64(q_bits[b, s]), rows[:n], sigma, sk)
     return O, LSE
 
 

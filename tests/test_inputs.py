@@ -72,7 +72,7 @@ def test_sparse_generator_indices():
 
 
 def test_config_table():
-    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7}
+    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7, 8}
     assert CONFIGS[2]["batch"] == 128 and CONFIGS[4]["seqlens"][0] == 65536
     assert CONFIGS[5]["topk"] == 2048
     # the fp8-cache workload is the memory-bound shape over fp8 records
@@ -108,3 +108,21 @@ def test_paged_fp8_generator():
     # in-range records: finite positive scales
     sc = inp.kcache[inp.block_table[1, 0], :, 576:580].copy().view("<f4")
     assert np.all(np.isfinite(sc)) and np.all(sc > 0)
+
+
+def test_paged_fp4_generator():
+    from mla_inputs import make_paged_fp4
+    inp = make_paged_fp4(3, 6, 8, [100, 64, 5], True, seed=5, sinks=True)
+    assert inp.q.shape == (3, 6, 8, 512)
+    assert inp.kv_codes.shape == (5, 64, 256) and inp.kv_scales.shape == (5, 64, 32)
+    assert inp.kv_codes.dtype == np.uint8 and inp.kv_scales.dtype == np.uint8
+    assert inp.poison_page == 4 and inp.block_table[1, 1] == 4
+    assert abs(inp.softmax_scale - float(np.float32(512 ** -0.5))) == 0
+    # rows past a sequence's end and the poison page carry NaN scale bytes; used rows valid ones
+    assert np.all(inp.kv_scales[inp.block_table[0, 1], 100 - 64:] == 0x7F)
+    assert np.all(inp.kv_scales[4] == 0x7F)
+    assert np.all(inp.kv_scales[inp.block_table[1, 0]] < 0x7F)
+    # the same page permutation and query draws as the bf16 512-wide generator
+    plain = make_paged(3, 6, 8, [100, 64, 5], True, seed=5, d_qk=512, sinks=True)
+    assert np.array_equal(plain.block_table, inp.block_table) and np.array_equal(plain.q, inp.q)
+    assert CONFIGS[8]["kind"] == "paged_v4_fp4"

@@ -11,9 +11,10 @@ import numpy as np
 import pytest
 import torch
 
-from mla_inputs import bf16_bits_from_f32, make_paged, make_paged_fp8, make_sparse
-from oracle import (E4M3_TABLE, attend, bf16_to_f64, lse_combine, paged_decode, paged_decode_fp8,
-                    sparse_decode, sparse_rows_f64, visible_count)
+from mla_inputs import (bf16_bits_from_f32, make_paged, make_paged_fp4, make_paged_fp8, make_sparse,
+                        quantize_rows_nvfp4)
+from oracle import (E2M1_TABLE, E4M3_TABLE, attend, bf16_to_f64, fp4_rows_f64, lse_combine, paged_decode,
+                    paged_decode_fp4, paged_decode_fp8, sparse_decode, sparse_rows_f64, visible_count)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SIGMA = float(np.float32(576 ** -0.5))
@@ -420,6 +421,94 @@ def test_sink_is_a_valueless_part_in_the_split_combine():
     o_t, l_t = attend(q, rows, SIGMA)
     oc, lc = lse_combine(np.stack([o_t, np.zeros_like(o_t)]), np.stack([l_t, s]))
     assert np.allclose(o, oc, rtol=0, atol=1e-13) and np.allclose(lse, lc, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- V4 geometry: FP4 (E2M1) KV
+def test_e2m1_golden_values_from_ocp_mx_spec():
+    n = 0
+    with open(os.path.join(GOLDEN, "e2m1_ocp.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            code_s, val_s = line.split()
+            code, val = int(code_s, 16), float(val_s)
+            got = E2M1_TABLE[code]
+            assert got == val and math.copysign(1, got) == math.copysign(1, val), (code, got, val)
+            n += 1
+    assert n == 16
+
+
+def test_every_fp4_value_times_every_ue4m3_scale_is_a_bf16_value():
+    """E2M1 (2 significant bits) times a non-negative E4M3 scale (4 significant bits, 2^-9..448)
+    has at most 6 significant bits and stays in bf16's range: the dequantised FP4 cache is
+    exactly a bf16 cache."""
+    scales = E4M3_TABLE[:0x7F]                       # every finite non-negative E4M3 byte
+    prod = (E2M1_TABLE[:, None] * scales[None, :]).reshape(-1)
+    back = bf16_to_f64(_bf16(prod.astype(np.float32)))
+    assert np.array_equal(back, prod)
+
+
+def test_fp4_row_layout_low_nibble_first_and_block16_scales():
+    """Byte j of a row holds elements 2j (low nibble) and 2j+1 (high nibble); scale byte b
+    multiplies elements 16b..16b+15 (hand-computed values)."""
+    codes = np.zeros((1, 256), dtype=np.uint8)
+    scales = np.full((1, 32), 0x38, dtype=np.uint8)  # 1.0
+    codes[0, 0] = 0x21                               # elements 0, 1: 0.5, 1.0
+    codes[0, 7] = 0xA3                               # elements 14, 15: 1.5, -1.0
+    codes[0, 8] = 0xF7                               # elements 16, 17: 6, -6
+    scales[0, 1] = 0x40                              # block 1 (elements 16..31): 2.0
+    scales[0, 31] = 0x01                             # block 31: 2^-9
+    codes[0, 255] = 0x70                             # elements 510, 511: 0, 6
+    v = fp4_rows_f64(codes, scales)[0]
+    want = np.zeros(512)
+    want[[0, 1, 14, 15, 16, 17, 510, 511]] = [0.5, 1.0, 1.5, -1.0, 12.0, -12.0, 0.0, 6.0 * 2.0 ** -9]
+    assert np.array_equal(v, want)
+
+
+def test_fp4_generator_round_trip_within_the_format_bound():
+    """Independently written quantiser (generator) and decoder (oracle): each value comes back
+    within one block scale (half the widest E2M1 gap, 4 -> 6), with its sign, and the row error
+    is far below the signal; a swapped nibble or a wrong magnitude table breaks both."""
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((300, 512)).astype(np.float32)
+    codes, scales = quantize_rows_nvfp4(x)
+    assert codes.shape == (300, 256) and scales.shape == (300, 32)
+    assert (scales < 0x7F).all()
+    xh = fp4_rows_f64(codes, scales)
+    s = np.repeat(E4M3_TABLE[scales], 16, axis=1)
+    assert (np.abs(xh - x) <= s * (1 + 1e-6)).all()
+    assert ((np.sign(xh) == np.sign(x)) | (xh == 0)).all()
+    rel = np.linalg.norm(xh - x, axis=1) / np.linalg.norm(x, axis=1)
+    assert rel.max() < 0.2 and rel.mean() < 0.12
+
+
+def test_paged_fp4_equals_bf16_latent512_on_the_same_values():
+    """An FP4 paged cache and a bf16 512-wide cache holding the same (dequantised) values,
+    through the same block tables (permuted pages, ragged, causal with s_q = 3, sinks), give
+    the same result."""
+    inp = make_paged_fp4(3, 3, 16, [150, 70, 2], True, seed=62, poison=True, sinks=True)
+    P = inp.num_pages
+    vals = fp4_rows_f64(inp.kv_codes.reshape(-1, 256), inp.kv_scales.reshape(-1, 32))
+    kc = _bf16(vals.astype(np.float32)).reshape(P, 64, 1, 512)
+    ok = np.isfinite(vals)
+    assert np.array_equal(bf16_to_f64(kc).reshape(-1, 512)[ok], vals[ok])
+    Ob, Lb = paged_decode(inp.q, kc, inp.block_table, inp.seqlens, inp.softmax_scale, True, sinks=inp.sinks)
+    Of, Lf = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                              inp.softmax_scale, True, sinks=inp.sinks)
+    assert np.isfinite(Of).all() and np.isfinite(Lf).all()
+    assert np.array_equal(Ob, Of) and np.array_equal(Lb, Lf)
+
+
+def test_paged_fp4_never_reads_poisoned_rows():
+    """NaN-scaled rows in unused block-table slots and past each sequence's end change nothing."""
+    args = (3, 2, 16, [100, 64, 5], True)
+    inp = make_paged_fp4(*args, seed=63, poison=True)
+    clean = make_paged_fp4(*args, seed=63, poison=False)
+    O, LSE = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                              inp.softmax_scale, True)
+    Oc, Lc = paged_decode_fp4(clean.q, clean.kv_codes, clean.kv_scales, clean.block_table, clean.seqlens,
+                              clean.softmax_scale, True)
+    assert np.isfinite(O).all() and np.array_equal(O, Oc) and np.array_equal(LSE, Lc)
 
 
 def test_visible_count():
