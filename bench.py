@@ -31,14 +31,19 @@ D_QK, D_V = 576, 512
 def paged_counts(inp):
     """Algorithmic bytes and flops of one paged decode step.
 
-    Bytes: every visible KV row once per sequence (bf16 1152 B; an fp8 record's 576 codes and
-    its fp32 scale, 580 B; V lies inside K), Q, O (bf16), LSE (fp32), the used block-table
-    entries and the sequence lengths.  Flops: 2 * (576 + 512) per (query row, visible token)."""
+    Bytes: every visible KV row once per sequence (bf16 1152 B, or 1024 B for a 512-wide latent
+    row; an fp8 record's 576 codes and its fp32 scale, 580 B; an FP4 row's 256 code bytes and
+    32 scale bytes, 288 B; V lies inside K), Q, O (bf16), LSE (fp32), the used block-table
+    entries, the sequence lengths and the sinks.  Flops: 2 * (d + 512) per (query row, visible
+    token), d = 576 or 512."""
     L = inp.seqlens.astype(np.int64)
     b, s_q, h_q = inp.batch, inp.s_q, inp.h_q
     M = s_q * h_q
-    d = D_QK if inp.kcache.dtype == np.uint8 else inp.kcache.shape[-1]    # 576, or 512-wide latent rows
-    row_bytes = 580 if inp.kcache.dtype == np.uint8 else d * 2
+    if hasattr(inp, "kv_codes"):             # FP4 pages of 512-wide rows
+        d, row_bytes = D_V, 256 + 32
+    else:
+        d = D_QK if inp.kcache.dtype == np.uint8 else inp.kcache.shape[-1]    # 576, or 512-wide rows
+        row_bytes = 580 if inp.kcache.dtype == np.uint8 else d * 2
     kv = int(L.sum()) * row_bytes
     nblk = int(((L + 63) // 64).sum())
     sinks = 0 if getattr(inp, "sinks", None) is None else h_q * 4
@@ -170,7 +175,10 @@ def setup_paged(torch, mla, inp, dev):
     from tests.helpers import dev_bf16, dev_i32, dev_u8
 
     q = dev_bf16(inp.q, dev)
-    if inp.kcache.dtype == np.uint8:
+    fp4 = hasattr(inp, "kv_codes")
+    if fp4:
+        kc, ks = dev_u8(inp.kv_codes, dev), dev_u8(inp.kv_scales, dev)
+    elif inp.kcache.dtype == np.uint8:
         kc = dev_u8(inp.kcache, dev)
     elif inp.kcache.shape[-1] == D_V:        # 512-wide latent rows (K and V)
         kc = dev_bf16(inp.kcache.reshape(inp.kcache.shape[0], 64, D_V), dev)
@@ -184,12 +192,19 @@ def setup_paged(torch, mla, inp, dev):
     ws = torch.zeros((max(mla.workspace_size(inp.batch, inp.s_q, inp.h_q, P), 256),), dtype=torch.uint8, device=dev)
     meta = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
 
+    def call(m):
+        if fp4:
+            mla.decode_paged_fp4(q, kc, ks, bt, sl, m, inp.softmax_scale, inp.causal, out=out, lse=lse,
+                                 workspace=ws, sinks=sk)
+        else:
+            mla.decode_paged(q, kc, bt, sl, m, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws,
+                             sinks=sk)
+
     def decode():
-        mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws, sinks=sk)
+        call(meta)
 
     def step():
-        m = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
-        mla.decode_paged(q, kc, bt, sl, m, inp.softmax_scale, inp.causal, out=out, lse=lse, workspace=ws, sinks=sk)
+        call(mla.get_metadata(sl, inp.h_q, inp.s_q, P))
 
     return step, decode
 
@@ -260,7 +275,7 @@ def run_calls(k, n):
 
     dev = torch.device("cuda:0")
     inp = make_config(k, poison=False)
-    if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4"):
+    if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4"):
         _, fn = setup_paged(torch, mla, inp, dev)
     else:
         _, fn = setup_sparse(torch, mla, inp, dev)
@@ -348,10 +363,10 @@ def main():
     if args.extra:
         flush = Flusher(torch, dev)
         extra = {}
-        for k in (2, 3, 4, 5, 6, 7):
+        for k in (2, 3, 4, 5, 6, 7, 8):
             print("[bench] workload %d" % k, file=sys.stderr, flush=True)
             ik = inp if k == 2 else make_config(k, poison=False)
-            if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4"):
+            if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4"):
                 _, fn = setup_paged(torch, mla, ik, dev)
                 b_k, f_k = paged_counts(ik)
             else:

@@ -23,7 +23,7 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP
 EXPORTS = (
     "mla_status_string", "mla_num_parts", "mla_get_metadata", "mla_get_metadata_host",
     "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_decode_paged_latent512",
-    "mla_sparse_splits",
+    "mla_decode_paged_fp4", "mla_sparse_splits",
     "mla_workspace_size_sparse", "mla_decode_sparse",
 )
 
@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged_latent512.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp,
                                                vp, vp, i32, vp, sz, vp, vp, vp]
     lib.mla_decode_paged_latent512.restype = i32
+    lib.mla_decode_paged_fp4.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp,
+                                         vp, vp, i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_paged_fp4.restype = i32
     lib.mla_sparse_splits.argtypes = [i32, i32, i32, i32]
     lib.mla_sparse_splits.restype = i32
     lib.mla_workspace_size_sparse.argtypes = [i32, i32, i32, i32, i32]
@@ -220,6 +223,56 @@ def _decode_paged_latent512(q, kcache, block_table, cache_seqlens, metadata, sof
         q.data_ptr(), kcache.data_ptr(), kcache.shape[0], block_table.data_ptr(), block_table.shape[1],
         cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
         None if sinks is None else sinks.data_ptr(),
+        tile_meta.data_ptr(), num_splits.data_ptr(), P,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, lse
+
+
+def decode_paged_fp4(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor,
+                     block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                     metadata: Tuple[torch.Tensor, torch.Tensor],
+                     softmax_scale: float = D_V ** -0.5, causal: bool = False,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     sinks: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """DeepSeek-V4-geometry decode over an FP4 cache (mla_decode_paged_fp4).
+
+    q bf16 [b, s_q, h_q, 512]; kv_codes uint8 [num_blocks, 64, 256] (E2M1, low nibble first);
+    kv_scales uint8 [num_blocks, 64, 32] (UE4M3, one per 16 values); sinks fp32 [h_q] or None.
+    Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q]).
+    """
+    batch, s_q, h_q, d = q.shape
+    if d != D_V:
+        raise ValueError("q must have 512 dims per head")
+    _require(q, "q", torch.bfloat16)
+    _require(kv_codes, "kv_codes", torch.uint8)
+    _require(kv_scales, "kv_scales", torch.uint8)
+    nb = kv_codes.shape[0]
+    if kv_codes.dim() != 3 or tuple(kv_codes.shape[1:]) != (PAGE, 256):
+        raise ValueError("kv_codes must be [num_blocks, 64, 256] uint8")
+    if tuple(kv_scales.shape) != (nb, PAGE, 32):
+        raise ValueError("kv_scales must be [num_blocks, 64, 32] uint8")
+    _require(block_table, "block_table", torch.int32)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
+    if sinks is not None:
+        _require(sinks, "sinks", torch.float32, (h_q,))
+    tile_meta, num_splits = metadata
+    P = tile_meta.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, (batch, s_q, h_q, D_V))
+    _require(lse, "lse", torch.float32, (batch, s_q, h_q))
+    need = workspace_size(batch, s_q, h_q, P)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_paged_fp4", lib.mla_decode_paged_fp4(
+        q.data_ptr(), kv_codes.data_ptr(), kv_scales.data_ptr(), nb, block_table.data_ptr(),
+        block_table.shape[1], cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale),
+        1 if causal else 0, None if sinks is None else sinks.data_ptr(),
         tile_meta.data_ptr(), num_splits.data_ptr(), P,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))

@@ -139,13 +139,15 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
                                       const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
                                       void* workspace, size_t workspace_bytes,
                                       void* out, float* lse, void* stream, bool fp8,
-                                      int d_qk = mla::kDqk, const float* sinks = nullptr) {
+                                      int d_qk = mla::kDqk, const float* sinks = nullptr,
+                                      const void* kv_scale = nullptr, bool fp4 = false) {
     if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0 || max_blocks <= 0 || num_blocks <= 0)
         return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(kcache) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+    if (fp4 && (!kv_scale || !aligned16(kv_scale))) return MLA_ERR_INVALID_ARG;
     if ((long long)s_q * h_q > mla::kMaxRows) return MLA_ERR_UNSUPPORTED;
     if (batch > mla::kMaxBatchMeta) return MLA_ERR_UNSUPPORTED;
     const size_t need = mla_workspace_size(batch, s_q, h_q, num_parts);
@@ -154,6 +156,8 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     const int M = s_q * h_q;
     // fp8 pages with more than 16 rows go through 32-bit buffer offsets
     if (fp8 && M > 16 && num_blocks * mla::kPage * mla::kRec > mla::kRowsSparseMaxPool) return MLA_ERR_UNSUPPORTED;
+    // FP4 pages: the row-split kernel's gathers, 32-bit offsets into the 256-byte code rows
+    if (fp4 && num_blocks * mla::kPage * 256 > mla::kRowsSparseMaxPool) return MLA_ERR_UNSUPPORTED;
 
     const long long slots = (long long)batch + num_parts;
     mla::AttnArgs a{};
@@ -177,6 +181,8 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     a.num_parts = num_parts;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.kv_fp8 = fp8 ? 1 : 0;
+    a.kv_fp4 = fp4 ? 1 : 0;
+    a.kv_scale = kv_scale;
     a.kv_rows = num_blocks * mla::kPage;
     a.d_qk = d_qk;
     a.sinks = sinks;
@@ -209,6 +215,18 @@ mla_status_t mla_decode_paged_latent512(const void* q, const void* kcache, int64
     return decode_paged_impl(q, kcache, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
                              softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
                              workspace_bytes, out, lse, stream, false, mla::kDv, sinks);
+}
+
+mla_status_t mla_decode_paged_fp4(const void* q, const void* kv_codes, const void* kv_scales, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  float softmax_scale, int causal, const float* sinks,
+                                  const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, void* stream) {
+    return decode_paged_impl(q, kv_codes, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                             softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
+                             workspace_bytes, out, lse, stream, false, mla::kDv, sinks, kv_scales, true);
 }
 
 mla_status_t mla_decode_paged_fp8(const void* q, const void* kcache, int64_t num_blocks,

@@ -30,6 +30,13 @@
 // converts the e4m3 codes exactly to bf16 and stores them in the same LDS layout as a paged
 // chunk, so the Q.K^T / P.V core is the paged one; the token scale multiplies the score and the
 // probability before P.V.
+//
+// FP4 pages (DeepSeek-V4 geometry, "[flashinfer] FlashInfer, NVFP4를 활용한 DeepSeek-V4 디코딩
+// 성능 최적화", README tensor table): a token's 512-wide latent row is 256 bytes of E2M1 codes
+// (two per byte, low nibble first) in one tensor and 32 UE4M3 scales, one per 16 values, in
+// another.  The same gather path loads a row's codes (one 16-byte load per lane) and its two
+// scale bytes, and writes e2m1 * scale as bf16 (exact: at most 6 significant bits) into the
+// paged chunk layout.
 #include "mla_device.h"
 
 namespace mla {
@@ -69,7 +76,7 @@ constexpr int kGather = 3;
 constexpr int kOutPitch = 1040;
 constexpr unsigned kNoRecord = 0xFFFFF000u;
 
-template <bool GATHER, int D>
+template <bool GATHER, bool SPARSE, int D>
 struct Cfg {
     // a ring slot holds a bf16 chunk; sparse adds the 32 token scales (32-byte stride)
     static constexpr int BUF = kChunk16 + (GATHER ? kChunk * 32 : 0);
@@ -81,31 +88,42 @@ struct Cfg {
     // eight waves, the last four repeated; 512-wide rows have no region B: 32 x 1 KB
     static constexpr int OPS = D == kDqk ? 5 : 4;
     static constexpr int RING = DEPTH * BUF;
-    static constexpr int IDX = GATHER ? kMaxSparseSplit * 4 : 0;        // a segment's index list
-    static constexpr int PAGES = GATHER ? 0 : kWaves * 64 * 4;            // per-wave page windows
+    static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;        // a split's index list
+    static constexpr int PAGES = SPARSE ? 0 : kWaves * 64 * 4;            // per-wave page windows
     static constexpr int PX = 2 * kWaves * 64 * 8;                        // exchanged P, by chunk parity
     static constexpr int VOTES = 2 * kWaves * 4;                          // restart votes, by chunk parity
-    static constexpr int LDS = RING + IDX + PAGES + PX + VOTES;
+    static constexpr int USED = RING + IDX + PAGES + PX + VOTES;
+    // the epilogue stages the output through all of LDS
+    static constexpr int LDS = USED > kWaves * 16 * kOutPitch ? USED : kWaves * 16 * kOutPitch;
 };
 
 // kernel modes: bf16 pages (direct copies), sparse fp8 records through an index list, fp8 pages
-// (their records gathered through an index list built from the block table)
-constexpr int kPagedBf16 = 0, kSparseFp8 = 1, kPagedFp8 = 2;
+// (their records gathered through an index list built from the block table), FP4 pages of the
+// 512-wide rows (gathered the same way)
+constexpr int kPagedBf16 = 0, kSparseFp8 = 1, kPagedFp8 = 2, kPagedFp4 = 3;
+// FP4 rows: 256 code bytes (16 granules) and 32 scale bytes per token; a wave's 4 records of a
+// chunk are its 64 lanes' code granules
+constexpr int kFp4RowBytes = 256;
+constexpr int kFp4ScaleShift = 3;     // scale offset = code offset / 8
 
 // D: width of a cached row, 576 (512 latent + 64 RoPE dims) or 512 (the DeepSeek-V4 latent row
-// that is both K and V, bf16 pages only)
+// that is both K and V: bf16 or FP4 pages)
 template <int MODE, bool SHARED, int D = kDqk>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_rows_kernel(const AttnArgs a) {
     constexpr bool SPARSE = MODE == kSparseFp8;
-    constexpr bool GATHER = MODE != kPagedBf16;     // fp8 records gathered through the index list
-    static_assert(D == kDqk || (D == kDv && MODE == kPagedBf16), "512-wide rows: bf16 pages only");
+    constexpr bool GATHER = MODE != kPagedBf16;     // records gathered through the index list
+    constexpr bool FP4 = MODE == kPagedFp4;
+    static_assert(FP4 ? D == kDv : (D == kDqk || (D == kDv && MODE == kPagedBf16)),
+                  "512-wide rows: bf16 or FP4 pages; FP4 pages: 512-wide rows");
+    constexpr int NG = FP4 ? 1 : kGather;            // gather loads per lane per chunk
+    constexpr unsigned REC = FP4 ? kFp4RowBytes : kRec;   // index-list unit: bytes per record
     constexpr int KS = D / 32;                      // Q.K^T MFMA steps (32 dims each)
     constexpr int ROWB = D * 2;                     // bytes of a bf16 row in HBM
     // raw masked scores with the scale in the exponent (576-wide bf16 pages, positive scales);
     // otherwise the scores are scaled before masking, which takes any scale
     constexpr bool RAWMAX = !GATHER && D == kDqk;
-    using C = Cfg<GATHER, D>;
+    using C = Cfg<GATHER, SPARSE, D>;
     constexpr int PF = kPF;
     constexpr int VPF = kVPF;
     constexpr int DEPTH = C::DEPTH;
@@ -168,8 +186,14 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     // ---- sparse gathers: load i of this lane fetches granule g_off/16 of record g_tok/4 of the
     // chunk and stores it at g_dst of the ring slot: codes as 16 bf16 (32 B, the second half at
     // g_dst ^ 16), a scale granule as its raw first dword
-    int g_tok[GATHER ? kGather : 1], g_off[GATHER ? kGather : 1], g_dst[GATHER ? kGather : 1];
-    if constexpr (GATHER) {
+    int g_tok[GATHER ? NG : 1], g_off[GATHER ? NG : 1], g_dst[GATHER ? NG : 1];
+    if constexpr (FP4) {
+        // lane: code granule lane & 15 (dims 32*(lane & 15) .. +31) of record lane >> 4
+        const int tok = 4 * wave + (lane >> 4);
+        g_tok[0] = tok * 4;
+        g_off[0] = (lane & 15) * 16;
+        g_dst[0] = tok * kRowA16 + (lane & 15) * 64;
+    } else if constexpr (GATHER) {
 #pragma unroll
         for (int i = 0; i < kGather; ++i) {
             int sl = 64 * i + lane;
@@ -183,9 +207,12 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                                   : kRegionB16 + tok * 128 + (((2 * (gran - 32)) ^ swzB(tok)) << 4);
         }
     }
-    // sparse record pool as a raw buffer (offsets past its end read zeros)
+    // gathered records as a raw buffer (offsets past its end read zeros); FP4 scales as another
     const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * kRec) : 0, 0x00020000);
+        const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * REC) : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t pool_sc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.kv_scale), (short)0, FP4 ? (int)(unsigned)(a.kv_rows * (kFp4RowBytes >> kFp4ScaleShift)) : 0,
+        0x00020000);
 
     bf16x8 qf[KS];
     f4 acc[16];
@@ -207,21 +234,13 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         m_run = -INFINITY;
         const int limit = a.causal ? (L - a.s_q + row / a.h_q) : (L - 1);
 
-        // sparse: the split's index list goes to LDS once, as record byte offsets (kNoRecord for
-        // unused entries and up to the end of the last chunk); fp8 pages: the record offsets of
-        // the segment's tokens through the block table
-        if constexpr (GATHER) {
+        // sparse: the split's index list (at most kMaxSparseSplit entries) goes to LDS once, as
+        // record byte offsets (kNoRecord for unused entries and up to the end of the last chunk)
+        if constexpr (SPARSE) {
             for (int e = threadIdx.x; e < nch * kChunk; e += kWaves * 64) {
                 long long v = -1;
-                if (e < t1 - t0) {
-                    if constexpr (SPARSE) {
-                        v = a.indices[(size_t)grp * a.topk + t0 + e];
-                    } else {
-                        const int t = t0 + e;
-                        v = (long long)a.block_table[(size_t)grp * a.max_blocks + (t >> 6)] * kPage + (t & 63);
-                    }
-                }
-                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)((unsigned)v * kRec) : (int)kNoRecord;
+                if (e < t1 - t0) v = a.indices[(size_t)grp * a.topk + t0 + e];
+                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)((unsigned)v * REC) : (int)kNoRecord;
             }
             __syncthreads();
         }
@@ -280,16 +299,68 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // ---- sparse: load i of chunk c into registers; conversion of those registers into chunk
         // c's ring slot.  Chunks past the segment's end gather its last chunk again (unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 gv[GATHER ? kGather : 1];
-        unsigned g_rec[GATHER ? kGather : 1];
+        u32x4 gv[GATHER ? NG : 1];
+        unsigned g_rec[GATHER ? NG : 1];
+        unsigned short g_sc = 0;      // FP4: the two scale bytes of this lane's 32 values
+        // paged gathers of the current chunk (wave-uniform): record of its first token, and how
+        // many of its tokens are read (0 for a page outside the cache)
+        unsigned gp_rec0 = 0;
+        int gp_n = 0;
         auto gather = [&](int c, int i) {
             const int cc = min(c, nch - 1);
-            const unsigned rec = *reinterpret_cast<const unsigned*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
+            unsigned rec;
+            if constexpr (SPARSE) {
+                rec = *reinterpret_cast<const unsigned*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
+            } else {
+                // paged records: a chunk lies inside one page (segments start on a page); tokens
+                // past the segment's end read nothing.  Gather 0 of a chunk comes first.
+                if (i == 0) {
+                    const int tb = t0 + cc * kChunk;
+                    const int pg = page_of(cc >> 1);
+                    const bool pg_ok = pg >= 0 && (long long)pg * kPage < a.kv_rows;
+                    gp_rec0 = (unsigned)pg * kPage + (tb & 63);
+                    gp_n = pg_ok ? min(kChunk, t1 - tb) : 0;
+                }
+                const int lt = g_tok[i] >> 2;
+                rec = lt < gp_n ? (gp_rec0 + lt) * REC : kNoRecord;
+            }
             g_rec[i] = rec;
             gv[i] = __builtin_amdgcn_raw_buffer_load_b128(pool, rec + (unsigned)g_off[i], 0, SHARED ? 0 : 2);
+            // (kNoRecord >> 3 also lies past the end of the scales)
+            if constexpr (FP4)
+                g_sc = __builtin_amdgcn_raw_buffer_load_b16(pool_sc, (rec >> kFp4ScaleShift) + ((unsigned)g_off[i] >> 3),
+                                                            0, SHARED ? 0 : 2);
         };
         auto convert = [&](int c, int i) {
             char* slot = ring + (c % DEPTH) * C::BUF;
+            if constexpr (FP4) {
+                // codes bytes 0..7: block 2*(lane & 15), bytes 8..15: the next block
+                const u32x4 r = gv[i];
+                const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)g_sc, 0);
+                const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)g_sc, 1);
+                unsigned o[16];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float sc = w < 2 ? s0 : s1;
+                    // with a unit scale the conversion is exact; the block scale multiplies in
+                    // fp32, exactly, and the product is a bf16 value
+#define MLA_FP4_PAIR(B_)                                                            \
+    {                                                                               \
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r[w], 1.0f, B_);    \
+        o[4 * w + B_] = pack_bf16x2(v[0] * sc, v[1] * sc);                          \
+    }
+                    MLA_FP4_PAIR(0) MLA_FP4_PAIR(1) MLA_FP4_PAIR(2) MLA_FP4_PAIR(3)
+#undef MLA_FP4_PAIR
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    *reinterpret_cast<uint4*>(slot + g_dst[i] + 16 * k) = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+                // token validity: 1 for a record, NaN for an unused entry (masked off)
+                if ((lane & 15) == 0)
+                    *reinterpret_cast<unsigned*>(slot + kChunk16 + (g_tok[i] >> 2) * 32) =
+                        g_rec[i] >= kNoRecord ? 0x7fc00000u : 0x3f800000u;
+                return;
+            }
             const u32x4 r = gv[i];
             uint4 lo = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.x, r.y));
             const uint4 hi = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.z, r.w));
@@ -373,8 +444,12 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                     // NaN marks an unused entry or a position past the list
                     const float sc = *reinterpret_cast<const float*>(buf + kChunk16 + tok * 32);
                     const bool valid = (sc == sc) & (i <= lim);
-                    T.tsc[i] = valid ? sc : 0.f;
-                    T.s[i] = valid ? s[i] * (a.scale_log2 * sc) : -INFINITY;
+                    if constexpr (FP4) {
+                        T.s[i] = valid ? s[i] * a.scale_log2 : -INFINITY;
+                    } else {
+                        T.tsc[i] = valid ? sc : 0.f;
+                        T.s[i] = valid ? s[i] * (a.scale_log2 * sc) : -INFINITY;
+                    }
                 }
                 T.mx = fmaxf(fmaxf(T.s[0], T.s[1]), fmaxf(T.s[2], T.s[3]));
             }
@@ -388,7 +463,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 if constexpr (!RAWMAX) p[i] = exp2_fast(T.s[i] - m_use);
                 else p[i] = exp2_fast(__builtin_fmaf(T.s[i], a.scale_log2, -m_use));
                 l_run += p[i];
-                if constexpr (GATHER) p[i] *= T.tsc[i];
+                if constexpr (GATHER && !FP4) p[i] *= T.tsc[i];
             }
             return make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         };
@@ -433,11 +508,11 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 wait_chunk();
             } else {
 #pragma unroll
-                for (int i = 0; i < kGather; ++i) gather(0, i);
+                for (int i = 0; i < NG; ++i) gather(0, i);
 #pragma unroll
-                for (int i = 0; i < kGather; ++i) convert(0, i);
+                for (int i = 0; i < NG; ++i) convert(0, i);
 #pragma unroll
-                for (int i = 0; i < kGather; ++i) gather(1, i);
+                for (int i = 0; i < NG; ++i) gather(1, i);
             }
             // chunk 0: Q.K^T of both tiles (the row's reference needs all 32 tokens; the copies of
             // chunk AHEAD, or the conversion of chunk 1 and the gathers of chunk 2, spread over
@@ -448,7 +523,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 auto side0 = [&](int ks) {
                     if constexpr (!GATHER) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
-                    } else if ((ks & 1) == 0 && ks / 2 < kGather) {
+                    } else if ((ks & 1) == 0 && ks / 2 < NG) {
                         convert(1, ks / 2);
                         gather(2, ks / 2);
                     }
@@ -481,7 +556,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 qk(k, h, s2, [&](int ks) {
                     if constexpr (!GATHER) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
-                    } else if ((ks & 1) == 0 && ks / 2 < kGather) {
+                    } else if ((ks & 1) == 0 && ks / 2 < NG) {
                         convert(k + 1, ks / 2);
                         gather(k + 2, ks / 2);
                     }
@@ -617,6 +692,8 @@ hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream
     else hipLaunchKernelGGL((rows::mla_decode_rows_kernel<MODE_, false, D_>), grid, block, 0, stream, a);
     if (sparse) {
         MLA_ROWS_LAUNCH(rows::kSparseFp8, kDqk)
+    } else if (a.kv_fp4) {
+        MLA_ROWS_LAUNCH(rows::kPagedFp4, kDv)
     } else if (a.kv_fp8) {
         MLA_ROWS_LAUNCH(rows::kPagedFp8, kDqk)
     } else if (a.d_qk == kDv) {

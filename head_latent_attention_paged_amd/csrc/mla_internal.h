@@ -18,7 +18,7 @@ constexpr int kMaxBatchMeta = 16384;
 constexpr int kMaxRows = 4096;       // s_q * h_q limit
 constexpr int kSparseTargetItems = 256;   // work items (one per compute unit) sparse splitting aims for
 constexpr int kMaxSparseSplit = 2048;     // index entries one sparse split may hold
-// largest record pool (bytes) the row-split sparse kernel addresses with 32-bit buffer offsets
+// largest record pool (bytes) the row-split kernel's gathers address with 32-bit buffer offsets
 constexpr long long kRowsSparseMaxPool = 0xF0000000LL;
 
 // Wave pairs (32 query rows each) per workgroup of the large-row decode kernel, used for
@@ -58,6 +58,9 @@ struct AttnArgs {
     int split_len;              // sparse entries per split (multiple of kChunk)
     int64_t kv_rows;            // sparse: records in the pool; paged fp8: pages * 64
     int kv_fp8;                 // paged: 1 = 64-token pages of 640-byte fp8 records
+    int kv_fp4;                 // paged: 1 = 64-token pages of 512-wide FP4 rows (kv: 256 code
+                                // bytes per token, kv_scale: 32 UE4M3 bytes per token)
+    const void* kv_scale;       // FP4 pages: uint8 [blocks, 64, 32]
     int d_qk;                   // paged bf16: row width, 576 or 512 (latent row that is K and V)
     const float* sinks;         // per-head attention sinks [h_q] (natural log), or null
     float scale_log2;           // softmax_scale * log2(e)

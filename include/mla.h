@@ -155,6 +155,33 @@ mla_status_t mla_decode_paged_latent512(const void* q, const void* kcache, int64
                                        void* out, float* lse, void* stream);
 
 /*
+ * The DeepSeek-V4 decode geometry over an FP4 cache ("[flashinfer] FlashInfer,
+ * NVFP4를 활용한 DeepSeek-V4 디코딩 성능 최적화", README tensor table: kv_cache
+ * [num_pages, 64, 256] packed E2M1, kv_scale [num_pages, 64, 32] UE4M3 block-16
+ * scales; "deepseek-ai/FlashMLA" project summary, section 기술적 세부 사항:
+ * e2m1 caches).  The query stays bf16.
+ *
+ *   kv_codes  [device] uint8[num_blocks, 64, 256]: the 512 values of a token's
+ *             latent row as OCP E2M1 nibbles, value 2j in the low nibble of
+ *             byte j and value 2j+1 in the high nibble
+ *   kv_scales [device] uint8[num_blocks, 64, 32]: byte b is the scale of
+ *             values 16b..16b+15, decoded as an E4M3FN byte (valid UE4M3
+ *             scales have the top bit clear).  Value = e2m1 * scale, exactly.
+ *
+ * q, sinks, metadata, block table, lengths, causal rule, workspace size
+ * (mla_workspace_size) and outputs are as for mla_decode_paged_latent512.
+ * Both cache pointers must be 16-byte aligned, and num_blocks * 64 * 256
+ * bytes must be at most 3.75 GiB (MLA_ERR_UNSUPPORTED beyond).
+ */
+mla_status_t mla_decode_paged_fp4(const void* q, const void* kv_codes, const void* kv_scales, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  float softmax_scale, int causal, const float* sinks,
+                                  const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* out, float* lse, void* stream);
+
+/*
  * Paged MLA decode over an fp8 cache: the same call as mla_decode_paged with
  * the cache in the fp8 layout of the decode path ("deepseek-ai/FlashMLA"
  * project summary, section 사용 방법 step 3: flash_mla_with_kvcache on the

@@ -10,9 +10,9 @@ import sys
 import numpy as np
 import pytest
 
-from mla_inputs import make_config, make_paged, make_paged_fp8, make_sparse
+from mla_inputs import make_config, make_paged, make_paged_fp4, make_paged_fp8, make_sparse
 from mla_inputs.gen import bf16_bits_from_f32, bf16_bits_to_f32, quantize_rows_e4m3
-from oracle import paged_decode, paged_decode_fp8, sparse_decode
+from oracle import paged_decode, paged_decode_fp4, paged_decode_fp8, sparse_decode
 from tests.helpers import check_parity, dev_bf16, dev_i32, dev_u8, to_host
 
 pytestmark = pytest.mark.gpu
@@ -60,6 +60,23 @@ def run_paged_v4(env, inp, num_parts=None):
     sk = None if inp.sinks is None else torch.from_numpy(inp.sinks).to(dev)
     meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
     out, lse = mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal, sinks=sk)
+    torch.cuda.synchronize()
+    return to_host(out, lse)
+
+
+def run_paged_fp4(env, inp, num_parts=None):
+    """512-wide FP4 rows (codes + UE4M3 block scales) with optional sinks: mla_decode_paged_fp4."""
+    import torch
+
+    mla, dev = env
+    q = dev_bf16(inp.q, dev)
+    codes = dev_u8(inp.kv_codes, dev)
+    scales = dev_u8(inp.kv_scales, dev)
+    bt = dev_i32(inp.block_table, dev)
+    sl = dev_i32(inp.seqlens, dev)
+    sk = None if inp.sinks is None else torch.from_numpy(inp.sinks).to(dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
+    out, lse = mla.decode_paged_fp4(q, codes, scales, bt, sl, meta, inp.softmax_scale, inp.causal, sinks=sk)
     torch.cuda.synchronize()
     return to_host(out, lse)
 
@@ -182,6 +199,9 @@ FP8_PAGED_CASES = [
     (2, 1, 32, [500, 64], False, 3),
     (1, 2, 64, [4000], False, 16),
     (3, 3, 16, [40, 96, 1], True, 3),
+    # one part holding more tokens than a sparse split's index list (many-row gathers)
+    (1, 2, 64, [5000], True, 1),
+    (2, 1, 32, [3000, 2500], False, 2),
 ]
 
 
@@ -236,6 +256,9 @@ V4_CASES = [
     (1, 6, 64, [2000], True, True, 16),
     (1, 6, 128, [700], True, True, None),
     (4, 6, 8, [5, 6, 7, 129], True, True, 2),
+    # long parts (more than 2048 tokens in one workgroup's segment)
+    (1, 6, 64, [5000], True, True, 1),
+    (2, 2, 32, [3000, 2500], True, False, 2),
 ]
 
 
@@ -271,6 +294,60 @@ def test_full_size_v4_geometry_sampled(env):
                                 inp.causal, batches=sample, sinks=inp.sinks)
     err, rmse = _sampled(o, l, o_ref, l_ref, sample, "config 7")
     _say("config 7 sampled max err", err, "rmse", rmse)
+
+
+# ----------------------------------------------------------------- V4 geometry over FP4 pages
+@pytest.mark.parametrize("case", V4_CASES, ids=[str(i) for i in range(len(V4_CASES))])
+def test_paged_fp4_cases(env, case):
+    batch, s_q, h_q, L, causal, sinks, P = case
+    _say("paged fp4 case", case)
+    inp = make_paged_fp4(batch, s_q, h_q, L, causal, seed=700 + sum(L) + h_q, poison=True, sinks=sinks)
+    o, l = run_paged_fp4(env, inp, P)
+    o_ref, l_ref = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                                    inp.softmax_scale, causal, sinks=inp.sinks)
+    check_parity(o, l, o_ref, l_ref, "fp4 " + str(case))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.5])
+def test_paged_fp4_softmax_scales(env, scale):
+    _say("paged fp4 scale", scale)
+    inp = make_paged_fp4(2, 6, 64, [900, 300], True, seed=750, poison=True, softmax_scale=scale, sinks=True)
+    o, l = run_paged_fp4(env, inp)
+    o_ref, l_ref = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                                    inp.softmax_scale, True, sinks=inp.sinks)
+    check_parity(o, l, o_ref, l_ref, "fp4 scale %g" % scale)
+
+
+def test_paged_fp4_every_code_and_scale_byte(env):
+    """Random codes and scale bytes over the whole UE4M3 range (subnormal scales, zero blocks,
+    values up to 6 * 448) with a small softmax scale, so that every conversion path is used."""
+    _say("paged fp4 full code range")
+    inp = make_paged_fp4(2, 6, 64, [700, 200], True, seed=760, poison=True, softmax_scale=2e-4, sinks=True)
+    rng = np.random.default_rng(761)
+    used = np.unique(inp.block_table[inp.block_table != inp.poison_page])
+    inp.kv_codes[used] = rng.integers(0, 256, size=inp.kv_codes[used].shape).astype(np.uint8)
+    inp.kv_scales[used] = rng.integers(0, 0x7F, size=inp.kv_scales[used].shape).astype(np.uint8)
+    for b in range(inp.batch):     # keep the poison past each sequence's end
+        L = int(inp.seqlens[b])
+        if L % 64:
+            inp.kv_scales[inp.block_table[b, L // 64], L % 64:] = 0x7F
+    o, l = run_paged_fp4(env, inp)
+    o_ref, l_ref = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                                    inp.softmax_scale, True, sinks=inp.sinks)
+    assert np.isfinite(o_ref).all()
+    check_parity(o, l, o_ref, l_ref, "fp4 full code range")
+
+
+def test_full_size_v4_fp4_sampled(env):
+    _say("full-size V4 geometry, FP4 pages")
+    inp = make_config(8, poison=False)
+    o, l = run_paged_fp4(env, inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    sample = sorted(np.random.default_rng(8).choice(inp.batch, size=4, replace=False).tolist())
+    o_ref, l_ref = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                                    inp.softmax_scale, inp.causal, batches=sample, sinks=inp.sinks)
+    err, rmse = _sampled(o, l, o_ref, l_ref, sample, "config 8")
+    _say("config 8 sampled max err", err, "rmse", rmse)
 
 
 # ----------------------------------------------------------------- sparse

@@ -106,6 +106,30 @@ def test_paged_latent512_validation_before_launch(mla):
     assert call(kc=24) == mla.MLA_ERR_INVALID_ARG                  # misaligned
 
 
+def test_paged_fp4_validation_before_launch(mla):
+    f = mla.lib.mla_decode_paged_fp4
+    ok = dict(q=16, kc=16, ks=16, nb=4, bt=16, maxb=1, sl=16, batch=1, s_q=6, h_q=64, scale=0.04, causal=1,
+              sinks=None, meta=16, ns=16, P=8, ws=16, wsb=1 << 30, out=16, lse=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["kc"], a["ks"], a["nb"], a["bt"], a["maxb"], a["sl"], a["batch"], a["s_q"],
+                 a["h_q"], a["scale"], a["causal"], a["sinks"], a["meta"], a["ns"], a["P"], a["ws"], a["wsb"],
+                 a["out"], a["lse"], None)
+
+    assert call(q=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(ks=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(ks=20) == mla.MLA_ERR_INVALID_ARG                  # misaligned scales
+    assert call(kc=24) == mla.MLA_ERR_INVALID_ARG                  # misaligned codes
+    assert call(scale=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert call(nb=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
+    assert call(wsb=100) == mla.MLA_ERR_WORKSPACE
+    # codes beyond 3.75 GiB (245761 pages x 16 KiB)
+    assert call(nb=245761) == mla.MLA_ERR_UNSUPPORTED
+
+
 def test_sparse_validation_before_launch(mla):
     f = mla.lib.mla_decode_sparse
     ok = dict(q=16, kv=16, nt=10, idx=16, topk=64, batch=1, s_q=1, h_q=16, scale=0.04, splits=0,
