@@ -331,36 +331,31 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 g_sc = __builtin_amdgcn_raw_buffer_load_b16(pool_sc, (rec >> kFp4ScaleShift) + ((unsigned)g_off[i] >> 3),
                                                             0, SHARED ? 0 : 2);
         };
+        // FP4: quarter w (8 values, dims 32*(lane & 15) + 8w .. +7) of this lane's registers into
+        // chunk c's ring slot.  Code bytes 0..7 belong to block 2*(lane & 15), bytes 8..15 to the
+        // next block.
+        auto convert_fp4 = [&](int c, int w) {
+            char* slot = ring + (c % DEPTH) * C::BUF;
+            const unsigned codes = gv[0][w];
+            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc >> (8 * (w >> 1))), 0);
+            unsigned o[4];
+            // with a unit scale the conversion is exact; the block scale multiplies in fp32,
+            // exactly, and the product is a bf16 value
+#define MLA_FP4_PAIR(B_)                                                              \
+    {                                                                                 \
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B_);     \
+        o[B_] = pack_bf16x2(v[0] * sc, v[1] * sc);                                    \
+    }
+            MLA_FP4_PAIR(0) MLA_FP4_PAIR(1) MLA_FP4_PAIR(2) MLA_FP4_PAIR(3)
+#undef MLA_FP4_PAIR
+            *reinterpret_cast<uint4*>(slot + g_dst[0] + 16 * w) = make_uint4(o[0], o[1], o[2], o[3]);
+            // token validity: 1 for a record, NaN for an unused entry (masked off)
+            if (w == 0 && (lane & 15) == 0)
+                *reinterpret_cast<unsigned*>(slot + kChunk16 + (g_tok[0] >> 2) * 32) =
+                    g_rec[0] >= kNoRecord ? 0x7fc00000u : 0x3f800000u;
+        };
         auto convert = [&](int c, int i) {
             char* slot = ring + (c % DEPTH) * C::BUF;
-            if constexpr (FP4) {
-                // codes bytes 0..7: block 2*(lane & 15), bytes 8..15: the next block
-                const u32x4 r = gv[i];
-                const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)g_sc, 0);
-                const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)g_sc, 1);
-                unsigned o[16];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float sc = w < 2 ? s0 : s1;
-                    // with a unit scale the conversion is exact; the block scale multiplies in
-                    // fp32, exactly, and the product is a bf16 value
-#define MLA_FP4_PAIR(B_)                                                            \
-    {                                                                               \
-        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r[w], 1.0f, B_);    \
-        o[4 * w + B_] = pack_bf16x2(v[0] * sc, v[1] * sc);                          \
-    }
-                    MLA_FP4_PAIR(0) MLA_FP4_PAIR(1) MLA_FP4_PAIR(2) MLA_FP4_PAIR(3)
-#undef MLA_FP4_PAIR
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    *reinterpret_cast<uint4*>(slot + g_dst[i] + 16 * k) = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
-                // token validity: 1 for a record, NaN for an unused entry (masked off)
-                if ((lane & 15) == 0)
-                    *reinterpret_cast<unsigned*>(slot + kChunk16 + (g_tok[i] >> 2) * 32) =
-                        g_rec[i] >= kNoRecord ? 0x7fc00000u : 0x3f800000u;
-                return;
-            }
             const u32x4 r = gv[i];
             uint4 lo = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.x, r.y));
             const uint4 hi = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.z, r.w));
@@ -482,6 +477,17 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             return __builtin_amdgcn_readfirstlane(any) != 0;
         };
         auto no_side = [](int) {};
+        // gathered chunks, during the Q.K^T steps of a chunk: conversion of chunk cn's registers,
+        // then the loads of chunk cn+1 into them (FP4: four conversion quarters, then the load)
+        auto gather_side = [&](int cn, int ks) {
+            if constexpr (FP4) {
+                if ((ks & 1) == 1 && ks < 8) convert_fp4(cn, ks >> 1);
+                if (ks == 8) gather(cn + 1, 0);
+            } else if ((ks & 1) == 0 && ks / 2 < NG) {
+                convert(cn, ks / 2);
+                gather(cn + 1, ks / 2);
+            }
+        };
         // copies are counted exactly (AHEAD-1 later chunks may still be in flight)
         auto wait_chunk = [&]() {
             if constexpr (AHEAD - 1 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -509,8 +515,13 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             } else {
 #pragma unroll
                 for (int i = 0; i < NG; ++i) gather(0, i);
+                if constexpr (FP4) {
 #pragma unroll
-                for (int i = 0; i < NG; ++i) convert(0, i);
+                    for (int w = 0; w < 4; ++w) convert_fp4(0, w);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NG; ++i) convert(0, i);
+                }
 #pragma unroll
                 for (int i = 0; i < NG; ++i) gather(1, i);
             }
@@ -523,9 +534,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 auto side0 = [&](int ks) {
                     if constexpr (!GATHER) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
-                    } else if ((ks & 1) == 0 && ks / 2 < NG) {
-                        convert(1, ks / 2);
-                        gather(2, ks / 2);
+                    } else {
+                        gather_side(1, ks);
                     }
                 };
                 f4 s0[2], s1[2];
@@ -556,9 +566,8 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                 qk(k, h, s2, [&](int ks) {
                     if constexpr (!GATHER) {
                         if ((ks & 1) == 0 && ks / 2 < C::OPS) copy_op(p, ks / 2);
-                    } else if ((ks & 1) == 0 && ks / 2 < NG) {
-                        convert(k + 1, ks / 2);
-                        gather(k + 2, ks / 2);
+                    } else {
+                        gather_side(k + 1, ks);
                     }
                 });
                 // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked and turned into
