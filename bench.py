@@ -224,6 +224,22 @@ def setup_sparse(torch, mla, inp, dev):
     return decode, decode
 
 
+def setup_prefill(torch, mla, inp, dev):
+    """A prompt chunk (batch 1 of the generator) through mla_sparse_prefill."""
+    from tests.helpers import dev_bf16, dev_i32, dev_u8
+
+    q, kv, idx = dev_bf16(inp.q[0], dev), dev_u8(inp.kv, dev), dev_i32(inp.indices[0], dev)
+    out = torch.empty((inp.s_q, inp.h_q, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    ws = torch.zeros((max(mla.workspace_size_sparse(1, inp.s_q, inp.h_q, inp.topk), 256),),
+                     dtype=torch.uint8, device=dev)
+
+    def prefill():
+        mla.sparse_prefill(q, kv, idx, inp.softmax_scale, 0, out=out, lse=lse, workspace=ws)
+
+    return prefill, prefill
+
+
 def cpu_baseline(inp, kind, counts_fn, min_s=10.0, max_s=30.0):
     """The float64 oracle on a bounded sample of the same workload, scaled to GB/s: whole
     sequences (paged) or query tokens (sparse) in order, repeating the workload when one pass
@@ -277,6 +293,8 @@ def run_calls(k, n):
     inp = make_config(k, poison=False)
     if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4"):
         _, fn = setup_paged(torch, mla, inp, dev)
+    elif CONFIGS[k]["kind"] == "sparse_prefill":
+        _, fn = setup_prefill(torch, mla, inp, dev)
     else:
         _, fn = setup_sparse(torch, mla, inp, dev)
     for _ in range(n):
@@ -363,12 +381,15 @@ def main():
     if args.extra:
         flush = Flusher(torch, dev)
         extra = {}
-        for k in (2, 3, 4, 5, 6, 7, 8):
+        for k in (2, 3, 4, 5, 6, 7, 8, 9):
             print("[bench] workload %d" % k, file=sys.stderr, flush=True)
             ik = inp if k == 2 else make_config(k, poison=False)
             if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4"):
                 _, fn = setup_paged(torch, mla, ik, dev)
                 b_k, f_k = paged_counts(ik)
+            elif CONFIGS[k]["kind"] == "sparse_prefill":
+                _, fn = setup_prefill(torch, mla, ik, dev)
+                b_k, f_k = sparse_counts(ik)
             else:
                 _, fn = setup_sparse(torch, mla, ik, dev)
                 b_k, f_k = sparse_counts(ik)

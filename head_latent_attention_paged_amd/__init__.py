@@ -24,7 +24,7 @@ EXPORTS = (
     "mla_status_string", "mla_num_parts", "mla_get_metadata", "mla_get_metadata_host",
     "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_decode_paged_latent512",
     "mla_decode_paged_fp4", "mla_sparse_splits",
-    "mla_workspace_size_sparse", "mla_decode_sparse",
+    "mla_workspace_size_sparse", "mla_decode_sparse", "mla_sparse_prefill",
 )
 
 
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_workspace_size_sparse.restype = sz
     lib.mla_decode_sparse.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.mla_decode_sparse.restype = i32
+    lib.mla_sparse_prefill.argtypes = [vp, vp, i64, vp, i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.mla_sparse_prefill.restype = i32
     return lib
 
 
@@ -318,6 +320,43 @@ def decode_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
     _check("mla_decode_sparse", lib.mla_decode_sparse(
         q.data_ptr(), kv.data_ptr(), kv.shape[0], indices.data_ptr(), topk, batch, s_q, h_q,
+        float(softmax_scale), int(splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, lse
+
+
+def sparse_prefill(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                   softmax_scale: float = D_QK ** -0.5, splits: int = 0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse prefill (mla_sparse_prefill): q bf16 [s_q, h_q, 576], kv uint8 [num_tokens, 640]
+    records, indices int32 [s_q, topk] or [s_q, 1, topk] (-1 = skip).  Returns
+    (out bf16 [s_q, h_q, 512], lse fp32 [s_q, h_q])."""
+    s_q, h_q, d = q.shape
+    if d != D_QK:
+        raise ValueError("q must have 576 dims per head")
+    _require(q, "q", torch.bfloat16)
+    _require(kv, "kv", torch.uint8)
+    if kv.dim() != 2 or kv.shape[1] != SPARSE_REC:
+        raise ValueError("kv must be [num_tokens, 640] uint8 records")
+    _require(indices, "indices", torch.int32)
+    if indices.dim() == 3 and indices.shape[1] == 1:
+        indices = indices[:, 0]
+    if indices.dim() != 2 or indices.shape[0] != s_q or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [s_q, topk] (or [s_q, 1, topk]) tensor")
+    topk = indices.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, (s_q, h_q, D_V))
+    _require(lse, "lse", torch.float32, (s_q, h_q))
+    need = workspace_size_sparse(1, s_q, h_q, topk, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _check("mla_sparse_prefill", lib.mla_sparse_prefill(
+        q.data_ptr(), kv.data_ptr(), kv.shape[0], indices.data_ptr(), topk, s_q, h_q,
         float(softmax_scale), int(splits), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
     return out, lse

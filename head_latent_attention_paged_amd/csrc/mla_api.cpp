@@ -290,6 +290,16 @@ mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens
     return MLA_OK;
 }
 
+mla_status_t mla_sparse_prefill(const void* q, const void* kv, int64_t num_tokens,
+                                const int32_t* indices, int topk, int s_q, int h_q,
+                                float softmax_scale, int splits,
+                                void* workspace, size_t workspace_bytes,
+                                void* out, float* lse, void* stream) {
+    // a prompt chunk is one "sequence" of s_q query tokens, each with its own index list
+    return mla_decode_sparse(q, kv, num_tokens, indices, topk, 1, s_q, h_q, softmax_scale, splits,
+                             workspace, workspace_bytes, out, lse, stream);
+}
+
 }  // extern "C"
 
 namespace mla {

@@ -242,6 +242,31 @@ mla_status_t mla_decode_sparse(const void* q, const void* kv, int64_t num_tokens
                                void* workspace, size_t workspace_bytes,
                                void* out, float* lse, void* stream);
 
+/*
+ * Sparse prefill ("deepseek-ai/FlashMLA" project summary, section "사용 방법"
+ * step 2: flash_mla_sparse_fwd(q, kv, indices, ...) takes the query tensor,
+ * the KV cache and a 3-D indices tensor naming the KV tokens each query token
+ * reads; section "기술적 세부 사항": quantised caches, -1 entries ignored).
+ * Every query token of a prompt chunk attends its own index list over the
+ * same fp8 record pool as mla_decode_sparse; one latent head (h_kv = 1).
+ *
+ *   q        [device] bf16 [s_q, h_q, 576]  (s_q query tokens)
+ *   kv       [device] uint8[num_tokens, 640] records, as for mla_decode_sparse
+ *   indices  [device] int32[s_q, topk] (the [s_q, 1, topk] tensor of one
+ *            latent head), rows in [0, num_tokens) or -1 to skip
+ *   splits, workspace (mla_workspace_size_sparse(1, s_q, h_q, topk, splits))
+ *            as for mla_decode_sparse
+ *   out      [device] bf16 [s_q, h_q, 512]; lse [device] fp32 [s_q, h_q]
+ *
+ * The result is that of mla_decode_sparse with batch = 1 (same kernels: one
+ * work item per query token and 64 heads).  s_q <= 2^24, h_q <= 4096.
+ */
+mla_status_t mla_sparse_prefill(const void* q, const void* kv, int64_t num_tokens,
+                                const int32_t* indices, int topk, int s_q, int h_q,
+                                float softmax_scale, int splits,
+                                void* workspace, size_t workspace_bytes,
+                                void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

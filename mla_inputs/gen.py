@@ -463,6 +463,10 @@ CONFIGS = {
     # the same geometry over an FP4 cache (E2M1 codes, UE4M3 block-16 scales)
     8: dict(kind="paged_v4_fp4", name="V4-geometry paged decode, FP4 KV: b=64 s_q=6 causal h_q=64 L=4096 d=512 + sinks",
             batch=64, s_q=6, h_q=64, seqlens=[4096] * 64, causal=True),
+    # sparse prefill: a 4096-token prompt chunk at the end of a 32768-token context, every query
+    # token with its own 2048-entry index list in its causal window
+    9: dict(kind="sparse_prefill", name="sparse fp8 prefill: s_q=4096 h_q=128 topk=2048 context=32768",
+            batch=1, s_q=4096, h_q=128, tokens_per_seq=32768, topk=2048, p_invalid=0.0),
 }
 
 
@@ -471,7 +475,7 @@ def config_info(k: int) -> dict:
 
 
 def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
-    """Inputs for workload ``k`` (1..8) with seed 1000 + k unless given."""
+    """Inputs for workload ``k`` (1..9) with seed 1000 + k unless given."""
     c = CONFIGS[k]
     seed = 1000 + k if seed is None else seed
     if c["kind"] == "paged":

@@ -567,3 +567,64 @@ def test_full_size_sparse_config_sampled(env):
     bs = tuple(np.array(sets).T)
     err, rmse = check_parity(o[bs], l[bs], o_ref[bs], l_ref[bs], "config 5")
     _say("config 5 sampled max err", err, "rmse", rmse)
+
+
+# ----------------------------------------------------------------- sparse prefill
+def run_prefill(env, inp, splits=0):
+    """A prompt chunk of s_q query tokens (batch 1 of the generator) through mla_sparse_prefill."""
+    import torch
+
+    mla, dev = env
+    assert inp.batch == 1
+    out, lse = mla.sparse_prefill(dev_bf16(inp.q[0], dev), dev_u8(inp.kv, dev), dev_i32(inp.indices[0], dev),
+                                  inp.softmax_scale, splits)
+    torch.cuda.synchronize()
+    return to_host(out, lse)
+
+
+PREFILL_CASES = [
+    # s_q, h_q, context tokens, topk, p_invalid, splits
+    (300, 64, 2048, 512, 0.05, 0),
+    (97, 128, 4096, 2048, 0.0, 0),
+    (64, 16, 1024, 200, 0.1, 0),
+    (40, 32, 1024, 100, 0.0, 0),
+    (33, 64, 3000, 1000, 0.02, 3),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(i) for i in range(len(PREFILL_CASES))])
+def test_sparse_prefill_cases(env, case):
+    s_q, h_q, ctx, topk, p_inv, splits = case
+    _say("sparse prefill case", case)
+    inp = make_sparse(1, s_q, h_q, ctx, topk, p_inv, seed=800 + s_q + h_q)
+    o, l = run_prefill(env, inp, splits)
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+    check_parity(o, l, o_ref[0], l_ref[0], "prefill " + str(case))
+
+
+def test_sparse_prefill_matches_sparse_decode_bitwise(env):
+    """The prefill call over a prompt chunk and the decode call over the same query tokens (as
+    one sequence of s_q tokens) run the same kernels: identical bits."""
+    import torch
+
+    mla, dev = env
+    _say("sparse prefill vs decode")
+    inp = make_sparse(1, 50, 64, 2048, 700, 0.05, seed=850)
+    o, l = run_prefill(env, inp)
+    od, ld = mla.decode_sparse(dev_bf16(inp.q, dev), dev_u8(inp.kv, dev), dev_i32(inp.indices, dev),
+                               inp.softmax_scale)
+    torch.cuda.synchronize()
+    od, ld = to_host(od, ld)
+    assert np.array_equal(o, od[0]) and np.array_equal(l, ld[0])
+
+
+def test_full_size_sparse_prefill_sampled(env):
+    _say("full-size config 9")
+    inp = make_config(9)
+    o, l = run_prefill(env, inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    rng = np.random.default_rng(9)
+    toks = sorted(rng.choice(inp.s_q, size=12, replace=False).tolist())
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale, sets=[(0, t) for t in toks])
+    err, rmse = check_parity(o[toks], l[toks], o_ref[0, toks], l_ref[0, toks], "config 9")
+    _say("config 9 sampled max err", err, "rmse", rmse)

@@ -72,7 +72,8 @@ def test_sparse_generator_indices():
 
 
 def test_config_table():
-    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7, 8}
+    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7, 8, 9}
+    assert CONFIGS[9]["kind"] == "sparse_prefill" and CONFIGS[9]["batch"] == 1
     assert CONFIGS[2]["batch"] == 128 and CONFIGS[4]["seqlens"][0] == 65536
     assert CONFIGS[5]["topk"] == 2048
     # the fp8-cache workload is the memory-bound shape over fp8 records

@@ -150,6 +150,27 @@ def test_sparse_validation_before_launch(mla):
     assert call(h_q=5000) == mla.MLA_ERR_UNSUPPORTED
 
 
+def test_sparse_prefill_validation_before_launch(mla):
+    f = mla.lib.mla_sparse_prefill
+    ok = dict(q=16, kv=16, nt=10, idx=16, topk=64, s_q=100, h_q=64, scale=0.04, splits=0,
+              ws=16, wsb=1 << 30, out=16, lse=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["kv"], a["nt"], a["idx"], a["topk"], a["s_q"], a["h_q"], a["scale"],
+                 a["splits"], a["ws"], a["wsb"], a["out"], a["lse"], None)
+
+    assert call(idx=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(s_q=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(topk=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert call(out=8) == mla.MLA_ERR_INVALID_ARG
+    assert call(splits=4, wsb=10) == mla.MLA_ERR_WORKSPACE
+    assert call(h_q=5000) == mla.MLA_ERR_UNSUPPORTED
+    assert call(s_q=(1 << 24) + 1) == mla.MLA_ERR_UNSUPPORTED
+
+
 def test_metadata_validation(mla):
     assert mla.lib.mla_get_metadata(None, 1, 16, 1, 8, 16, 16, None) == mla.MLA_ERR_INVALID_ARG
     assert mla.lib.mla_get_metadata(16, 0, 16, 1, 8, 16, 16, None) == mla.MLA_ERR_INVALID_ARG
