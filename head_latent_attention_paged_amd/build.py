@@ -26,6 +26,7 @@ SOURCES = {
     "mla_decode_big.hip": VGPR_FORM,
     "mla_decode_rows.hip": [],
     "mla_decode_fp8.hip": VGPR_FORM,
+    "mla_decode_wide.hip": [],
     "mla_api.cpp": [],
 }
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

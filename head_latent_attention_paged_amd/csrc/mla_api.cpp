@@ -72,9 +72,11 @@ int mla_num_parts(int num_cus, int h_q, int s_q) {
     long long rows = (long long)(h_q > 0 ? h_q : 1) * (s_q > 0 ? s_q : 1);
     if (rows > mla::kMaxRows) rows = mla::kMaxRows;
     const Tiling t = mla::choose_tiling((int)rows);
-    // one workgroup per CU; the many-row kernel (one workgroup per CU at a time) does better with
+    // row groups per part: 128-row workgroups of the one-wave-per-SIMD kernel beyond 64 rows
+    const int row_groups = rows > mla::kWideMinRows ? (int)((rows + mla::kWideRows - 1) / mla::kWideRows) : t.row_groups;
+    // one workgroup per CU; the many-row kernels (one workgroup per CU at a time) do better with
     // two rounds of shorter parts, which even out the varying part lengths of ragged batches
-    int p = (rows > 32 ? 2 : 1) * num_cus / t.row_groups;
+    int p = (rows > 32 ? 2 : 1) * num_cus / row_groups;
     if (p >= 8) p -= p % 8;
     return p >= 1 ? p : 1;
 }

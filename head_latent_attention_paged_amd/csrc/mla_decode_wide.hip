@@ -1,0 +1,467 @@
+// gfx950 paged decode kernel for many query rows per KV stream, one wave per SIMD.
+//
+// A workgroup holds 128 query rows in four waves, one per SIMD; each wave owns 32 whole rows.
+// Per 32-token chunk a wave computes S^T[32 tokens x 32 rows] = K Q^T with 32x32x16 MFMAs
+// (tokens on the MFMA M side: "FlashMLA-ETAP: Efficient Transpose Attention Pipeline ...",
+// section 핵심 메커니즘, transposed form), the online softmax of its rows over all 32 tokens, and
+// O^T[512 dims x 32 rows] += V^T P^T.  In the 32x32 accumulator layout a lane holds 16 tokens of
+// one row, so a row's maximum and sum need one lane exchange, and the lane's probabilities are
+// exactly its half of the P^T B operand of the P.V MFMAs (V^T is read in the matching token
+// order with transposing LDS reads).  No probability crosses a wave.  Each K or V^T fragment read
+// from LDS feeds a 32-row MFMA, twice the work per LDS byte of a 16-row tile, and the 512 O^T
+// accumulators of a wave's rows live in the accumulation registers.
+//
+// Chunk loop, iteration k: Q.K^T(k) with the copies of chunk k+2 spread over its MFMAs, then
+// P.V(k-1) with the masking and probabilities of chunk k spread over its MFMAs.  One workgroup
+// barrier per chunk guards the ring of KV chunks, which all four waves fill.
+//
+// Softmax reference: a row's reference is the maximum of its first chunk and never moves inside
+// a pass, so the accumulators are touched only by MFMAs; p = 2^(s - m) <= 2^kRefSlack keeps bf16
+// P and the fp32 sums finite.  A score that outgrows its row's reference by more (or a finite
+// score in a row whose first chunk had none) makes the workgroup run the pass again with each
+// row's maximum over the segment as reference (at most once per segment).
+#include "mla_device.h"
+
+namespace mla {
+
+namespace wide {
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 4;
+constexpr int kRowsWave = 32;
+constexpr int kRowsWg = kWaves * kRowsWave;
+constexpr float kRefSlack = 64.f;
+// LDS chunk layout (measured conflict-free for these read patterns): region A holds dims
+// 0..511 of a row in 1 KB at a 1056-byte row stride; region B the 64 RoPE dims in 128-byte rows,
+// 16-byte granule g at slot g ^ swzB(row)
+constexpr int kRowA16 = 1056;
+constexpr int kRegionB16 = kChunk * kRowA16;
+constexpr int kChunk16 = kRegionB16 + kChunk * 128;
+constexpr int kDepth = 4;            // ring: chunk k-1 (P.V), chunk k (Q.K^T), two in flight
+constexpr int kAhead = 2;
+// output staging: a wave's 32 rows x 1 KB (bf16 O, or half the fp32 partial) at this pitch
+constexpr int kOutPitch = 1040;
+__device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ f16v mfma32(bf16x8 a, bf16x8 b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The S^T chain with its accumulator in VGPRs (the accumulation registers hold all of O^T):
+// the first step starts from zero, later steps accumulate through SrcC back to back.  The
+// compiler does not see these as MFMAs, so s_fence_s waits out the result latency (32x32x16:
+// 16 passes; a VALU read of the result needs 18 wait states) before anything reads S.
+__device__ __forceinline__ void mfma32_v_first(f16v& c, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v(f16v& c, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void s_result_fence(f16v& c) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
+template <int D>
+struct Cfg {
+    static constexpr int OPS = D == kDqk ? 9 : 8;          // 1 KB copies per wave per chunk
+    static constexpr int RING = kDepth * kChunk16;
+    static constexpr int PAGES = kWaves * 64 * 4;          // per-wave page windows
+    static constexpr int VOTES = kWaves * 4;
+    static constexpr int USED = RING + PAGES + VOTES;
+    static constexpr int STAGE = kWaves * kRowsWave * kOutPitch;
+    static constexpr int LDS = USED > STAGE ? USED : STAGE;
+};
+
+// D: width of a cached bf16 row, 576 (512 latent + 64 RoPE dims) or 512 (the DeepSeek-V4 latent
+// row that is both K and V)
+template <bool SHARED, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_wide_kernel(const AttnArgs a) {
+    constexpr int KS = D / 16;                     // Q.K^T MFMA steps (16 dims each)
+    constexpr int ROWB = D * 2;                    // bytes of a row in HBM
+    // raw masked scores with the scale in the exponent (576-wide rows, positive scales);
+    // otherwise scores are scaled before masking, which takes any scale
+    constexpr bool RAWMAX = D == kDqk;
+    using C = Cfg<D>;
+    constexpr int PF = 4;                          // K fragment prefetch distance (MFMA steps)
+    constexpr int VPF = 4;                         // V^T fragment prefetch distance
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    char* ring = smem;
+    int* lpages = reinterpret_cast<int*>(smem + C::RING);
+    int* votes = reinterpret_cast<int*>(smem + C::RING + C::PAGES);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31;         // row of the B / C operands, token of a K read
+    const int g = lane >> 5;           // k half of the operands
+    const int j16 = lane & 15, ih = (lane >> 4) & 1;
+
+    // ---- work item -> (part, row group); row groups of one part share an XCD
+    const int R = ceil_div(a.M, kRowsWg);
+    const int n_items = a.num_parts;
+    int item, rg;
+    {
+        const int bid = blockIdx.x;
+        if ((n_items & 7) == 0) {
+            const int xcd = bid & 7, k = bid >> 3;
+            item = (k / R) * 8 + xcd;
+            rg = k % R;
+        } else {
+            item = bid / R;
+            rg = bid % R;
+        }
+    }
+
+    auto copy_s = [&](const void* sbase, unsigned voff, const void* l) {
+        if constexpr (SHARED) dma16_s_shared(sbase, voff, l);
+        else dma16_s(sbase, voff, l);
+    };
+
+    // ---- LDS fragment offsets that do not depend on the chunk
+    // K (A operand), step ks: token r32, dims 16*ks + 8*g .. +7; in region B (RoPE step m = ks-32)
+    // slot (2m + g) ^ swzB(r32) = ((2m) ^ (swz & 6)) | (g ^ (swz & 1))
+    const int kaddr = r32 * kRowA16 + 16 * g;
+    const int kaddrB = kRegionB16 + r32 * 128 + ((g ^ (swzB(r32) & 1)) << 4);
+    const int kswB = (swzB(r32) & 6) << 4;
+    // V^T (A operand) of dim tile dt and token step s: the 16-lane group (ih, g) reads token rows
+    // 4g + 16s + j16/4 (and +8) at dims 32*dt + 16*ih + 4*(j16 & 3); after the transpose lane
+    // (dim 32*dt + r32, g) holds tokens 4g + 16s + {0..3} and 4g + 16s + 8 + {0..3}
+    const int vaddr = (4 * g + (j16 >> 2)) * kRowA16 + (16 * ih + 4 * (j16 & 3)) * 2;
+    // the value of lane ^ 32 (the other half of a row); the address is built at each use
+    // lane id recomputed where it is needed (no register holds it through the loops)
+    auto lane_now = []() {
+        int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    auto xor32 = [&](float x) {
+        return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_now() ^ 32) << 2, __float_as_int(x)));
+    };
+
+    bf16x8 qf[KS];
+    f16v acc[16];
+    float m_run, l_run, m_lane;
+
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
+        const int nch = ceil_div(t1 - t0, kChunk);
+        // ---- Q fragments (B operand): dims 16*ks + 8*g .. +7 of this lane's row
+        {
+            // per-lane addresses are built where they are used (opaque row), not held through the
+            // chunk loop
+            const int ql = lane_now();
+            const int qrw = rg * kRowsWg + kRowsWave * wave + (ql & 31);
+            const int qr = qrw < a.M ? qrw : 0, qg = ql >> 5;
+            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + qr) * ROWB + qg * 16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 32);
+                if (qrw >= a.M) v = make_uint4(0, 0, 0, 0);
+                qf[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        m_run = -INFINITY;
+        // the lane's tokens are visible below this position (past the segment's end, or the
+        // causal limit of the row), relative to its token offset 4*g in a chunk
+        const int vl = lane_now();
+        const int vrow = rg * kRowsWg + kRowsWave * wave + (vl & 31), vg = vl >> 5;
+        int hq = a.h_q;                    // (the divisor's reciprocal is not held either)
+        asm volatile("" : "+s"(hq));
+        const int vis_end = min(t1, (a.causal ? (L - a.s_q + vrow / hq) : (L - 1)) + 1) - 4 * vg;
+
+        // page numbers of the segment, 64 at a time into a per-wave LDS window
+        int bt_base = -1000000;
+        auto page_of = [&](int p) {
+            int* win = lpages + wave * 64;
+            if (p - bt_base >= 64 || p < bt_base) {
+                bt_base = p;
+                const int np = ceil_div(t1, kPage) - (t0 >> 6);
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int v = (ln < np - p) ? a.block_table[(size_t)grp * a.max_blocks + (t0 >> 6) + p + ln] : 0;
+                win[ln] = v;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            return __builtin_amdgcn_readfirstlane(win[p - bt_base]);
+        };
+
+        // ---- copies of one chunk: 32 rows of region A (1 KB each) and, for 576-wide rows, 4 KB of
+        // region B (8 rows of 128 B per copy), spread over the four waves.  Chunks past the
+        // segment's end re-copy its last chunk into their (unused) slot, so the number of copies
+        // per chunk is fixed and the waits are exact.
+        struct Plan {
+            const char* base;
+            char* dst;
+            int nrows;
+        };
+        auto plan_for = [&](int c) {
+            Plan p;
+            const int cc = min(c, nch - 1);
+            p.dst = ring + (c % kDepth) * kChunk16;
+            const int tb = t0 + cc * kChunk;
+            p.nrows = min(kChunk, t1 - tb);
+            const int page = page_of(cc >> 1);
+            p.base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * ROWB;
+            return p;
+        };
+        auto copy_op = [&](const Plan& p, int j) {
+            if (j < kChunk / kWaves) {        // row wave + 4j of region A
+                const int q = wave + kWaves * j;
+                const int rr = min(q, p.nrows - 1);
+                copy_s(p.base + rr * ROWB, (unsigned)lane << 4, p.dst + q * kRowA16);
+            } else {                          // region B rows 8*wave .. +7
+                const int sl = wave * 64 + lane;
+                const int br = sl >> 3;
+                const int rr = min(br, p.nrows - 1);
+                copy_s(p.base, (unsigned)(rr * ROWB + (64 + ((sl & 7) ^ swzB(br))) * 16),
+                       p.dst + kRegionB16 + wave * 1024);
+            }
+        };
+        auto wait_chunk = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * C::OPS) : "memory"); };
+
+        // ---- LDS fragments
+        auto kfrag = [&](const char* buf, int ks) -> bf16x8 {
+            const int off = ks < 32 ? kaddr + 32 * ks
+                                    : kaddrB + ((32 * (ks - 32)) ^ kswB);
+            return *reinterpret_cast<const bf16x8*>(buf + off);
+        };
+        auto vfrag = [&](const char* buf, int i) -> bf16x8 {     // i = 2 * dt + s
+            const int off = vaddr + 64 * (i >> 1) + 16 * kRowA16 * (i & 1);
+            const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + off));
+            const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + off + 8 * kRowA16));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+
+        // S^T of chunk c for this wave's 32 rows: one accumulation chain (back-to-back MFMAs
+        // accumulate through SrcC); side(ks) runs between the steps
+        auto qk = [&](int c, f16v& sacc, auto&& side) {
+            const char* buf = ring + (c % kDepth) * kChunk16;
+            bf16x8 kf[PF];
+#pragma unroll
+            for (int i = 0; i < PF - 1; ++i) kf[i] = kfrag(buf, i);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + PF - 1 < KS) kf[(ks + PF - 1) % PF] = kfrag(buf, ks + PF - 1);
+                if (ks == 0) mfma32_v_first(sacc, kf[0], qf[0]);
+                else mfma32_v(sacc, kf[ks % PF], qf[ks]);
+                side(ks);
+            }
+            s_result_fence(sacc);
+        };
+        // O^T += V^T P^T over chunk c: token step s (16 tokens) for all 16 dim tiles, s = 0, 1
+        // (the two steps of a tile are 16 MFMAs apart); side(i) runs between the MFMAs
+        auto pv = [&](int c, const bf16x8 (&pb)[2], auto&& side) {
+            const char* buf = ring + (c % kDepth) * kChunk16;
+            bf16x8 vf[VPF];
+            auto vidx = [](int n) { return 2 * (n & 15) + (n >> 4); };     // MFMA n: tile n&15, step n>>4
+#pragma unroll
+            for (int i = 0; i < VPF - 1; ++i) vf[i] = vfrag(buf, vidx(i));
+#pragma unroll
+            for (int n = 0; n < 32; ++n) {
+                if (n + VPF - 1 < 32) vf[(n + VPF - 1) % VPF] = vfrag(buf, vidx(n + VPF - 1));
+                acc[n & 15] = mfma32(vf[n % VPF], pb[n >> 4], acc[n & 15]);
+                side(n);
+            }
+        };
+
+        // ---- masking of chunk c: lane value v is token 8*(v>>2) + 4*g + (v&3) of this lane's row
+        auto mask = [&](int c, f16v& s, float& mx) {
+            const int tb = t0 + c * kChunk;
+            const int bnd = vis_end - tb;                             // valid: 8*(v>>2) + (v&3) < bnd
+            float m = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const bool ok = 8 * (v >> 2) + (v & 3) < bnd;
+                if constexpr (RAWMAX) s[v] = ok ? s[v] : -INFINITY;
+                else s[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
+                m = fmaxf(m, s[v]);
+            }
+            if constexpr (RAWMAX) m *= a.scale_log2;   // a positive scale commutes with the max
+            m = fmaxf(m, xor32(m));
+            mx = m;
+        };
+        // probabilities under the row's reference of token step h2 (lane values 8*h2 .. +7): the
+        // bf16 B operand of that step of P.V
+        auto probs = [&](const f16v& s, int h2) -> bf16x8 {
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = s[8 * h2 + e];
+                if constexpr (RAWMAX) p[e] = exp2_fast(__builtin_fmaf(x, a.scale_log2, -m_use));
+                else p[e] = exp2_fast(x - m_use);
+                l_run += p[e];
+            }
+            const uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+            return __builtin_bit_cast(bf16x8, u);
+        };
+        auto no_side = [](int) {};
+
+        // ---- passes over the segment (a second one only after a restart vote)
+        for (int pass = 0;; ++pass) {
+            l_run = 0.f;
+            m_lane = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc[t] = f16v{};
+            bool outgrown = false;
+            bf16x8 pb[2];
+#pragma unroll
+            for (int c = 0; c < kAhead; ++c) {
+                const Plan p = plan_for(c);
+#pragma unroll
+                for (int j = 0; j < C::OPS; ++j) copy_op(p, j);
+            }
+            wait_chunk();
+            __syncthreads();
+            // chunk 0: Q.K^T with the copies of chunk 2 spread over it, reference, probabilities
+            {
+                const Plan p = plan_for(kAhead);
+                f16v s;
+                qk(0, s, [&](int ks) {
+                    if ((ks & 3) == 1 && ks / 4 < C::OPS) copy_op(p, ks / 4);
+                });
+                float mx;
+                mask(0, s, mx);
+                m_lane = fmaxf(m_lane, mx);
+                if (m_run == -INFINITY) m_run = mx;     // a restart pass keeps its reference
+                pb[0] = probs(s, 0);
+                pb[1] = probs(s, 1);
+            }
+            for (int k = 1; k < nch; ++k) {
+                wait_chunk();
+                // chunk k in LDS for every wave; slot (k-2) % kDepth free
+                __syncthreads();
+                const Plan p = plan_for(k + kAhead);
+                f16v s;
+                qk(k, s, [&](int ks) {
+                    if ((ks & 3) == 1 && ks / 4 < C::OPS) copy_op(p, ks / 4);
+                });
+                // O^T += V^T P^T (k-1) while S^T(k) is masked and turned into probabilities (step
+                // 0's operand once the MFMAs of step 0 are issued, step 1's after the last)
+                float mx = 0.f;
+                pv(k - 1, pb, [&](int n) {
+                    if (n == 3) {
+                        mask(k, s, mx);
+                        m_lane = fmaxf(m_lane, mx);
+                        // also true for a finite score in a row without a reference
+                        outgrown = outgrown | (mx > m_run + kRefSlack);
+                    }
+                    if (n == 16) pb[0] = probs(s, 0);
+                });
+                pb[1] = probs(s, 1);
+            }
+            pv(nch - 1, pb, no_side);
+            // the copies past the segment's end land; every wave's vote visible
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (lane == 0) votes[wave] = __builtin_amdgcn_ballot_w64(outgrown) != 0 ? 1 : 0;
+            __syncthreads();
+            int any = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) any |= votes[w];
+            // (a second pass, whose reference is the segment maximum, cannot vote; the bound on
+            // the passes is a guard)
+            if (__builtin_amdgcn_readfirstlane(any) == 0 || pass == 1) break;
+            // run the pass again with each row's maximum over the segment as reference
+            m_run = fmaxf(m_lane, xor32(m_lane));
+            __syncthreads();               // votes read before the next pass writes them
+        }
+
+        // ---- row sums: the two lanes of a row
+        l_run += xor32(l_run);
+        float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        const int el = lane_now();
+        const int orow = rg * kRowsWg + kRowsWave * wave + (el & 31);
+        if (final_out && a.sinks) {
+            // the head's attention sink joins the denominator (a split row gets it in the combine)
+            int hs = a.h_q;
+            asm volatile("" : "+s"(hs));
+            const float sk = a.sinks[(orow < a.M ? orow : 0) % hs];
+            const float hi = fmaxf(lse_v, sk), lo = fminf(lse_v, sk);
+            const float tot = lo == -INFINITY ? hi : hi + log1pf(expf(lo - hi));
+            inv *= l_run > 0.f ? expf(lse_v - tot) : 0.f;
+            lse_v = tot;
+        }
+        if (orow < a.M && el < 32) {
+            if (final_out) a.lse[(size_t)grp * a.M + orow] = lse_v;
+            else a.part_lse[(size_t)slot * a.M + orow] = lse_v;
+        }
+        // ---- output through LDS: each half of the wave's O (32 rows x 256 dims, fp32 x 1/l) goes
+        // to its own staging area, then out as whole rows: bf16 O, or the fp32 partial.  One
+        // path for both, tile by tile.  Lane value v of dim tile dt is dim 32*dt + 8*(v>>2) +
+        // 4*g + (v&3).
+        char* stg = smem + wave * (kRowsWave * kOutPitch);
+        const int row0 = rg * kRowsWg + kRowsWave * wave;
+        // computed here, not hoisted out of the segment and pass loops, where they would hold
+        // registers through the chunk loop
+        int nrow = a.M - row0;
+        asm volatile("" : "+s"(nrow));
+        const int ln = el, er = el & 31, eg = el >> 5;
+        __syncthreads();                   // the ring is no longer read: LDS is free
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const f16v& o = acc[8 * hf + dt];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f4*>(stg + er * kOutPitch + (32 * dt + 8 * q + 4 * eg) * 4) =
+                        f4{o[4 * q] * inv, o[4 * q + 1] * inv, o[4 * q + 2] * inv, o[4 * q + 3] * inv};
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own staging writes
+            if (final_out) {
+                char* obase = static_cast<char*>(a.out) + ((size_t)grp * a.M + row0) * (kDv * 2) + 512 * hf;
+#pragma unroll 4
+                for (int r = 0; r < kRowsWave; ++r) {
+                    const f4 v = *reinterpret_cast<const f4*>(stg + r * kOutPitch + ln * 16);
+                    if (r < nrow)
+                        *reinterpret_cast<uint2*>(obase + (size_t)r * (kDv * 2) + ln * 8) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            } else {
+                char* pbase = reinterpret_cast<char*>(a.part_o) + ((size_t)slot * a.M + row0) * (kDv * 4) + 1024 * hf;
+#pragma unroll 4
+                for (int r = 0; r < kRowsWave; ++r) {
+                    const f4 v = *reinterpret_cast<const f4*>(stg + r * kOutPitch + ln * 16);
+                    if (r < nrow) *reinterpret_cast<f4*>(pbase + (size_t)r * (kDv * 4) + ln * 16) = v;
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read back before the next half
+        }
+        __syncthreads();                   // LDS free for the next segment
+    };
+
+    const int* meta = a.tile_meta + (size_t)item * kMetaInts;
+    const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
+    for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
+        const int L = a.seqlens[bb];
+        const int nb = ceil_div(L, kPage);
+        const int lo = (bb == b0) ? blk0 : 0;
+        const int hi = (bb == b1) ? blk1 : nb;
+        if (lo >= hi) continue;
+        const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
+        const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
+        run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+    }
+}
+
+}  // namespace wide
+
+hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream) {
+    const int R = (a.M + wide::kRowsWg - 1) / wide::kRowsWg;
+    const dim3 grid(a.num_parts * R), block(wide::kWaves * 64);
+#define MLA_WIDE_LAUNCH(D_)                                                                                \
+    if (R > 1) hipLaunchKernelGGL((wide::mla_decode_wide_kernel<true, D_>), grid, block, 0, stream, a);   \
+    else hipLaunchKernelGGL((wide::mla_decode_wide_kernel<false, D_>), grid, block, 0, stream, a);
+    if (a.d_qk == kDv) {
+        MLA_WIDE_LAUNCH(kDv)
+    } else {
+        MLA_WIDE_LAUNCH(kDqk)
+    }
+#undef MLA_WIDE_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace mla
