@@ -72,11 +72,13 @@ int mla_num_parts(int num_cus, int h_q, int s_q) {
     long long rows = (long long)(h_q > 0 ? h_q : 1) * (s_q > 0 ? s_q : 1);
     if (rows > mla::kMaxRows) rows = mla::kMaxRows;
     const Tiling t = mla::choose_tiling((int)rows);
-    // row groups per part: 128-row workgroups of the one-wave-per-SIMD kernel beyond 64 rows
+    // One workgroup per CU.  16 < rows <= 64 (the row-split kernels): two rounds of shorter
+    // parts, which even out the varying part lengths of ragged batches.  More rows (the
+    // one-wave-per-SIMD kernel's 128-row groups): one round, because every extra split of a
+    // sequence writes and reads back fp32 partials of all its rows (measured on the 256- and
+    // 384-row workloads: one round with fewer splits is 10-20% faster than two).
     const int row_groups = rows > mla::kWideMinRows ? (int)((rows + mla::kWideRows - 1) / mla::kWideRows) : t.row_groups;
-    // one workgroup per CU; the many-row kernels (one workgroup per CU at a time) do better with
-    // two rounds of shorter parts, which even out the varying part lengths of ragged batches
-    int p = (rows > 32 ? 2 : 1) * num_cus / row_groups;
+    int p = (rows > mla::kWideMinRows ? 1 : rows > 32 ? 2 : 1) * num_cus / row_groups;
     if (p >= 8) p -= p % 8;
     return p >= 1 ? p : 1;
 }

@@ -28,14 +28,25 @@ namespace wide {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 
+#ifndef MLA_WIDE_KPF
+#define MLA_WIDE_KPF 4
+#endif
+#ifndef MLA_WIDE_VPF
+#define MLA_WIDE_VPF 4
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kRowsWave = 32;
 constexpr int kRowsWg = kWaves * kRowsWave;
 constexpr float kRefSlack = 64.f;
-// LDS chunk layout (measured conflict-free for these read patterns): region A holds dims
-// 0..511 of a row in 1 KB at a 1056-byte row stride; region B the 64 RoPE dims in 128-byte rows,
-// 16-byte granule g at slot g ^ swzB(row)
-constexpr int kRowA16 = 1056;
+// LDS chunk layout (measured conflict-free on gfx950 for both operand reads): region A holds
+// dims 0..511 of a row in 1 KB at a 1088-byte row stride, its 16-byte granule g at slot
+// g ^ ((row >> 2) & 3): the 32 tokens x 16 B of a K read and the 4 rows x 64 B of a V^T
+// transposing read per half-wave both fall on distinct banks (at a 1056-byte stride, without the
+// XOR, half the LDS cycles of this kernel were bank conflicts).  Region B holds the 64 RoPE dims
+// in 128-byte rows, granule g at slot g ^ swzB(row).
+constexpr int kRowA16 = 1088;
+__device__ __forceinline__ int swzA(int r) { return (r >> 2) & 3; }
 constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 constexpr int kDepth = 4;            // ring: chunk k-1 (P.V), chunk k (Q.K^T), two in flight
@@ -84,8 +95,8 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     // otherwise scores are scaled before masking, which takes any scale
     constexpr bool RAWMAX = D == kDqk;
     using C = Cfg<D>;
-    constexpr int PF = 4;                          // K fragment prefetch distance (MFMA steps)
-    constexpr int VPF = 4;                         // V^T fragment prefetch distance
+    constexpr int PF = MLA_WIDE_KPF;               // K fragment prefetch distance (MFMA steps)
+    constexpr int VPF = MLA_WIDE_VPF;              // V^T fragment prefetch distance
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     char* ring = smem;
     int* lpages = reinterpret_cast<int*>(smem + C::RING);
@@ -119,15 +130,22 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     };
 
     // ---- LDS fragment offsets that do not depend on the chunk
-    // K (A operand), step ks: token r32, dims 16*ks + 8*g .. +7; in region B (RoPE step m = ks-32)
-    // slot (2m + g) ^ swzB(r32) = ((2m) ^ (swz & 6)) | (g ^ (swz & 1))
-    const int kaddr = r32 * kRowA16 + 16 * g;
+    // K (A operand), step ks: token r32, dims 16*ks + 8*g .. +7 = granule 2ks + g.  Region A slot
+    // (2ks + g) ^ swzA: bits 0 and 1 are g ^ swzA.0 and (ks & 1) ^ swzA.1, so even and odd steps
+    // each have one base and a 64-byte step.  Region B (RoPE step m = ks-32): slot
+    // (2m + g) ^ swzB = ((2m) ^ (swzB & 6)) | (g ^ (swzB & 1)).
+    const int kaddrE = r32 * kRowA16 + 16 * ((((swzA(r32) >> 1) & 1) << 1) | (g ^ (swzA(r32) & 1)));
+    const int kaddrO = r32 * kRowA16 + 16 * (((1 ^ ((swzA(r32) >> 1) & 1)) << 1) | (g ^ (swzA(r32) & 1)));
     const int kaddrB = kRegionB16 + r32 * 128 + ((g ^ (swzB(r32) & 1)) << 4);
     const int kswB = (swzB(r32) & 6) << 4;
     // V^T (A operand) of dim tile dt and token step s: the 16-lane group (ih, g) reads token rows
     // 4g + 16s + j16/4 (and +8) at dims 32*dt + 16*ih + 4*(j16 & 3); after the transpose lane
-    // (dim 32*dt + r32, g) holds tokens 4g + 16s + {0..3} and 4g + 16s + 8 + {0..3}
-    const int vaddr = (4 * g + (j16 >> 2)) * kRowA16 + (16 * ih + 4 * (j16 & 3)) * 2;
+    // (dim 32*dt + r32, g) holds tokens 4g + 16s + {0..3} and 4g + 16s + 8 + {0..3}.  Those dims
+    // are granule 4dt + 2ih + (j16&3)/2, byte 8*(j16&1); the rows' swzA is g (and (g+2)&3 for
+    // the rows +8), which only touches the granule's low two bits.
+    const int vgr = 2 * ih + ((j16 & 3) >> 1);
+    const int vaddr1 = (4 * g + (j16 >> 2)) * kRowA16 + ((vgr ^ g) << 4) + (j16 & 1) * 8;
+    const int vaddr2 = (4 * g + (j16 >> 2) + 8) * kRowA16 + ((vgr ^ ((g + 2) & 3)) << 4) + (j16 & 1) * 8;
     // the value of lane ^ 32 (the other half of a row); the address is built at each use
     // lane id recomputed where it is needed (no register holds it through the loops)
     auto lane_now = []() {
@@ -205,10 +223,10 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             return p;
         };
         auto copy_op = [&](const Plan& p, int j) {
-            if (j < kChunk / kWaves) {        // row wave + 4j of region A
+            if (j < kChunk / kWaves) {        // row q = wave + 4j of region A (swzA(q) = j & 3)
                 const int q = wave + kWaves * j;
                 const int rr = min(q, p.nrows - 1);
-                copy_s(p.base + rr * ROWB, (unsigned)lane << 4, p.dst + q * kRowA16);
+                copy_s(p.base + rr * ROWB, (unsigned)(lane ^ (j & 3)) << 4, p.dst + q * kRowA16);
             } else {                          // region B rows 8*wave .. +7
                 const int sl = wave * 64 + lane;
                 const int br = sl >> 3;
@@ -221,14 +239,14 @@ void mla_decode_wide_kernel(const AttnArgs a) {
 
         // ---- LDS fragments
         auto kfrag = [&](const char* buf, int ks) -> bf16x8 {
-            const int off = ks < 32 ? kaddr + 32 * ks
+            const int off = ks < 32 ? ((ks & 1) ? kaddrO : kaddrE) + 64 * (ks >> 1)
                                     : kaddrB + ((32 * (ks - 32)) ^ kswB);
             return *reinterpret_cast<const bf16x8*>(buf + off);
         };
         auto vfrag = [&](const char* buf, int i) -> bf16x8 {     // i = 2 * dt + s
-            const int off = vaddr + 64 * (i >> 1) + 16 * kRowA16 * (i & 1);
-            const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + off));
-            const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + off + 8 * kRowA16));
+            const int off = 64 * (i >> 1) + 16 * kRowA16 * (i & 1);
+            const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr1 + off));
+            const short4v v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vaddr2 + off));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
         };
 

@@ -57,10 +57,11 @@ const char* mla_status_string(mla_status_t status);
 /*
  * Number of KV parts the tile scheduler splits one decode step into: about
  * one workgroup per compute unit once the row groups of a sequence are
- * counted (two when s_q*h_q > 32).  num_cus <= 0 queries the current device.  Returns >= 1, a
- * multiple of 8 when num_cus is (so the part -> XCD mapping is exact).
- * Any value >= 1 is valid for the calls below; larger values force more
- * KV splits.
+ * counted (64-row groups up to 64 rows, 128-row groups beyond), two per
+ * compute unit when 32 < s_q*h_q <= 64.  num_cus <= 0 queries the current
+ * device.  Returns >= 1, a multiple of 8 when num_cus is (so the part -> XCD
+ * mapping is exact).  Any value >= 1 is valid for the calls below; larger
+ * values force more KV splits.
  */
 int mla_num_parts(int num_cus, int h_q, int s_q);
 

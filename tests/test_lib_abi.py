@@ -40,6 +40,10 @@ def test_status_strings(mla):
 def test_num_parts_and_workspace(mla):
     assert mla.num_parts(16, 1, num_cus=256) == 256
     assert mla.num_parts(128, 2, num_cus=256) % 8 == 0
+    # more than 64 rows: one round of 128-row workgroups (256 rows -> 2 groups, 384 -> 3)
+    assert mla.num_parts(128, 2, num_cus=256) == 128
+    assert mla.num_parts(64, 6, num_cus=256) == 80
+    assert mla.num_parts(32, 2, num_cus=256) == 512
     assert mla.num_parts(16, 1, num_cus=3) >= 1
     ws = mla.workspace_size(128, 1, 16, 256)
     assert ws >= (128 + 256) * 16 * 513 * 4
