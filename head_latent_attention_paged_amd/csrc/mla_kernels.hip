@@ -927,10 +927,10 @@ static hipError_t launch_decode_t(const AttnArgs& a, int items, int R, hipStream
 
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const Tiling t = choose_tiling(a.M);
-    // bf16 pages with more than 64 rows: the one-wave-per-SIMD kernel (576-wide rows need a
-    // positive scale, which it applies in the exponent)
-    if (!sparse && !a.kv_fp8 && !a.kv_fp4 && a.M > kWideMinRows && (a.d_qk == kDv || a.scale_log2 > 0.f))
-        return launch_decode_wide(a, stream);
+    // bf16 and FP4 pages with more than 64 rows: the one-wave-per-SIMD kernel (576-wide bf16
+    // rows need a positive scale, which it applies in the exponent)
+    if (!sparse && !a.kv_fp8 && a.M > kWideMinRows && (a.kv_fp4 || a.d_qk == kDv || a.scale_log2 > 0.f))
+        return launch_decode_wide(a, false, stream);
     // 512-wide rows (K and V): the row-split kernel, whatever the rows and the scale
     if (!sparse && a.d_qk == kDv) return launch_decode_rows(a, false, stream);
     if (!sparse && a.kv_fp8) {
