@@ -1,4 +1,5 @@
-// gfx950 paged decode kernel for many query rows per KV stream, one wave per SIMD.
+// gfx950 paged decode kernel for many query rows per KV stream, one wave per SIMD: bf16 pages
+// (576- or 512-wide rows) and FP4 pages of 512-wide rows.
 //
 // A workgroup holds 128 query rows in four waves, one per SIMD; each wave owns 32 whole rows.
 // Per 32-token chunk a wave computes S^T[32 tokens x 32 rows] = K Q^T with 32x32x16 MFMAs
@@ -20,6 +21,11 @@
 // P and the fp32 sums finite.  A score that outgrows its row's reference by more (or a finite
 // score in a row whose first chunk had none) makes the workgroup run the pass again with each
 // row's maximum over the segment as reference (at most once per segment).
+//
+// FP4 pages ("[flashinfer] FlashInfer, NVFP4를 활용한 DeepSeek-V4 디코딩 성능 최적화", README
+// tensor table: E2M1 codes two per byte, UE4M3 scales per 16 values): each wave loads its 8 rows
+// of a chunk one chunk ahead into registers and converts them exactly into the bf16 chunk layout
+// (every E2M1 x UE4M3 product is a bf16 value), so the MFMA core is the bf16 one.
 #include "mla_device.h"
 
 namespace mla {
@@ -51,11 +57,12 @@ constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 constexpr int kNoRecord = 0xFFFFF000u;   // a record offset past every pool: its loads read zeros
 
-// kernel modes: bf16 pages (direct HBM -> LDS copies); sparse fp8 records through an index
-// list; fp8 pages and FP4 pages of the 512-wide rows, their records found through the block
-// table.  The last three gather records into registers one chunk ahead and convert them
-// exactly to bf16 in the same LDS layout, so the MFMA core is the same for all.
-constexpr int kPagedBf16 = 0, kSparseFp8 = 1, kPagedFp8 = 2, kPagedFp4 = 3;
+// kernel modes: bf16 pages (direct HBM -> LDS copies), and FP4 pages of the 512-wide rows, whose
+// rows are gathered into registers one chunk ahead and converted exactly to bf16 in the same
+// LDS layout, so the MFMA core is the same for both.  (fp8 records would need 20 more registers
+// for the records in flight than this kernel has next to 576-wide Q; they use the row-split
+// kernel.)
+constexpr int kPagedBf16 = 0, kPagedFp4 = 3;
 // output staging: a wave's 32 rows x 1 KB (bf16 O, or half the fp32 partial) at this pitch
 constexpr int kOutPitch = 1040;
 __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
@@ -78,7 +85,7 @@ __device__ __forceinline__ void s_result_fence(f16v& c) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
 }
 
-template <bool GATHER, bool SPARSE, int D>
+template <bool GATHER, int D>
 struct Cfg {
     static constexpr int OPS = D == kDqk ? 9 : 8;          // 1 KB copies per wave per chunk
     // a ring slot: a bf16 chunk, and for gathered records their 32 token scales (fp32)
@@ -88,10 +95,9 @@ struct Cfg {
     static constexpr int DEPTH = GATHER ? 3 : 4;
     static constexpr int AHEAD = DEPTH - 2;
     static constexpr int RING = DEPTH * BUF;
-    static constexpr int IDX = SPARSE ? kMaxSparseSplit * 4 : 0;        // a split's index list
-    static constexpr int PAGES = SPARSE ? 0 : kWaves * 64 * 4;          // per-wave page windows
+    static constexpr int PAGES = kWaves * 64 * 4;          // per-wave page windows
     static constexpr int VOTES = kWaves * 4;
-    static constexpr int USED = RING + IDX + PAGES + VOTES;
+    static constexpr int USED = RING + PAGES + VOTES;
     static constexpr int STAGE = kWaves * kRowsWave * kOutPitch;
     static constexpr int LDS = USED > STAGE ? USED : STAGE;
 };
@@ -101,31 +107,26 @@ struct Cfg {
 template <int MODE, bool SHARED, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_wide_kernel(const AttnArgs a) {
-    constexpr bool GATHER = MODE != kPagedBf16;
-    constexpr bool SPARSE = MODE == kSparseFp8;
     constexpr bool FP4 = MODE == kPagedFp4;
-    static_assert(FP4 ? D == kDv : (MODE == kPagedBf16 || D == kDqk), "row width of the mode");
+    constexpr bool GATHER = FP4;
+    static_assert(MODE == kPagedBf16 || (FP4 && D == kDv), "FP4 pages hold 512-wide rows");
     constexpr int KS = D / 16;                     // Q.K^T MFMA steps (16 dims each)
     constexpr int ROWB = D * 2;                    // bytes of a bf16 row in HBM
     // raw masked scores with the scale in the exponent (576-wide bf16 rows, positive scales);
     // otherwise scores are scaled before masking, which takes any scale
     constexpr bool RAWMAX = !GATHER && D == kDqk;
-    using C = Cfg<GATHER, SPARSE, D>;
+    using C = Cfg<GATHER, D>;
     constexpr int DEPTH = C::DEPTH, AHEAD = C::AHEAD;
-    // gathers per lane per chunk (a wave loads 8 records): fp8 records are 37 granules (36 of
-    // codes, one holding the fp32 scale), 296 per wave in 5 loads of 64 lanes (slots 296..319
-    // repeat slots 232..255: the same data to the same place); FP4 rows are 16 granules of codes
-    // (plus 2 scale bytes per lane), 128 per wave in 2 loads
-    constexpr int NG = FP4 ? 2 : 5;
-    constexpr unsigned REC = FP4 ? 256u : (unsigned)kRec;   // bytes per record
-    // K and V^T fragment prefetch distances (MFMA steps); fp8 records hold 20 more registers
-    constexpr int PF = GATHER && !FP4 ? 3 : MLA_WIDE_KPF;
-    constexpr int VPF = GATHER && !FP4 ? 3 : MLA_WIDE_VPF;
+    // FP4 gathers per lane per chunk: a wave loads 8 rows of 16 code granules (plus 2 scale
+    // bytes per granule), 128 granules in 2 loads of 64 lanes
+    constexpr int NG = 2;
+    constexpr unsigned REC = 256u;                 // code bytes per FP4 row
+    constexpr int PF = MLA_WIDE_KPF;               // K fragment prefetch distance (MFMA steps)
+    constexpr int VPF = MLA_WIDE_VPF;              // V^T fragment prefetch distance
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     char* ring = smem;
-    int* lidx = reinterpret_cast<int*>(smem + C::RING);
-    int* lpages = reinterpret_cast<int*>(smem + C::RING + C::IDX);
-    int* votes = reinterpret_cast<int*>(smem + C::RING + C::IDX + C::PAGES);
+    int* lpages = reinterpret_cast<int*>(smem + C::RING);
+    int* votes = reinterpret_cast<int*>(smem + C::RING + C::PAGES);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,7 +136,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
 
     // ---- work item -> (part, row group); row groups of one part share an XCD
     const int R = ceil_div(a.M, kRowsWg);
-    const int n_items = SPARSE ? a.batch * a.num_parts : a.num_parts;
+    const int n_items = a.num_parts;
     int item, rg;
     {
         const int bid = blockIdx.x;
@@ -181,7 +182,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     auto xor32 = [&](float x) {
         return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_now() ^ 32) << 2, __float_as_int(x)));
     };
-    // gathered records as raw buffers (offsets past the end read zeros); FP4 scales as another
+    // FP4 codes and scales as raw buffers (offsets past the end read zeros)
     const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * REC) : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t pool_sc = __builtin_amdgcn_make_buffer_rsrc(
@@ -215,18 +216,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         const int vrow = rg * kRowsWg + kRowsWave * wave + (vl & 31), vg = vl >> 5;
         int hq = a.h_q;                    // (the divisor's reciprocal is not held either)
         asm volatile("" : "+s"(hq));
-        const int vis_end = (SPARSE ? t1 : min(t1, (a.causal ? (L - a.s_q + vrow / hq) : (L - 1)) + 1)) - 4 * vg;
-
-        // sparse: the split's index list goes to LDS once, as record byte offsets (kNoRecord for
-        // unused entries and up to the end of the last chunk)
-        if constexpr (SPARSE) {
-            for (int e = threadIdx.x; e < nch * kChunk; e += kWaves * 64) {
-                long long v = -1;
-                if (e < t1 - t0) v = a.indices[(size_t)grp * a.topk + t0 + e];
-                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)((unsigned)v * REC) : (int)kNoRecord;
-            }
-            __syncthreads();
-        }
+        const int vis_end = min(t1, (a.causal ? (L - a.s_q + vrow / hq) : (L - 1)) + 1) - 4 * vg;
 
         // page numbers of the segment, 64 at a time into a per-wave LDS window
         int bt_base = -1000000;
@@ -278,71 +268,38 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         };
         auto wait_chunk = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"((AHEAD - 1) * C::OPS) : "memory"); };
 
-        // ---- gathered records: load i of chunk c into registers, and its conversion into chunk
-        // c's ring slot.  Load slot sl = 64i + lane is granule gran of record rt of the chunk
-        // (records 8*wave .. 8*wave+7).  Chunks past the segment's end gather its last chunk
-        // again (into an unused slot).
+        // ---- FP4 rows: load i of chunk c into registers, and its conversion into chunk c's ring
+        // slot.  Load slot sl = 64i + lane is code granule gran of row rt of the chunk (rows
+        // 8*wave .. 8*wave+7).  Chunks past the segment's end gather its last chunk again (into
+        // an unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         u32x4 gv[GATHER ? NG : 1];
         unsigned g_bad = 0;       // bit i: load i of this lane reads no record (unused entry)
         unsigned short g_sc[FP4 ? NG : 1];      // FP4: the two scale bytes of the lane's granule
         auto gslot = [&](int i, int& rt, int& gran) {
-            const int ln = lane_now();
-            if constexpr (FP4) {
-                const int sl = 64 * i + ln;
-                rt = 8 * wave + (sl >> 4);
-                gran = sl & 15;
-            } else {
-                int sl = 64 * i + ln;
-                if (sl >= 8 * 37) sl -= 64;
-                const int q = sl / 37;
-                rt = 8 * wave + q;
-                gran = sl - 37 * q;
-            }
+            const int sl = 64 * i + lane_now();
+            rt = 8 * wave + (sl >> 4);
+            gran = sl & 15;
         };
-        unsigned gp_rec0 = 0;     // paged: record of the chunk's first token (wave-uniform)
-        int gp_n = 0;             // paged: tokens of the chunk that are read (0: page outside)
+        unsigned gp_rec0 = 0;     // row of the chunk's first token (wave-uniform)
+        int gp_n = 0;             // tokens of the chunk that are read (0: page outside the cache)
         auto gather = [&](int c, int i) {
             const int cc = min(c, nch - 1);
             int rt, gran;
             gslot(i, rt, gran);
-            unsigned rec;
-            if constexpr (SPARSE) {
-                rec = (unsigned)lidx[cc * kChunk + rt];
-            } else {
-                // a chunk lies inside one page (segments start on a page); gather 0 comes first
-                if (i == 0) {
-                    const int tb = t0 + cc * kChunk;
-                    const int pg = page_of(cc >> 1);
-                    const bool pg_ok = pg >= 0 && (long long)pg * kPage < a.kv_rows;
-                    gp_rec0 = (unsigned)pg * kPage + (tb & 63);
-                    gp_n = pg_ok ? min(kChunk, t1 - tb) : 0;
-                }
-                rec = rt < gp_n ? (gp_rec0 + rt) * REC : kNoRecord;
+            // a chunk lies inside one page (segments start on a page); gather 0 comes first
+            if (i == 0) {
+                const int tb = t0 + cc * kChunk;
+                const int pg = page_of(cc >> 1);
+                const bool pg_ok = pg >= 0 && (long long)pg * kPage < a.kv_rows;
+                gp_rec0 = (unsigned)pg * kPage + (tb & 63);
+                gp_n = pg_ok ? min(kChunk, t1 - tb) : 0;
             }
+            const unsigned rec = rt < gp_n ? (gp_rec0 + rt) * REC : kNoRecord;
             g_bad = (g_bad & ~(1u << i)) | ((rec >= kNoRecord ? 1u : 0u) << i);
             gv[i] = __builtin_amdgcn_raw_buffer_load_b128(pool, rec + (unsigned)gran * 16, 0, SHARED ? 0 : 2);
             // (kNoRecord >> 3 also lies past the end of the scales)
-            if constexpr (FP4)
-                g_sc[i] = __builtin_amdgcn_raw_buffer_load_b16(pool_sc, (rec >> 3) + (unsigned)gran * 2, 0, SHARED ? 0 : 2);
-        };
-        // fp8: 16 codes -> 16 bf16 (exact) at their two granules; the scale granule's first dword
-        // to the token scales (NaN for an unused entry, which the mask turns into -inf)
-        auto convert = [&](int c, int i) {
-            char* slot = ring + (c % DEPTH) * C::BUF;
-            int rt, gran;
-            gslot(i, rt, gran);
-            const u32x4 r = gv[i];
-            if (gran < 36) {
-                uint4 lo, hi;
-                fp8x16_to_bf16(make_uint4(r.x, r.y, r.z, r.w), lo, hi);
-                const int dst = gran < 32 ? rt * kRowA16 + (((2 * gran) ^ swzA(rt)) << 4)
-                                          : kRegionB16 + rt * 128 + (((2 * (gran - 32)) ^ swzB(rt)) << 4);
-                *reinterpret_cast<uint4*>(slot + dst) = lo;
-                *reinterpret_cast<uint4*>(slot + (dst ^ 16)) = hi;
-            } else {
-                *reinterpret_cast<unsigned*>(slot + kChunk16 + rt * 4) = (g_bad >> i) & 1 ? 0x7fc00000u : r.x;
-            }
+            g_sc[i] = __builtin_amdgcn_raw_buffer_load_b16(pool_sc, (rec >> 3) + (unsigned)gran * 2, 0, SHARED ? 0 : 2);
         };
         // FP4: quarter w (8 values: granule 4*gran + w of the bf16 row) of load i; the block scale
         // multiplies in fp32 after an exact unit-scale conversion (the product is a bf16 value);
@@ -370,26 +327,17 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         auto convert_all = [&](int c) {
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
-                if constexpr (FP4) {
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) convert_fp4(c, i, w);
-                } else {
-                    convert(c, i);
-                }
+                for (int w = 0; w < 4; ++w) convert_fp4(c, i, w);
             }
         };
-        // during the Q.K^T steps of a chunk: chunk cn's conversion, then chunk cn+1's loads into the
-        // same registers (FP4: four conversion quarters per load, then the load)
+        // during the Q.K^T steps of a chunk: chunk cn's conversion in four quarters per load, then
+        // chunk cn+1's load into the same registers
         auto gather_side = [&](int cn, int ks) {
-            if constexpr (FP4) {
-                const int i = ks >> 3, st = ks & 7;
-                if (i < NG) {
-                    if ((st & 1) == 1) convert_fp4(cn, i, st >> 1);
-                    if (st == 7) gather(cn + 1, i);
-                }
-            } else if ((ks & 3) == 1 && ks / 4 < NG) {
-                convert(cn, ks / 4);
-                gather(cn + 1, ks / 4);
+            const int i = ks >> 3, st = ks & 7;
+            if (i < NG) {
+                if ((st & 1) == 1) convert_fp4(cn, i, st >> 1);
+                if (st == 7) gather(cn + 1, i);
             }
         };
 
@@ -444,8 +392,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             const int bnd = vis_end - tb;                             // valid: 8*(v>>2) + (v&3) < bnd
             float m = -INFINITY;
             if constexpr (GATHER) {
-                // token scales of the lane's tokens 8q + 4g + (0..3): NaN marks an unused entry;
-                // fp8 scores take the token scale, FP4 values carry their scales already
+                // token entries of the lane's tokens 8q + 4g + (0..3): NaN marks an unused one
                 const char* buf = ring + (c % DEPTH) * C::BUF + kChunk16 + 16 * g;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -454,8 +401,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                     for (int r = 0; r < 4; ++r) {
                         const int v = 4 * q + r;
                         const bool ok = (sc[r] == sc[r]) & (8 * q + r < bnd);
-                        if constexpr (FP4) s[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
-                        else s[v] = ok ? s[v] * (a.scale_log2 * sc[r]) : -INFINITY;
+                        s[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
                         m = fmaxf(m, s[v]);
                     }
                 }
@@ -483,16 +429,6 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                 if constexpr (RAWMAX) p[e] = exp2_fast(__builtin_fmaf(x, a.scale_log2, -m_use));
                 else p[e] = exp2_fast(x - m_use);
                 l_run += p[e];
-            }
-            if constexpr (GATHER && !FP4) {
-                // fp8 values are codes: the token scale multiplies p (0 for an unused entry)
-                const char* buf = ring + (c % DEPTH) * C::BUF + kChunk16 + 16 * g + 64 * h2;
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const f4 sc = *reinterpret_cast<const f4*>(buf + 32 * q);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) p[4 * q + r] *= sc[r] == sc[r] ? sc[r] : 0.f;
-                }
             }
             const uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
@@ -653,7 +589,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         __syncthreads();                   // LDS free for the next segment
     };
 
-    if constexpr (!SPARSE) {
+    {
         const int* meta = a.tile_meta + (size_t)item * kMetaInts;
         const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
         for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
@@ -666,28 +602,18 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
             run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
         }
-    } else {
-        // (query token, split of its index list)
-        const int grp = item / a.num_parts;
-        const int split = item % a.num_parts;
-        const int e0 = split * a.split_len;
-        const int e1 = min(e0 + a.split_len, a.topk);
-        if (e0 < e1) run_segment(grp, e0, e1, 0, a.num_parts == 1, grp * a.num_parts + split);
     }
 }
 
 }  // namespace wide
 
-hipError_t launch_decode_wide(const AttnArgs& a, bool sparse, hipStream_t stream) {
+hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream) {
     const int R = (a.M + wide::kRowsWg - 1) / wide::kRowsWg;
-    const int items = sparse ? a.batch * a.num_parts : a.num_parts;
-    const dim3 grid(items * R), block(wide::kWaves * 64);
+    const dim3 grid(a.num_parts * R), block(wide::kWaves * 64);
 #define MLA_WIDE_LAUNCH(MODE_, D_)                                                                                 \
     if (R > 1) hipLaunchKernelGGL((wide::mla_decode_wide_kernel<MODE_, true, D_>), grid, block, 0, stream, a);    \
     else hipLaunchKernelGGL((wide::mla_decode_wide_kernel<MODE_, false, D_>), grid, block, 0, stream, a);
-    // (fp8 records, sparse or paged, need 20 more registers for the records in flight than this
-    // kernel has next to 576-wide Q: those modes stay with the row-split kernel)
-    if (sparse || a.kv_fp8) return hipErrorInvalidValue;
+    if (a.kv_fp8) return hipErrorInvalidValue;      // (the row-split kernel's mode)
     if (a.kv_fp4) {
         MLA_WIDE_LAUNCH(wide::kPagedFp4, kDv)
     } else if (a.d_qk == kDv) {

@@ -74,7 +74,7 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_big(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_rows(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_m16_fp8(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_decode_wide(const AttnArgs& a, bool sparse, hipStream_t stream);
+hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream);
 // query rows per workgroup of the one-wave-per-SIMD kernel (used above 64 rows)
 constexpr int kWideRows = 128;
 constexpr int kWideMinRows = 64;

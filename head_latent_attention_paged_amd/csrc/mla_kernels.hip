@@ -930,7 +930,7 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     // bf16 and FP4 pages with more than 64 rows: the one-wave-per-SIMD kernel (576-wide bf16
     // rows need a positive scale, which it applies in the exponent)
     if (!sparse && !a.kv_fp8 && a.M > kWideMinRows && (a.kv_fp4 || a.d_qk == kDv || a.scale_log2 > 0.f))
-        return launch_decode_wide(a, false, stream);
+        return launch_decode_wide(a, stream);
     // 512-wide rows (K and V): the row-split kernel, whatever the rows and the scale
     if (!sparse && a.d_qk == kDv) return launch_decode_rows(a, false, stream);
     if (!sparse && a.kv_fp8) {
