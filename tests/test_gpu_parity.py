@@ -147,6 +147,11 @@ PAGED_CASES = [
     (2, 1, 48, [77, 300], False, None),
     (1, 2, 64, [4000], False, 16),
     (5, 1, 32, [33, 31, 32, 1, 97], False, 2),
+    # 128-row workgroups that end mid-group: an idle fourth wave (96 rows), a second group of 2
+    # rows (130), a partly filled wave (200)
+    (2, 3, 32, [300, 77], True, None),
+    (2, 2, 65, [150, 64], True, 3),
+    (1, 5, 40, [700], True, 2),
 ]
 
 
@@ -258,6 +263,10 @@ V4_CASES = [
     (4, 6, 8, [5, 6, 7, 129], True, True, 2),
     # long parts (more than 2048 tokens in one workgroup's segment)
     (1, 6, 64, [5000], True, True, 1),
+    # 128-row workgroups that end mid-group (96, 130 and 200 rows)
+    (2, 3, 32, [300, 77], True, True, None),
+    (2, 2, 65, [150, 64], True, True, None),
+    (1, 5, 40, [700], True, False, 3),
     (2, 2, 32, [3000, 2500], True, False, 2),
 ]
 
@@ -414,6 +423,7 @@ RAMP_CASES = [
     (2, 1, 64, [1500, 700], False, -150.0, None),
     (2, 1, 32, [1200, 333], False, 150.0, 8),
     (1, 2, 128, [2000], True, 120.0, None),
+    (1, 2, 128, [2000], True, -150.0, 4),
     (2, 2, 64, [900, 1300], True, 150.0, 16),
 ]
 
