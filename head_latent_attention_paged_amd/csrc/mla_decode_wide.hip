@@ -269,31 +269,29 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         auto wait_chunk = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"((AHEAD - 1) * C::OPS) : "memory"); };
 
         // ---- FP4 rows: load i of chunk c into registers, and its conversion into chunk c's ring
-        // slot.  Load slot sl = 64i + lane is code granule gran of row rt of the chunk (rows
-        // 8*wave .. 8*wave+7).  Chunks past the segment's end gather its last chunk again (into
-        // an unused slot).
+        // slot.  Load i of lane (r4 = lane >> 4, gran = lane & 15) is code granule gran of row
+        // rt = 8*wave + 4i + r4 of the chunk.  swzA(rt) = (2*wave + i) & 3 is wave-uniform, so the
+        // converted granule 4*gran + w lands at the lane's base cbase plus a wave-uniform offset.
+        // Chunks past the segment's end gather its last chunk again (into an unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         u32x4 gv[GATHER ? NG : 1];
         unsigned g_bad = 0;       // bit i: load i of this lane reads no record (unused entry)
         unsigned short g_sc[FP4 ? NG : 1];      // FP4: the two scale bytes of the lane's granule
-        auto gslot = [&](int i, int& rt, int& gran) {
-            const int sl = 64 * i + lane_now();
-            rt = 8 * wave + (sl >> 4);
-            gran = sl & 15;
-        };
         unsigned gp_rec0 = 0;     // row of the chunk's first token (wave-uniform)
         int gp_n = 0;             // tokens of the chunk that are read (0: page outside the cache)
+        unsigned chunk_ok = 0;    // bit c & 3: chunk c's page lies in the cache (wave-uniform)
         auto gather = [&](int c, int i) {
             const int cc = min(c, nch - 1);
-            int rt, gran;
-            gslot(i, rt, gran);
+            const int ln = lane_now();
+            const int rt = 4 * i + (ln >> 4), gran = ln & 15;    // row within the wave's 8
             // a chunk lies inside one page (segments start on a page); gather 0 comes first
             if (i == 0) {
                 const int tb = t0 + cc * kChunk;
                 const int pg = page_of(cc >> 1);
                 const bool pg_ok = pg >= 0 && (long long)pg * kPage < a.kv_rows;
-                gp_rec0 = (unsigned)pg * kPage + (tb & 63);
-                gp_n = pg_ok ? min(kChunk, t1 - tb) : 0;
+                gp_rec0 = (unsigned)pg * kPage + (tb & 63) + 8 * wave;
+                gp_n = pg_ok ? min(kChunk, t1 - tb) - 8 * wave : 0;
+                chunk_ok = (chunk_ok & ~(1u << (c & 3))) | ((pg_ok ? 1u : 0u) << (c & 3));
             }
             const unsigned rec = rt < gp_n ? (gp_rec0 + rt) * REC : kNoRecord;
             g_bad = (g_bad & ~(1u << i)) | ((rec >= kNoRecord ? 1u : 0u) << i);
@@ -305,9 +303,9 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         // multiplies in fp32 after an exact unit-scale conversion (the product is a bf16 value);
         // the token entry is 1, or NaN for an unused one
         auto convert_fp4 = [&](int c, int i, int w) {
-            char* slot = ring + (c % DEPTH) * C::BUF;
-            int rt, gran;
-            gslot(i, rt, gran);
+            const int ln = lane_now();
+            const int cbase = (ln >> 4) * kRowA16 + (ln & 15) * 64;
+            char* slot = ring + (c % DEPTH) * C::BUF + (8 * wave + 4 * i) * kRowA16 + ((w ^ ((2 * wave + i) & 3)) << 4);
             const unsigned codes = gv[i][w];
             const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc[i] >> (8 * (w >> 1))), 0);
             unsigned o[4];
@@ -318,10 +316,10 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     }
             MLA_FP4_PAIR(0) MLA_FP4_PAIR(1) MLA_FP4_PAIR(2) MLA_FP4_PAIR(3)
 #undef MLA_FP4_PAIR
-            *reinterpret_cast<uint4*>(slot + rt * kRowA16 + (((4 * gran + w) ^ swzA(rt)) << 4)) =
-                make_uint4(o[0], o[1], o[2], o[3]);
-            if (w == 0 && gran == 0)
-                *reinterpret_cast<unsigned*>(slot + kChunk16 + rt * 4) = (g_bad >> i) & 1 ? 0x7fc00000u : 0x3f800000u;
+            *reinterpret_cast<uint4*>(slot + cbase) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (w == 0 && (ln & 15) == 0)
+                *reinterpret_cast<unsigned*>(ring + (c % DEPTH) * C::BUF + kChunk16 + (8 * wave + 4 * i + (ln >> 4)) * 4) =
+                    (g_bad >> i) & 1 ? 0x7fc00000u : 0x3f800000u;
         };
         // all of chunk c's loads (prologue)
         auto convert_all = [&](int c) {
@@ -391,7 +389,15 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             const int tb = t0 + c * kChunk;
             const int bnd = vis_end - tb;                             // valid: 8*(v>>2) + (v&3) < bnd
             float m = -INFINITY;
-            if constexpr (GATHER) {
+            const bool whole = __builtin_amdgcn_ballot_w64(bnd < kChunk - 4) == 0;   // lane's last token: kChunk - 5
+            if (GATHER && whole && ((chunk_ok >> (c & 3)) & 1)) {
+                // every token of the chunk is read and visible to every row of the wave
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    s[v] *= a.scale_log2;
+                    m = fmaxf(m, s[v]);
+                }
+            } else if constexpr (GATHER) {
                 // token entries of the lane's tokens 8q + 4g + (0..3): NaN marks an unused one
                 const char* buf = ring + (c % DEPTH) * C::BUF + kChunk16 + 16 * g;
 #pragma unroll
@@ -405,14 +411,21 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                         m = fmaxf(m, s[v]);
                     }
                 }
+            } else if (whole) {
+                // every token of the chunk is visible to every row of the wave: no mask
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    if constexpr (!RAWMAX) s[v] *= a.scale_log2;
+                    m = fmaxf(m, s[v]);
+                }
             } else {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const bool ok = 8 * (v >> 2) + (v & 3) < bnd;
-                if constexpr (RAWMAX) s[v] = ok ? s[v] : -INFINITY;
-                else s[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
-                m = fmaxf(m, s[v]);
-            }
+                for (int v = 0; v < 16; ++v) {
+                    const bool ok = 8 * (v >> 2) + (v & 3) < bnd;
+                    if constexpr (RAWMAX) s[v] = ok ? s[v] : -INFINITY;
+                    else s[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
+                    m = fmaxf(m, s[v]);
+                }
             }
             if constexpr (RAWMAX) m *= a.scale_log2;   // a positive scale commutes with the max
             m = fmaxf(m, xor32(m));
