@@ -55,13 +55,13 @@ constexpr int kRowA16 = 1088;
 __device__ __forceinline__ int swzA(int r) { return (r >> 2) & 3; }
 constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
-constexpr int kNoRecord = 0xFFFFF000u;   // a record offset past every pool: its loads read zeros
+constexpr unsigned kNoRecord = 0xFFFFF000u;   // a record offset past every pool: its loads read zeros
 
 // kernel modes: bf16 pages (direct HBM -> LDS copies), and FP4 pages of the 512-wide rows, whose
 // rows are gathered into registers one chunk ahead and converted exactly to bf16 in the same
 // LDS layout, so the MFMA core is the same for both.  (fp8 records would need 20 more registers
 // for the records in flight than this kernel has next to 576-wide Q; they use the row-split
-// kernel.)
+// kernel.  The mode numbers are the row-split kernel's.)
 constexpr int kPagedBf16 = 0, kPagedFp4 = 3;
 // output staging: a wave's 32 rows x 1 KB (bf16 O, or half the fp32 partial) at this pitch
 constexpr int kOutPitch = 1040;
@@ -73,8 +73,8 @@ __device__ __forceinline__ f16v mfma32(bf16x8 a, bf16x8 b, f16v c) {
 
 // The S^T chain with its accumulator in VGPRs (the accumulation registers hold all of O^T):
 // the first step starts from zero, later steps accumulate through SrcC back to back.  The
-// compiler does not see these as MFMAs, so s_fence_s waits out the result latency (32x32x16:
-// 16 passes; a VALU read of the result needs 18 wait states) before anything reads S.
+// compiler does not see these as MFMAs, so s_result_fence waits out the result latency
+// (32x32x16: 16 passes; a VALU read of the result needs 18 wait states) before anything reads S.
 __device__ __forceinline__ void mfma32_v_first(f16v& c, bf16x8 a, bf16x8 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
@@ -172,13 +172,13 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     const int vgr = 2 * ih + ((j16 & 3) >> 1);
     const int vaddr1 = (4 * g + (j16 >> 2)) * kRowA16 + ((vgr ^ g) << 4) + (j16 & 1) * 8;
     const int vaddr2 = (4 * g + (j16 >> 2) + 8) * kRowA16 + ((vgr ^ ((g + 2) & 3)) << 4) + (j16 & 1) * 8;
-    // the value of lane ^ 32 (the other half of a row); the address is built at each use
-    // lane id recomputed where it is needed (no register holds it through the loops)
+    // the lane id, recomputed where it is needed (no register holds it through the loops)
     auto lane_now = []() {
         int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         asm volatile("" : "+v"(l));
         return l;
     };
+    // the value of lane ^ 32 (the other half of a row)
     auto xor32 = [&](float x) {
         return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_now() ^ 32) << 2, __float_as_int(x)));
     };
