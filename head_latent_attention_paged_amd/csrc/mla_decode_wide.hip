@@ -523,7 +523,9 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             pv(nch - 1, pb, no_side);
             // the copies past the segment's end land; every wave's vote visible
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (lane == 0) votes[wave] = __builtin_amdgcn_ballot_w64(outgrown) != 0 ? 1 : 0;
+            // (the ballot runs on the whole wave: inside the lane-0 branch it would see one row)
+            const bool wave_vote = __builtin_amdgcn_ballot_w64(outgrown) != 0;
+            if (lane == 0) votes[wave] = wave_vote ? 1 : 0;
             __syncthreads();
             int any = 0;
 #pragma unroll

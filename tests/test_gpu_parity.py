@@ -282,7 +282,7 @@ def test_paged_v4_geometry_cases(env, case):
     check_parity(o, l, o_ref, l_ref, "v4 " + str(case))
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.05, 0.5])
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.5, 2.5])
 def test_paged_v4_softmax_scales(env, scale):
     _say("paged v4 scale", scale)
     inp = make_paged(2, 6, 64, [900, 300], True, seed=650, poison=True, softmax_scale=scale, d_qk=512,
@@ -317,7 +317,7 @@ def test_paged_fp4_cases(env, case):
     check_parity(o, l, o_ref, l_ref, "fp4 " + str(case))
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.05, 0.5])
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.5, 2.5])
 def test_paged_fp4_softmax_scales(env, scale):
     _say("paged fp4 scale", scale)
     inp = make_paged_fp4(2, 6, 64, [900, 300], True, seed=750, poison=True, softmax_scale=scale, sinks=True)
@@ -369,6 +369,13 @@ SPARSE_CASES = [
     (1, 1, 16, 64, 1, 0.0, 0),
     (2, 6, 64, 2000, 512, 0.05, 1),
     (1, 2, 48, 700, 600, 0.2, 7),
+    # more than 64 heads: forced ragged splits with half the entries unused, 96 and 65 heads (a
+    # row group that ends mid-way), 200 heads (row groups share the records), a single record
+    (1, 2, 128, 600, 77, 0.5, 3),
+    (2, 1, 96, 1000, 300, 0.1, 0),
+    (1, 1, 65, 500, 400, 0.0, 0),
+    (1, 2, 200, 3000, 1000, 0.05, 2),
+    (1, 1, 128, 64, 1, 0.0, 0),
 ]
 
 
@@ -382,7 +389,7 @@ def test_sparse_cases(env, case):
     check_parity(o, l, o_ref, l_ref, str(case))
 
 
-@pytest.mark.parametrize("h_q", [16, 64])
+@pytest.mark.parametrize("h_q", [16, 64, 128])
 def test_sparse_all_skipped_and_duplicates(env, h_q):
     _say("sparse skip/dup h_q", h_q)
     inp = make_sparse(2, 2, h_q, 300, 64, 0.0, seed=31)
@@ -504,6 +511,8 @@ SPARSE_RAMP_CASES = [
     (2, 64, 3000, 2048, 0.05, -150.0, 0),
     (2, 128, 2500, 1500, 0.1, 150.0, 2),
     (2, 32, 2500, 1500, 0.1, 150.0, 0),
+    (2, 128, 3000, 2048, 0.05, -150.0, 0),
+    (1, 160, 2500, 1000, 0.05, 150.0, 0),
 ]
 
 
@@ -517,7 +526,7 @@ def test_sparse_wide_score_range(env, case):
     check_parity(o, l, o_ref, l_ref, "sparse ramp " + str(case))
 
 
-@pytest.mark.parametrize("h_q,scale", [(16, 2.5), (64, 2.5), (16, 0.7), (64, 0.7)])
+@pytest.mark.parametrize("h_q,scale", [(16, 2.5), (64, 2.5), (16, 0.7), (64, 0.7), (128, 2.5), (128, 0.7)])
 def test_large_softmax_scale(env, h_q, scale):
     """Scores with a spread of tens to hundreds of nats on random data, paged and sparse."""
     _say("large scale", h_q, scale)
@@ -532,7 +541,7 @@ def test_large_softmax_scale(env, h_q, scale):
         check_parity(o, l, o_ref, l_ref, "sparse scale %g h_q %d splits %d" % (scale, h_q, splits))
 
 
-@pytest.mark.parametrize("h_q", [16, 64])
+@pytest.mark.parametrize("h_q", [16, 64, 128])
 @pytest.mark.parametrize("scale", [0.0, -0.05])
 def test_non_positive_softmax_scale(env, h_q, scale):
     """softmax_scale = 0 (uniform weights) and a negative scale, paged and sparse."""
@@ -599,6 +608,7 @@ PREFILL_CASES = [
     (64, 16, 1024, 200, 0.1, 0),
     (40, 32, 1024, 100, 0.0, 0),
     (33, 64, 3000, 1000, 0.02, 3),
+    (50, 128, 2048, 700, 0.3, 2),
 ]
 
 
