@@ -152,6 +152,11 @@ PAGED_CASES = [
     (2, 3, 32, [300, 77], True, None),
     (2, 2, 65, [150, 64], True, 3),
     (1, 5, 40, [700], True, 2),
+    # 128 rows: empty sequences around a short one, an all-empty causal batch, 24 ragged
+    # sequences (0..3000 tokens) split over the default parts
+    (3, 1, 128, [0, 50, 0], False, None),
+    (2, 2, 64, [0, 0], True, None),
+    (24, 1, 128, [2012, 2415, 67, 2423, 1406, 1545, 1890, 857, 2938, 161, 833, 1150, 1713, 1225, 393, 135, 3, 146, 446, 2997, 572, 1957, 2250, 703], False, None),
 ]
 
 
@@ -376,6 +381,9 @@ SPARSE_CASES = [
     (1, 1, 65, 500, 400, 0.0, 0),
     (1, 2, 200, 3000, 1000, 0.05, 2),
     (1, 1, 128, 64, 1, 0.0, 0),
+    # top-k beyond one split's 2048 entries (at least three splits)
+    (1, 2, 128, 6000, 5000, 0.1, 0),
+    (2, 1, 16, 9000, 4500, 0.0, 0),
 ]
 
 
