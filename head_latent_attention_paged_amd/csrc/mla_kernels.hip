@@ -735,6 +735,7 @@ void mla_decode_m16_kernel(const AttnArgs a) {
 // --------------------------------------------------------------------------
 // K2: combine split-KV partials (one 128-thread half-block per output row)
 // --------------------------------------------------------------------------
+constexpr int kCombineGroup = 4;
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ prefix,
@@ -757,21 +758,40 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
     __bf16* orow = out + ((size_t)grp * rows + r) * kDv + d4 * 4;
     // an attention sink is one more term of the denominator, with LSE = the sink and no value
     const float sk = sinks ? sinks[r % h_q] : -INFINITY;
+    // The splits go in groups of kCombineGroup whose LSEs and values are loaded together (one
+    // memory round trip per group, not one for the maximum and one for the sum).  mu is the
+    // running maximum; a group that raises it rescales what the earlier groups summed.
     float mu = sk;
-    for (int i = 0; i < n; ++i) mu = fmaxf(mu, part_lse[(size_t)(base + i) * rows + r]);
+    float wsum = sk != -INFINITY ? 1.f : 0.f;
     f4 o = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (mu != -INFINITY) {
-        if (sk != -INFINITY) wsum = expf(sk - mu);
-        for (int i = 0; i < n; ++i) {
-            const float li = part_lse[(size_t)(base + i) * rows + r];
-            const float w = (li == -INFINITY) ? 0.f : expf(li - mu);
-            wsum += w;
-            const f4 v = *reinterpret_cast<const f4*>(part_o + ((size_t)(base + i) * rows + r) * kDv + d4 * 4);
-            o += v * w;
+    for (int i0 = 0; i0 < n; i0 += kCombineGroup) {
+        float li[kCombineGroup];
+        f4 v[kCombineGroup];
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; ++j) {
+            const int i = base + (i0 + j < n ? i0 + j : n - 1);    // (past n: a repeat, unused)
+            li[j] = part_lse[(size_t)i * rows + r];
+            v[j] = *reinterpret_cast<const f4*>(part_o + ((size_t)i * rows + r) * kDv + d4 * 4);
         }
-        o *= 1.f / wsum;
+        float mg = mu;
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; ++j)
+            if (i0 + j < n) mg = fmaxf(mg, li[j]);
+        if (mg == -INFINITY) continue;                          // nothing finite so far
+        const float sc = mu == -INFINITY ? 0.f : expf(mu - mg);  // mu <= mg
+        wsum *= sc;
+        o *= sc;
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; ++j) {
+            if (i0 + j < n && li[j] != -INFINITY) {
+                const float w = expf(li[j] - mg);
+                wsum += w;
+                o += v[j] * w;
+            }
+        }
+        mu = mg;
     }
+    if (mu != -INFINITY) o *= 1.f / wsum;
     const uint2 pk = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     *reinterpret_cast<uint2*>(orow) = pk;
     if (d4 == 0) lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
