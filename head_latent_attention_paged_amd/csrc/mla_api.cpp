@@ -114,11 +114,10 @@ static mla_status_t check_meta_args(const int32_t* seqlens, int batch, int num_p
 
 mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_parts,
                               int32_t* tile_meta, int32_t* num_splits, void* stream) {
-    (void)h_q;
-    (void)s_q;
     const mla_status_t st = check_meta_args(cache_seqlens, batch, num_parts, tile_meta, num_splits);
     if (st != MLA_OK) return st;
-    if (mla::launch_metadata(cache_seqlens, batch, num_parts, tile_meta, num_splits,
+    const int ovh = mla::meta_overhead_blocks((long long)h_q * s_q);
+    if (mla::launch_metadata(cache_seqlens, batch, num_parts, ovh, tile_meta, num_splits,
                              static_cast<hipStream_t>(stream)) != hipSuccess)
         return MLA_ERR_HIP;
     return MLA_OK;
@@ -126,13 +125,12 @@ mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, 
 
 mla_status_t mla_get_metadata_host(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_parts,
                                    int32_t* tile_meta, int32_t* num_splits) {
-    (void)h_q;
-    (void)s_q;
     const mla_status_t st = check_meta_args(cache_seqlens, batch, num_parts, tile_meta, num_splits);
     if (st != MLA_OK) return st;
     for (int b = 0; b < batch; ++b)
         if (cache_seqlens[b] < 0) return MLA_ERR_INVALID_ARG;
-    mla::metadata_host(cache_seqlens, batch, num_parts, tile_meta, num_splits);
+    mla::metadata_host(cache_seqlens, batch, num_parts, mla::meta_overhead_blocks((long long)h_q * s_q),
+                       tile_meta, num_splits);
     return MLA_OK;
 }
 
@@ -309,13 +307,14 @@ mla_status_t mla_sparse_prefill(const void* q, const void* kv, int64_t num_token
 namespace mla {
 
 // Host twin of mla_metadata_kernel: the same integer partition, computed sequentially.
-void metadata_host(const int32_t* seqlens, int batch, int num_parts, int32_t* tile_meta, int32_t* num_splits) {
+void metadata_host(const int32_t* seqlens, int batch, int num_parts, int ovh, int32_t* tile_meta,
+                   int32_t* num_splits) {
     std::vector<long long> cpre(batch + 1, 0);
     std::vector<int> nb(batch, 0);
     for (int b = 0; b < batch; ++b) {
         const int L = seqlens[b];
         nb[b] = L > 0 ? (L + kPage - 1) / kPage : 0;
-        cpre[b + 1] = cpre[b] + (nb[b] > 0 ? nb[b] + kMetaOverheadBlocks : 0);
+        cpre[b + 1] = cpre[b] + (nb[b] > 0 ? nb[b] + ovh : 0);
     }
     const long long total = cpre[batch];
     const long long payload = total > 0 ? (total + num_parts - 1) / num_parts : 1;
@@ -323,7 +322,7 @@ void metadata_host(const int32_t* seqlens, int batch, int num_parts, int32_t* ti
     for (int b = 0; b < batch; ++b) {
         int sp = 0;
         if (nb[b] > 0) {
-            const long long u0 = cpre[b] + kMetaOverheadBlocks;
+            const long long u0 = cpre[b] + ovh;
             sp = (int)((u0 + nb[b] - 1) / payload - u0 / payload + 1);
         }
         num_splits[b + 1] = num_splits[b] + sp;
@@ -340,12 +339,12 @@ void metadata_host(const int32_t* seqlens, int batch, int num_parts, int32_t* ti
             int b = 0;
             while (cpre[b + 1] <= u) ++b;
             bb[e] = b;
-            const long long off = u - cpre[b] - kMetaOverheadBlocks;
+            const long long off = u - cpre[b] - ovh;
             blk[e] = off > 0 ? (int)off : 0;
         }
         int slot = 0;
         if (bb[0] < batch) {
-            const long long first = (cpre[bb[0]] + kMetaOverheadBlocks) / payload;
+            const long long first = (cpre[bb[0]] + ovh) / payload;
             slot = (p < first) ? 0 : (int)(num_splits[bb[0]] + (p - first));
         }
         int32_t* m = tile_meta + (size_t)p * kMetaInts;

@@ -13,7 +13,6 @@ constexpr int kPage = 64;            // tokens per page
 constexpr int kRec = 640;            // bytes per sparse fp8 record
 constexpr int kChunk = 32;           // tokens per kernel chunk
 constexpr int kMetaInts = 8;
-constexpr int kMetaOverheadBlocks = 0;   // per-sequence fixed cost, in 64-token blocks
 constexpr int kMaxBatchMeta = 16384;
 constexpr int kMaxRows = 4096;       // s_q * h_q limit
 constexpr int kSparseTargetItems = 256;   // work items (one per compute unit) sparse splitting aims for
@@ -66,9 +65,9 @@ struct AttnArgs {
     float scale_log2;           // softmax_scale * log2(e)
 };
 
-hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts,
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int overhead,
                            int32_t* tile_meta, int32_t* num_splits, hipStream_t stream);
-void metadata_host(const int32_t* seqlens, int batch, int num_parts,
+void metadata_host(const int32_t* seqlens, int batch, int num_parts, int overhead,
                    int32_t* tile_meta, int32_t* num_splits);
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream);
 hipError_t launch_decode_big(const AttnArgs& a, bool sparse, hipStream_t stream);
@@ -78,6 +77,10 @@ hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream);
 // query rows per workgroup of the one-wave-per-SIMD kernel (used above 64 rows)
 constexpr int kWideRows = 128;
 constexpr int kWideMinRows = 64;
+// Per-sequence fixed cost in the tile scheduler's partition, in 64-token blocks: none up to 64
+// rows (equal sequences then split into equal parts with one segment each), two above, where a
+// segment start (Q, the first chunks, the epilogue of 128-row workgroups) costs more.
+inline int meta_overhead_blocks(long long rows) { return rows > kWideMinRows ? 2 : 0; }
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream, const float* sinks = nullptr, int h_q = 1);

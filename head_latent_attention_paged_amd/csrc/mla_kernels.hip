@@ -832,7 +832,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
 }
 
 __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_t* __restrict__ seqlens, int batch,
-                                                                    int num_parts, int32_t* __restrict__ tile_meta,
+                                                                    int num_parts, int ovh,
+                                                                    int32_t* __restrict__ tile_meta,
                                                                     int32_t* __restrict__ num_splits) {
     __shared__ int cpre[kMaxBatchMeta + 1];   // cost prefix C_b
     __shared__ int spre[kMaxBatchMeta + 1];   // split prefix
@@ -847,7 +848,7 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
         if (b < batch) {
             const int L = seqlens[b];
             const int nb = L > 0 ? (L + kPage - 1) / kPage : 0;
-            cost = nb > 0 ? nb + kMetaOverheadBlocks : 0;
+            cost = nb > 0 ? nb + ovh : 0;
         }
         int tot;
         const int ex = block_excl_scan(cost, tmp, tot);
@@ -865,10 +866,11 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
         const int b = b0 + t;
         int sp = 0;
         if (b < batch) {
-            const int L = seqlens[b];
-            const int nb = L > 0 ? (L + kPage - 1) / kPage : 0;
+            // the sequence's blocks from its cost (the lengths are not read a second time)
+            const int cost = cpre[b + 1] - cpre[b];
+            const int nb = cost > 0 ? cost - ovh : 0;
             if (nb > 0) {
-                const int u0 = cpre[b] + kMetaOverheadBlocks;
+                const int u0 = cpre[b] + ovh;
                 sp = (u0 + nb - 1) / payload - u0 / payload + 1;
             }
         }
@@ -897,12 +899,12 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
                 if (cpre[mid + 1] <= u) lo = mid + 1; else hi = mid;
             }
             bb[e] = lo;
-            const int off = (int)(u - cpre[lo]) - kMetaOverheadBlocks;
+            const int off = (int)(u - cpre[lo]) - ovh;
             blk[e] = off > 0 ? off : 0;
         }
         int slot = 0;
         if (bb[0] < batch) {
-            const int first = (cpre[bb[0]] + kMetaOverheadBlocks) / payload;
+            const int first = (cpre[bb[0]] + ovh) / payload;
             slot = spre[bb[0]] + (p - first);
             if (p < first) slot = 0;
         }
@@ -932,10 +934,10 @@ Tiling choose_tiling(int rows) {
     return t;
 }
 
-hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts,
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int overhead,
                            int32_t* tile_meta, int32_t* num_splits, hipStream_t stream) {
     hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(kMetaThreads), 0, stream,
-                       seqlens, batch, num_parts, tile_meta, num_splits);
+                       seqlens, batch, num_parts, overhead, tile_meta, num_splits);
     return hipGetLastError();
 }
 

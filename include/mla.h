@@ -76,15 +76,17 @@ int mla_num_parts(int num_cus, int h_q, int s_q);
  *   tile_meta     [device] int32[num_parts * MLA_META_INTS]  (out)
  *   num_splits    [device] int32[batch + 1]                  (out)
  *
- * Work is counted in 64-token blocks and cut into num_parts contiguous,
- * equally sized ranges of the flattened (sequence, block) order; a sequence
- * crossing a range edge is split.
+ * Work is counted in 64-token blocks, plus a fixed cost per non-empty
+ * sequence (none for s_q*h_q <= 64 rows, two blocks above), and cut into
+ * num_parts contiguous, equally sized ranges of the flattened (sequence,
+ * block) order; a sequence crossing a range edge is split.
  * num_splits is the exclusive prefix sum of the number of parts touching
  * each sequence (num_splits[b+1] - num_splits[b] = splits of sequence b);
  * it indexes the partial results in the workspace.  tile_meta[p] holds
  * {begin_seq, begin_block, end_seq, end_block, first_partial_slot, 0,0,0}.
- * h_q and s_q are accepted for the call shape of the pages' API; the
- * partition does not depend on them.  batch <= MLA_MAX_BATCH_META.
+ * h_q and s_q (the call shape of the pages' API) choose that fixed cost;
+ * the decode result does not depend on the partition.
+ * batch <= MLA_MAX_BATCH_META.
  */
 mla_status_t mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q,
                               int num_parts, int32_t* tile_meta, int32_t* num_splits,

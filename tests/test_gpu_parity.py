@@ -111,14 +111,15 @@ def run_sparse(env, inp, splits=0):
     ([0, 0, 5], 4), ([100] * 9, 1), (list(range(0, 3000, 37)), 64),
     (list(np.random.default_rng(1).integers(0, 9000, size=3000)), 128),
 ])
-def test_metadata_kernel_matches_host_twin(env, L, P):
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_metadata_kernel_matches_host_twin(env, L, P, h_q):
     import torch
 
     mla, dev = env
-    _say("metadata", len(L), P)
+    _say("metadata", len(L), P, h_q)
     L = np.asarray(L, dtype=np.int32)
-    meta_h, ns_h = mla.get_metadata_host(L, P)
-    meta_d, ns_d = mla.get_metadata(dev_i32(L, dev), 16, 1, P)
+    meta_h, ns_h = mla.get_metadata_host(L, P, h_q=h_q)
+    meta_d, ns_d = mla.get_metadata(dev_i32(L, dev), h_q, 1, P)
     torch.cuda.synchronize()
     assert np.array_equal(meta_d.cpu().numpy(), meta_h)
     assert np.array_equal(ns_d.cpu().numpy(), ns_h)
