@@ -157,6 +157,7 @@ PAGED_CASES = [
     # sequences (0..3000 tokens) split over the default parts
     (3, 1, 128, [0, 50, 0], False, None),
     (2, 2, 64, [0, 0], True, None),
+    (1, 6, 16, [322], True, 8),
     (24, 1, 128, [2012, 2415, 67, 2423, 1406, 1545, 1890, 857, 2938, 161, 833, 1150, 1713, 1225, 393, 135, 3, 146, 446, 2997, 572, 1957, 2250, 703], False, None),
 ]
 
@@ -274,6 +275,10 @@ V4_CASES = [
     (2, 2, 65, [150, 64], True, True, None),
     (1, 5, 40, [700], True, False, 3),
     (2, 2, 32, [3000, 2500], True, False, 2),
+    # a split whose tokens the first causal rows cannot see (a -inf partial beside the sink): the
+    # last block alone (3 parts), and in the combine's second group of splits (8 parts)
+    (1, 6, 64, [130], True, True, 3),
+    (1, 6, 64, [322], True, True, 8),
 ]
 
 
