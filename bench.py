@@ -1,12 +1,17 @@
-"""Benchmark: paged MLA decode on one MI355X against the HBM / bf16-MFMA roofline.
+"""Benchmark: paged and sparse MLA decode on one MI355X against the HBM / bf16-MFMA roofline.
 
-One step = one pass of the hot path over one batch: the tile-scheduler metadata, the
-decode kernel (gather, Q.K^T, online softmax, P.V, split epilogue) and the split-KV
-combine, on the memory-bound workload (batch 128, s_q 1, 16 heads, 4096 cached tokens
-each, 8192 pages permuted over the pool).  Inputs are seeded synthetic data resident in
-HBM before timing.  Prints one JSON line.
+One step = one pass of the hot path over one batch: the tile-scheduler metadata, the decode
+kernel (page gather, Q.K^T, online softmax, P.V, split epilogue) and the split-KV combine, on
+the long-context workload (batch 16, s_q 1, 16 heads, 65536 cached tokens each, 16384 pages
+permuted over the pool; 1208.6 MB of algorithmic bytes, the largest workload).  Inputs are
+seeded synthetic data resident in HBM before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu]
+The same JSON line also carries every workload's decode call timed on its own: median, p10 and
+p90 over calls that each follow a 512 MB read evicting L2 and the Infinity Cache, with GB/s,
+TFLOPS and the fraction of the roofline that bounds it (HBM for the memory-bound shapes, bf16
+MFMA for the compute-bound ones).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only K]
 """
 
 from __future__ import annotations
@@ -26,6 +31,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA datasheet (2.5 PFLOP/s)
 D_QK, D_V = 576, 512
+HEADLINE = 4                   # the long-context workload: the most bytes per call
+# what bounds each workload: the tiny one is latency only
+BOUND = {1: "latency", 2: "hbm", 3: "mfma", 4: "hbm", 5: "hbm", 6: "hbm", 7: "mfma", 8: "mfma", 9: "mfma"}
+PAGED_KINDS = ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4")
 
 
 def paged_counts(inp):
@@ -68,17 +77,16 @@ def sparse_counts(inp):
 
 
 CSRC = os.path.join(ROOT, "head_latent_attention_paged_amd", "csrc")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_paged_membound_b128_L4096_hbm_traffic.txt")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_paged_longctx_b16_L65536_hbm_traffic.txt")
 
-
-# sources of what the memory-bound call runs (memory-bound decode and combine kernels, their
-# shared device code and the host-side launch); the many-row kernels are not part of it
-DEFAULT_PATH_SOURCES = ("mla_api.cpp", "mla_device.h", "mla_internal.h", "mla_kernels.hip")
+# sources of what the 16-row paged decode call runs (the 16-row decode kernel, the combine,
+# their shared device code and the launch code); the many-row kernels are not part of it
+DEFAULT_PATH_SOURCES = ("mla_device.h", "mla_internal.h", "mla_kernels.hip")
 
 
 def kernel_source_hash():
-    """sha256 over the sources of the memory-bound call, to tell whether a stored counter profile
-    still describes the kernels being run."""
+    """sha256 over the sources of the 16-row paged decode call, to tell whether a stored counter
+    profile still describes the kernels being run."""
     import hashlib
 
     h = hashlib.sha256()
@@ -141,7 +149,8 @@ class Flusher:
 
 
 def time_calls(torch, fn, n, flush=None):
-    """Per-call device time (ms) with events on the current stream; optional flush between calls."""
+    """Per-call device time (ms) with events on the current stream (the one the library
+    launches on); optional flush before each call, outside the events."""
     s = torch.cuda.current_stream()
     times = []
     for _ in range(n):
@@ -157,21 +166,9 @@ def time_calls(torch, fn, n, flush=None):
     return np.array(times)
 
 
-def time_back_to_back(torch, fn, n):
-    """Mean device time (ms) per call of n back-to-back calls between two events on the current
-    stream: the kernels' own durations plus the gaps between consecutive launches."""
-    s = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(n):
-        fn()
-    e1.record(s)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / n
-
-
 def setup_paged(torch, mla, inp, dev):
+    """(step, decode) for a paged workload: step = metadata + decode call; decode = the call
+    with the metadata computed once."""
     from tests.helpers import dev_bf16, dev_i32, dev_u8
 
     q = dev_bf16(inp.q, dev)
@@ -203,10 +200,10 @@ def setup_paged(torch, mla, inp, dev):
     def decode():
         call(meta)
 
-    def step():
-        call(mla.get_metadata(sl, inp.h_q, inp.s_q, P))
+    def metadata():
+        return mla.get_metadata(sl, inp.h_q, inp.s_q, P)
 
-    return step, decode
+    return call, decode, metadata
 
 
 def setup_sparse(torch, mla, inp, dev):
@@ -221,7 +218,7 @@ def setup_sparse(torch, mla, inp, dev):
     def decode():
         mla.decode_sparse(q, kv, idx, inp.softmax_scale, 0, out=out, lse=lse, workspace=ws)
 
-    return decode, decode
+    return decode
 
 
 def setup_prefill(torch, mla, inp, dev):
@@ -237,7 +234,50 @@ def setup_prefill(torch, mla, inp, dev):
     def prefill():
         mla.sparse_prefill(q, kv, idx, inp.softmax_scale, 0, out=out, lse=lse, workspace=ws)
 
-    return prefill, prefill
+    return prefill
+
+
+def setup_call(torch, mla, k, inp, dev):
+    """Workload k's decode call (metadata computed once for paged workloads) and its counts."""
+    from mla_inputs import CONFIGS
+
+    kind = CONFIGS[k]["kind"]
+    if kind in PAGED_KINDS:
+        _, fn, _ = setup_paged(torch, mla, inp, dev)
+        return fn, paged_counts(inp)
+    if kind == "sparse_prefill":
+        return setup_prefill(torch, mla, inp, dev), sparse_counts(inp)
+    return setup_sparse(torch, mla, inp, dev), sparse_counts(inp)
+
+
+# the kernels each workload's call runs (kernel-trace names), for reading the profiles
+KERNELS = {
+    1: "mla_decode_m16_kernel + mla_combine_kernel",
+    2: "mla_decode_m16_kernel + mla_combine_kernel",
+    3: "mla_decode_wide_kernel<0, true, 576> + mla_combine_kernel",
+    4: "mla_decode_m16_kernel + mla_combine_kernel",
+    5: "mla_decode_rows_kernel<1, false, 576> (one split)",
+    6: "mla_decode_m16_fp8_kernel + mla_combine_kernel",
+    7: "mla_decode_wide_kernel<0, true, 512> + mla_combine_kernel",
+    8: "mla_decode_wide_kernel<3, true, 512> + mla_combine_kernel",
+    9: "mla_decode_rows_kernel<1, true, 576> (one split)",
+}
+
+
+def workload_entry(k, name, t_ms, byts, flops):
+    us = float(np.median(t_ms)) * 1e3
+    gbs = byts / (us * 1e-6) / 1e9
+    tfl = flops / (us * 1e-6) / 1e12
+    e = {"workload": name, "kernels": KERNELS[k], "calls": int(len(t_ms)),
+         "us_median": round(us, 2), "us_p10": round(float(np.percentile(t_ms, 10)) * 1e3, 2),
+         "us_p90": round(float(np.percentile(t_ms, 90)) * 1e3, 2),
+         "GBps": round(gbs, 1), "TFLOPS": round(tfl, 1),
+         "algorithmic_bytes": byts, "algorithmic_flops": flops, "bound": BOUND[k]}
+    if BOUND[k] == "hbm":
+        e.update(peak=HBM_PEAK_GBS, peak_unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    elif BOUND[k] == "mfma":
+        e.update(peak=BF16_PEAK_TFLOPS, peak_unit="TFLOP/s", frac=round(tfl / BF16_PEAK_TFLOPS, 4))
+    return e
 
 
 def cpu_baseline(inp, kind, counts_fn, min_s=10.0, max_s=30.0):
@@ -287,43 +327,61 @@ def run_calls(k, n):
     import torch
 
     import head_latent_attention_paged_amd as mla
-    from mla_inputs import CONFIGS, make_config
+    from mla_inputs import make_config
 
     dev = torch.device("cuda:0")
     inp = make_config(k, poison=False)
-    if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4"):
-        _, fn = setup_paged(torch, mla, inp, dev)
-    elif CONFIGS[k]["kind"] == "sparse_prefill":
-        _, fn = setup_prefill(torch, mla, inp, dev)
-    else:
-        _, fn = setup_sparse(torch, mla, inp, dev)
+    fn, _ = setup_call(torch, mla, k, inp, dev)
     for _ in range(n):
         fn()
     torch.cuda.synchronize()
     print("ran %d decode calls of workload %d" % (n, k), flush=True)
 
 
+def time_steps(torch, inp, call, metadata, steps, warmup):
+    """The timed steps: metadata + decode call, K times back to back.  Wall clock around the
+    whole loop (synchronised on both sides); HIP events on the launch stream around each step's
+    decode call, for the per-launch time of the decode kernel and its combine."""
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call(metadata())
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        m = metadata()
+        ev[i][0].record(s)
+        call(m)
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = np.array([a.elapsed_time(b) for a, b in ev])
+    return wall, per_call
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--extra", action="store_true", help="also time the other workloads (flushed, per call)")
+    ap.add_argument("--calls", type=int, default=30, help="flushed calls timed per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--only", type=int, default=0, metavar="K",
+                    help="time only workload K (its flushed calls; the steps too when K is the headline)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration) and exit")
     ap.add_argument("--calls-of", type=int, default=0, metavar="K",
                     help="only run workload K's decode call --steps times, untimed (for counter passes), and exit")
     args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
     if args.copy_probe:
         copy_probe()
         return
     if args.calls_of:
         run_calls(args.calls_of, args.steps)
         return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
-        sys.exit(2)
 
     import torch
 
@@ -331,90 +389,63 @@ def main():
     from mla_inputs import CONFIGS, make_config
 
     dev = torch.device("cuda:0")
-    print("[bench] generating the memory-bound workload", file=sys.stderr, flush=True)
-    inp = make_config(2, poison=False)
-    byts, flops = paged_counts(inp)
-    step, decode = setup_paged(torch, mla, inp, dev)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # the decode call (decode kernel + combine) timed with events on the stream it launches on
-    dec_ms = time_back_to_back(torch, decode, max(args.steps, 20))
-    achieved = byts / (dec_ms * 1e-3) / 1e9
-    traffic, traffic_note = traffic_from_profile()
-
     res = {
         "metric": "paged MLA decode us/call, achieved HBM GB/s and TFLOPS vs MI355X roofline",
-        "value": round(byts / (ms_per_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": CONFIGS[2]["name"], "batch": inp.batch, "s_q": inp.s_q, "h_q": inp.h_q,
-                   "seq_len": int(inp.seqlens[0]), "page": 64, "pages": inp.num_pages,
-                   "parallelism": "single GPU"},
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "tflops_per_step": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
-        "algorithmic_bytes": byts,
-        "algorithmic_flops": flops,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_note": traffic_note, "algorithmic_bytes_per_launch": byts,
-                     "kernel": "mla_decode_paged call (mla_decode_m16_kernel + mla_combine_kernel)",
-                     "us_per_launch": round(dec_ms * 1e3, 2)},
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
     }
+    head = None
+    if args.only in (0, HEADLINE):
+        print("[bench] workload %d (headline): generating" % HEADLINE, file=sys.stderr, flush=True)
+        head = make_config(HEADLINE, poison=False)
+        byts, flops = paged_counts(head)
+        call, _, metadata = setup_paged(torch, mla, head, dev)
+        wall, per_call = time_steps(torch, head, call, metadata, args.steps, args.warmup)
+        ms_per_step = wall * 1e3 / args.steps
+        dec_ms = float(per_call.mean())
+        achieved = byts / (dec_ms * 1e-3) / 1e9
+        traffic, traffic_note = traffic_from_profile()
+        res.update({
+            "value": round(byts / (ms_per_step * 1e-3) / 1e9, 2),
+            "ms_per_step": round(ms_per_step, 5),
+            "config": {"workload": CONFIGS[HEADLINE]["name"], "batch": head.batch, "s_q": head.s_q,
+                       "h_q": head.h_q, "seq_len": int(head.seqlens[0]), "page": 64, "pages": head.num_pages,
+                       "kv_dtype": "bf16", "parallelism": "single GPU"},
+            "us_per_step": round(ms_per_step * 1e3, 2),
+            "tflops_per_step": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+            "algorithmic_bytes": byts,
+            "algorithmic_flops": flops,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "traffic_note": traffic_note, "algorithmic_bytes_per_launch": byts,
+                         "kernel": "mla_decode_paged call (%s)" % KERNELS[HEADLINE],
+                         "us_per_launch": round(dec_ms * 1e3, 2),
+                         "us_per_launch_p10": round(float(np.percentile(per_call, 10)) * 1e3, 2),
+                         "us_per_launch_p90": round(float(np.percentile(per_call, 90)) * 1e3, 2),
+                         "timing": "HIP events on the launch stream around each timed step's decode call"},
+        })
 
-    if args.extra:
-        flush = Flusher(torch, dev)
-        extra = {}
-        for k in (2, 3, 4, 5, 6, 7, 8, 9):
-            print("[bench] workload %d" % k, file=sys.stderr, flush=True)
-            ik = inp if k == 2 else make_config(k, poison=False)
-            if CONFIGS[k]["kind"] in ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4"):
-                _, fn = setup_paged(torch, mla, ik, dev)
-                b_k, f_k = paged_counts(ik)
-            elif CONFIGS[k]["kind"] == "sparse_prefill":
-                _, fn = setup_prefill(torch, mla, ik, dev)
-                b_k, f_k = sparse_counts(ik)
-            else:
-                _, fn = setup_sparse(torch, mla, ik, dev)
-                b_k, f_k = sparse_counts(ik)
-            for _ in range(3):
-                fn()
-            t = time_calls(torch, fn, 30, flush=flush)
-            us = float(np.median(t)) * 1e3
-            extra["config%d" % k] = {
-                "workload": CONFIGS[k]["name"], "us_median": round(us, 2),
-                "us_p10": round(float(np.percentile(t, 10)) * 1e3, 2),
-                "us_p90": round(float(np.percentile(t, 90)) * 1e3, 2),
-                "GBps": round(b_k / (us * 1e-6) / 1e9, 1), "TFLOPS": round(f_k / (us * 1e-6) / 1e12, 1),
-                "hbm_frac": round(b_k / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "mfma_frac": round(f_k / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "algorithmic_bytes": b_k, "algorithmic_flops": f_k,
-            }
-            if k != 2:
-                del ik
-                torch.cuda.empty_cache()
-        res["workloads_flushed"] = extra
+    flush = Flusher(torch, dev)
+    work = {}
+    for k in ([args.only] if args.only else sorted(CONFIGS)):
+        print("[bench] workload %d: %s" % (k, CONFIGS[k]["name"]), file=sys.stderr, flush=True)
+        ik = head if k == HEADLINE and head is not None else make_config(k, poison=False)
+        fn, (b_k, f_k) = setup_call(torch, mla, k, ik, dev)
+        for _ in range(3):
+            fn()
+        t = time_calls(torch, fn, args.calls * (4 if k == 1 else 1), flush=flush)
+        work["config%d" % k] = workload_entry(k, CONFIGS[k]["name"], t, b_k, f_k)
+        del fn
+        if ik is not head:
+            del ik
+        torch.cuda.empty_cache()
+    res["workloads_flushed"] = work
 
-    if not args.no_cpu:
+    if head is not None and not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, "paged", paged_counts)
-    print(json.dumps(res))
+        res["cpu_baseline"] = cpu_baseline(head, "paged", paged_counts)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -1,5 +1,8 @@
 """Shared helpers for the GPU parity tests: host -> device copies and the parity bar."""
 
+import json
+import os
+
 import numpy as np
 
 
@@ -41,3 +44,22 @@ def check_parity(o, l, o_ref, l_ref, what=""):
         lerr = np.abs(l[finite] - l_ref[finite]).max()
         assert lerr <= 1e-3, "%s: max|LSE-LSE_ref| = %.3g" % (what, lerr)
     return err, float(np.sqrt(np.mean((o - o_ref) ** 2)))
+
+
+def record_parity(what, o, l, o_ref, l_ref):
+    """Error figures of one compared output (max |O - O_ref| against the bar, RMSE of O against
+    the float64 reference, max |LSE - LSE_ref| on finite rows), appended as one JSON line to the
+    file named by MLA_PARITY_LOG when it is set.  Returns the figures."""
+    finite = np.isfinite(l_ref)
+    rec = {"what": what, "rows": int(l_ref.size),
+           "max_abs_err": float(np.abs(o - o_ref).max()),
+           "tol": float(1e-2 * np.abs(o_ref).max() + 2e-3),
+           "rmse": float(np.sqrt(np.mean((o - o_ref) ** 2))),
+           "rms_ref": float(np.sqrt(np.mean(o_ref ** 2))),
+           "max_lse_err": float(np.abs(l[finite] - l_ref[finite]).max()) if finite.any() else 0.0}
+    path = os.environ.get("MLA_PARITY_LOG")
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    return rec
