@@ -24,8 +24,9 @@ EXPORTS = (
     "mla_status_string", "mla_num_parts", "mla_get_metadata", "mla_get_metadata_host",
     "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_decode_paged_latent512",
     "mla_decode_paged_fp4", "mla_sparse_splits",
-    "mla_workspace_size_sparse", "mla_decode_sparse", "mla_sparse_prefill",
+    "mla_workspace_size_sparse", "mla_decode_sparse", "mla_sparse_prefill", "mla_decode_paged_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20     # MLA_NOALLOC_SCRATCH_BYTES
 
 
 class MLAError(RuntimeError):
@@ -55,6 +56,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32,
                                      vp, vp, i32, vp, sz, vp, vp, vp]
     lib.mla_decode_paged.restype = i32
+    lib.mla_decode_paged_noalloc.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32,
+                                             vp, vp, i32, vp, vp, vp]
+    lib.mla_decode_paged_noalloc.restype = i32
     lib.mla_decode_paged_fp8.argtypes = lib.mla_decode_paged.argtypes
     lib.mla_decode_paged_fp8.restype = i32
     lib.mla_decode_paged_latent512.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp,
@@ -195,6 +199,40 @@ def decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tenso
         cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
         tile_meta.data_ptr(), num_splits.data_ptr(), P,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, lse
+
+
+def decode_paged_noalloc(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                         cache_seqlens: torch.Tensor, metadata: Tuple[torch.Tensor, torch.Tensor],
+                         softmax_scale: float = D_QK ** -0.5, causal: bool = False,
+                         out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_paged_noalloc: the bf16 paged decode with the split-KV partials in the
+    library's own per-GPU array (no workspace argument).  Shapes as for decode_paged with a
+    bf16 [num_blocks, 64, 1, 576] cache.  Pass ``out`` and ``lse`` to allocate nothing here
+    either."""
+    batch, s_q, h_q, d = q.shape
+    if d != D_QK:
+        raise ValueError("q must have 576 dims per head")
+    _require(q, "q", torch.bfloat16)
+    _require(kcache, "kcache", torch.bfloat16)
+    if kcache.dim() != 4 or tuple(kcache.shape[1:]) != (PAGE, 1, D_QK):
+        raise ValueError("kcache must be [num_blocks, 64, 1, 576]")
+    _require(block_table, "block_table", torch.int32)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
+    tile_meta, num_splits = metadata
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, (batch, s_q, h_q, D_V))
+    _require(lse, "lse", torch.float32, (batch, s_q, h_q))
+    _check("mla_decode_paged_noalloc", lib.mla_decode_paged_noalloc(
+        q.data_ptr(), kcache.data_ptr(), kcache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        cache_seqlens.data_ptr(), batch, s_q, h_q, float(softmax_scale), 1 if causal else 0,
+        tile_meta.data_ptr(), num_splits.data_ptr(), tile_meta.shape[0],
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
     return out, lse
 

@@ -28,6 +28,7 @@ SOURCES = {
     "mla_decode_fp8.hip": VGPR_FORM,
     "mla_decode_wide.hip": [],
     "mla_api.cpp": [],
+    "mla_noalloc.hip": [],
 }
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -142,7 +142,8 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
                                       void* workspace, size_t workspace_bytes,
                                       void* out, float* lse, void* stream, bool fp8,
                                       int d_qk = mla::kDqk, const float* sinks = nullptr,
-                                      const void* kv_scale = nullptr, bool fp4 = false) {
+                                      const void* kv_scale = nullptr, bool fp4 = false,
+                                      mla::ScratchSource scratch = nullptr) {
     if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0 || max_blocks <= 0 || num_blocks <= 0)
@@ -153,6 +154,12 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     if ((long long)s_q * h_q > mla::kMaxRows) return MLA_ERR_UNSUPPORTED;
     if (batch > mla::kMaxBatchMeta) return MLA_ERR_UNSUPPORTED;
     const size_t need = mla_workspace_size(batch, s_q, h_q, num_parts);
+    if (scratch) {
+        // no caller workspace: the library's own fixed-size array, looked up only once every
+        // host-side check has passed (a rejected call touches no device)
+        const mla_status_t st = scratch(need, &workspace, &workspace_bytes);
+        if (st != MLA_OK) return st;
+    }
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
     if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
     const int M = s_q * h_q;
@@ -206,6 +213,25 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
                              softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
                              workspace_bytes, out, lse, stream, false);
 }
+
+}  // extern "C"
+
+namespace mla {
+
+mla_status_t decode_paged_scratch(const void* q, const void* kcache, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  float softmax_scale, int causal,
+                                  const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                  void* out, float* lse, void* stream, ScratchSource scratch) {
+    return decode_paged_impl(q, kcache, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                             softmax_scale, causal, tile_meta, num_splits, num_parts, nullptr, 0, out, lse,
+                             stream, false, kDqk, nullptr, nullptr, false, scratch);
+}
+
+}  // namespace mla
+
+extern "C" {
 
 mla_status_t mla_decode_paged_latent512(const void* q, const void* kcache, int64_t num_blocks,
                                        const int32_t* block_table, int max_blocks,

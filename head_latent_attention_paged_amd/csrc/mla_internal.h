@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <cstddef>
+#include "mla.h"
 #include <cstdint>
 
 namespace mla {
@@ -81,6 +82,16 @@ constexpr int kWideMinRows = 64;
 // rows (equal sequences then split into equal parts with one segment each), two above, where a
 // segment start (Q, the first chunks, the epilogue of 128-row workgroups) costs more.
 inline int meta_overhead_blocks(long long rows) { return rows > kWideMinRows ? 2 : 0; }
+// Supplies the workspace of a call that brings none: given the bytes the call needs, sets the
+// pointer and size of the library's own array, or returns an error status.
+typedef mla_status_t (*ScratchSource)(size_t need, void** ptr, size_t* bytes);
+// mla_decode_paged with the workspace taken from `scratch` after the host-side checks pass
+mla_status_t decode_paged_scratch(const void* q, const void* kcache, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  float softmax_scale, int causal,
+                                  const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                  void* out, float* lse, void* stream, ScratchSource scratch);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream, const float* sinks = nullptr, int h_q = 1);

@@ -15,7 +15,9 @@
  *    Tensors are dense and row-major.  q, kcache, kv, out and workspace must
  *    be 16-byte aligned.
  *  - The caller allocates and owns every buffer and the stream.  The library
- *    allocates nothing, keeps no state between calls and never synchronises.
+ *    allocates nothing, keeps no state between calls and never synchronises
+ *    (mla_decode_paged_noalloc aside, whose workspace is an array the library
+ *    holds on each GPU).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    All work is enqueued on it asynchronously.
  *  - Arguments the host can check are validated before anything is
@@ -128,6 +130,36 @@ mla_status_t mla_decode_paged(const void* q, const void* kcache, int64_t num_blo
                               const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
                               void* workspace, size_t workspace_bytes,
                               void* out, float* lse, void* stream);
+
+/*
+ * mla_decode_paged without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes the same arguments as mla_decode_paged except
+ * workspace and workspace_bytes, and computes the same result with the same
+ * kernels.  The split-KV partials go to an array of MLA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on (from the library's load to
+ * the end of the process); the call allocates and frees nothing.
+ *
+ *  - The array used is the current device's (hipGetDevice); `stream` must
+ *    belong to that device.  Its address is looked up on the first call on a
+ *    device.
+ *  - A shape whose workspace (mla_workspace_size(batch, s_q, h_q, num_parts))
+ *    exceeds MLA_NOALLOC_SCRATCH_BYTES returns MLA_ERR_WORKSPACE before
+ *    anything is launched; 32 MiB holds the partials of s_q * h_q = 16 rows for
+ *    batch + num_parts up to 1022.  Other argument errors are those of
+ *    mla_decode_paged.
+ *  - Nothing in the array needs to start at zero.  Every call on one GPU shares
+ *    its array, which keeps the last call's partials: calls that overlap in
+ *    time on one GPU (two streams, two threads) race and give undefined
+ *    results.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+mla_status_t mla_decode_paged_noalloc(const void* q, const void* kcache, int64_t num_blocks,
+                                      const int32_t* block_table, int max_blocks,
+                                      const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                      float softmax_scale, int causal,
+                                      const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                                      void* out, float* lse, void* stream);
 
 /*
  * Paged decode in the DeepSeek-V4 main-attention geometry ("[flashinfer]

@@ -80,6 +80,28 @@ def test_paged_validation_before_launch(mla):
     assert _paged_call(mla, ws=None) == mla.MLA_ERR_INVALID_ARG
 
 
+def _noalloc_call(mla, **kw):
+    a = dict(q=16, kc=16, nb=4, bt=16, maxb=1, sl=16, batch=1, s_q=1, h_q=16, scale=0.04, causal=0,
+             meta=16, ns=16, P=8, out=16, lse=16)
+    a.update(kw)
+    return mla.lib.mla_decode_paged_noalloc(a["q"], a["kc"], a["nb"], a["bt"], a["maxb"], a["sl"], a["batch"],
+                                            a["s_q"], a["h_q"], a["scale"], a["causal"], a["meta"], a["ns"],
+                                            a["P"], a["out"], a["lse"], None)
+
+
+def test_paged_noalloc_validation_before_launch(mla):
+    # argument errors of mla_decode_paged, and a workspace beyond the library's array, are
+    # rejected before the array is looked up or anything is launched (no device is touched)
+    assert _noalloc_call(mla, q=None) == mla.MLA_ERR_INVALID_ARG
+    assert _noalloc_call(mla, batch=0) == mla.MLA_ERR_INVALID_ARG
+    assert _noalloc_call(mla, scale=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert _noalloc_call(mla, s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
+    # 16 rows: batch + parts up to 1022 fit in 32 MiB, 1023 do not
+    assert mla.workspace_size(766, 1, 16, 256) <= mla.NOALLOC_SCRATCH_BYTES < mla.workspace_size(767, 1, 16, 256)
+    assert _noalloc_call(mla, batch=767, P=256) == mla.MLA_ERR_WORKSPACE
+    assert _noalloc_call(mla, batch=128, s_q=2, h_q=128, P=128) == mla.MLA_ERR_WORKSPACE
+
+
 def test_paged_fp8_validation_before_launch(mla):
     # the same host checks as the bf16 call, plus the 32-bit offset limit of the many-row path
     assert _paged_call(mla, fp8=True, kc=None) == mla.MLA_ERR_INVALID_ARG
