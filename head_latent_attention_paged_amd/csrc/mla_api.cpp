@@ -163,10 +163,6 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
     if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
     const int M = s_q * h_q;
-    // fp8 pages with more than 16 rows go through 32-bit buffer offsets
-    if (fp8 && M > 16 && num_blocks * mla::kPage * mla::kRec > mla::kRowsSparseMaxPool) return MLA_ERR_UNSUPPORTED;
-    // FP4 pages: the row-split kernel's gathers, 32-bit offsets into the 256-byte code rows
-    if (fp4 && num_blocks * mla::kPage * 256 > mla::kRowsSparseMaxPool) return MLA_ERR_UNSUPPORTED;
 
     const long long slots = (long long)batch + num_parts;
     mla::AttnArgs a{};

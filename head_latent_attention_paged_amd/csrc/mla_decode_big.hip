@@ -640,9 +640,10 @@ static hipError_t launch_big_t(const AttnArgs& a, int items, hipStream_t stream)
 
 hipError_t launch_decode_big(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const int items = sparse ? a.batch * a.num_parts : a.num_parts;
-    if (big_pairs(a.M) == 1)
-        return sparse ? launch_big_t<true, 1>(a, items, stream) : launch_big_t<false, 1>(a, items, stream);
-    return sparse ? launch_big_t<true, 2>(a, items, stream) : launch_big_t<false, 2>(a, items, stream);
+    // sparse calls come here with 16 < h_q <= 32 only (more heads take the row-split kernel)
+    if (sparse) return big_pairs(a.M) == 1 ? launch_big_t<true, 1>(a, items, stream) : hipErrorInvalidValue;
+    if (big_pairs(a.M) == 1) return launch_big_t<false, 1>(a, items, stream);
+    return launch_big_t<false, 2>(a, items, stream);
 }
 
 }  // namespace mla

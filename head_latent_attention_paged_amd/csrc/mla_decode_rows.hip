@@ -68,13 +68,12 @@ __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
 
 // Sparse gathers: a chunk's 32 records are 32 x 36 granules of 16 codes plus 32 scale granules;
 // a wave loads 4 records = 148 granules with 3 loads of 64 lanes (slots 148..191 repeat slots
-// 84..127: same data to the same place).  Index entries become byte offsets into the record
-// pool once per segment; an unused entry (or one past the list) gets kNoRecord, which lies
-// beyond the buffer's range, so its loads return zeros.
+// 84..127: same data to the same place).  Index entries become record numbers once per segment;
+// an unused entry (or one past the list) becomes -1, which reads record 0 and is marked unused.
+// Loads take 64-bit addresses, so the record pool has no size limit.
 constexpr int kGather = 3;
 // output staging: a wave's 16 rows x 256 values (fp32 1 KB, bf16 512 B per row) at this row pitch
 constexpr int kOutPitch = 1040;
-constexpr unsigned kNoRecord = 0xFFFFF000u;
 
 template <bool GATHER, bool SPARSE, int D>
 struct Cfg {
@@ -207,12 +206,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                                   : kRegionB16 + tok * 128 + (((2 * (gran - 32)) ^ swzB(tok)) << 4);
         }
     }
-    // gathered records as a raw buffer (offsets past its end read zeros); FP4 scales as another
-    const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * REC) : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t pool_sc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.kv_scale), (short)0, FP4 ? (int)(unsigned)(a.kv_rows * (kFp4RowBytes >> kFp4ScaleShift)) : 0,
-        0x00020000);
+    // gathered records (FP4: code rows) and the FP4 scale rows, addressed with 64-bit offsets
+    const char* pool = static_cast<const char*>(a.kv);
+    const char* pool_sc = static_cast<const char*>(a.kv_scale);
 
     bf16x8 qf[KS];
     f4 acc[16];
@@ -235,12 +231,12 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         const int limit = a.causal ? (L - a.s_q + row / a.h_q) : (L - 1);
 
         // sparse: the split's index list (at most kMaxSparseSplit entries) goes to LDS once, as
-        // record byte offsets (kNoRecord for unused entries and up to the end of the last chunk)
+        // record numbers (-1 for unused entries and up to the end of the last chunk)
         if constexpr (SPARSE) {
             for (int e = threadIdx.x; e < nch * kChunk; e += kWaves * 64) {
                 long long v = -1;
                 if (e < t1 - t0) v = a.indices[(size_t)grp * a.topk + t0 + e];
-                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)((unsigned)v * REC) : (int)kNoRecord;
+                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)v : -1;
             }
             __syncthreads();
         }
@@ -300,7 +296,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // c's ring slot.  Chunks past the segment's end gather its last chunk again (unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         u32x4 gv[GATHER ? NG : 1];
-        unsigned g_rec[GATHER ? NG : 1];
+        int g_rec[GATHER ? NG : 1];       // record of load i, -1: none (reads record 0)
         unsigned short g_sc = 0;      // FP4: the two scale bytes of this lane's 32 values
         // paged gathers of the current chunk (wave-uniform): record of its first token, and how
         // many of its tokens are read (0 for a page outside the cache)
@@ -308,9 +304,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         int gp_n = 0;
         auto gather = [&](int c, int i) {
             const int cc = min(c, nch - 1);
-            unsigned rec;
+            int rec;
             if constexpr (SPARSE) {
-                rec = *reinterpret_cast<const unsigned*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
+                rec = *reinterpret_cast<const int*>(reinterpret_cast<const char*>(lidx) + cc * kChunk * 4 + g_tok[i]);
             } else {
                 // paged records: a chunk lies inside one page (segments start on a page); tokens
                 // past the segment's end read nothing.  Gather 0 of a chunk comes first.
@@ -322,22 +318,26 @@ void mla_decode_rows_kernel(const AttnArgs a) {
                     gp_n = pg_ok ? min(kChunk, t1 - tb) : 0;
                 }
                 const int lt = g_tok[i] >> 2;
-                rec = lt < gp_n ? (gp_rec0 + lt) * REC : kNoRecord;
+                rec = lt < gp_n ? (int)(gp_rec0 + lt) : -1;
             }
             g_rec[i] = rec;
-            gv[i] = __builtin_amdgcn_raw_buffer_load_b128(pool, rec + (unsigned)g_off[i], 0, SHARED ? 0 : 2);
-            // (kNoRecord >> 3 also lies past the end of the scales)
+            const size_t rr = rec >= 0 ? (size_t)rec : 0;
+            const u32x4* gp = reinterpret_cast<const u32x4*>(pool + rr * REC + g_off[i]);
+            if constexpr (SHARED) gv[i] = *gp;
+            else gv[i] = __builtin_nontemporal_load(gp);
             if constexpr (FP4)
-                g_sc = __builtin_amdgcn_raw_buffer_load_b16(pool_sc, (rec >> kFp4ScaleShift) + ((unsigned)g_off[i] >> 3),
-                                                            0, SHARED ? 0 : 2);
+                g_sc = *reinterpret_cast<const unsigned short*>(pool_sc + rr * (kFp4RowBytes >> kFp4ScaleShift) +
+                                                                (g_off[i] >> 3));
         };
         // FP4: quarter w (8 values, dims 32*(lane & 15) + 8w .. +7) of this lane's registers into
         // chunk c's ring slot.  Code bytes 0..7 belong to block 2*(lane & 15), bytes 8..15 to the
         // next block.
         auto convert_fp4 = [&](int c, int w) {
             char* slot = ring + (c % DEPTH) * C::BUF;
-            const unsigned codes = gv[0][w];
-            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc >> (8 * (w >> 1))), 0);
+            // an unused token converts to zeros (record 0's bytes, which it read, are not its own)
+            const bool none = g_rec[0] < 0;
+            const unsigned codes = none ? 0u : gv[0][w];
+            const float sc = none ? 0.f : __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc >> (8 * (w >> 1))), 0);
             unsigned o[4];
             // with a unit scale the conversion is exact; the block scale multiplies in fp32,
             // exactly, and the product is a bf16 value
@@ -352,15 +352,16 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             // token validity: 1 for a record, NaN for an unused entry (masked off)
             if (w == 0 && (lane & 15) == 0)
                 *reinterpret_cast<unsigned*>(slot + kChunk16 + (g_tok[0] >> 2) * 32) =
-                    g_rec[0] >= kNoRecord ? 0x7fc00000u : 0x3f800000u;
+                    g_rec[0] < 0 ? 0x7fc00000u : 0x3f800000u;
         };
         auto convert = [&](int c, int i) {
             char* slot = ring + (c % DEPTH) * C::BUF;
-            const u32x4 r = gv[i];
+            // an unused entry converts to zeros (record 0's bytes, which it read, are not its own)
+            const u32x4 r = g_rec[i] < 0 ? u32x4{0u, 0u, 0u, 0u} : gv[i];
             uint4 lo = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.x, r.y));
             const uint4 hi = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.z, r.w));
             // scale granule: the raw fp32 scale, NaN for an unused entry (masked off)
-            const unsigned sc = g_rec[i] >= kNoRecord ? 0x7fc00000u : r.x;
+            const unsigned sc = g_rec[i] < 0 ? 0x7fc00000u : r.x;
             lo.x = g_off[i] == 36 * 16 ? sc : lo.x;
             *reinterpret_cast<uint4*>(slot + g_dst[i]) = lo;
             *reinterpret_cast<uint4*>(slot + (g_dst[i] ^ 16)) = hi;

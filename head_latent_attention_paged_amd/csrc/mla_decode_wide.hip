@@ -55,7 +55,6 @@ constexpr int kRowA16 = 1088;
 __device__ __forceinline__ int swzA(int r) { return (r >> 2) & 3; }
 constexpr int kRegionB16 = kChunk * kRowA16;
 constexpr int kChunk16 = kRegionB16 + kChunk * 128;
-constexpr unsigned kNoRecord = 0xFFFFF000u;   // a record offset past every pool: its loads read zeros
 
 // kernel modes: bf16 pages (direct HBM -> LDS copies), and FP4 pages of the 512-wide rows, whose
 // rows are gathered into registers one chunk ahead and converted exactly to bf16 in the same
@@ -182,11 +181,9 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     auto xor32 = [&](float x) {
         return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_now() ^ 32) << 2, __float_as_int(x)));
     };
-    // FP4 codes and scales as raw buffers (offsets past the end read zeros)
-    const __amdgpu_buffer_rsrc_t pool = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.kv), (short)0, GATHER ? (int)(unsigned)(a.kv_rows * REC) : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t pool_sc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.kv_scale), (short)0, FP4 ? (int)(unsigned)(a.kv_rows * 32) : 0, 0x00020000);
+    // FP4 code rows and scale rows, addressed with 64-bit offsets (no limit on the cache size)
+    const char* pool = static_cast<const char*>(a.kv);
+    const char* pool_sc = static_cast<const char*>(a.kv_scale);
 
     bf16x8 qf[KS];
     f16v acc[16];
@@ -293,11 +290,14 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                 gp_n = pg_ok ? min(kChunk, t1 - tb) - 8 * wave : 0;
                 chunk_ok = (chunk_ok & ~(1u << (c & 3))) | ((pg_ok ? 1u : 0u) << (c & 3));
             }
-            const unsigned rec = rt < gp_n ? (gp_rec0 + rt) * REC : kNoRecord;
-            g_bad = (g_bad & ~(1u << i)) | ((rec >= kNoRecord ? 1u : 0u) << i);
-            gv[i] = __builtin_amdgcn_raw_buffer_load_b128(pool, rec + (unsigned)gran * 16, 0, SHARED ? 0 : 2);
-            // (kNoRecord >> 3 also lies past the end of the scales)
-            g_sc[i] = __builtin_amdgcn_raw_buffer_load_b16(pool_sc, (rec >> 3) + (unsigned)gran * 2, 0, SHARED ? 0 : 2);
+            // an unused token reads row 0 (converted to zeros below)
+            const bool bad = rt >= gp_n;
+            const size_t rec = bad ? 0 : (size_t)(gp_rec0 + rt);
+            g_bad = (g_bad & ~(1u << i)) | ((bad ? 1u : 0u) << i);
+            const u32x4* gp = reinterpret_cast<const u32x4*>(pool + rec * REC + gran * 16);
+            if constexpr (SHARED) gv[i] = *gp;
+            else gv[i] = __builtin_nontemporal_load(gp);
+            g_sc[i] = *reinterpret_cast<const unsigned short*>(pool_sc + rec * 32 + gran * 2);
         };
         // FP4: quarter w (8 values: granule 4*gran + w of the bf16 row) of load i; the block scale
         // multiplies in fp32 after an exact unit-scale conversion (the product is a bf16 value);
@@ -306,8 +306,10 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             const int ln = lane_now();
             const int cbase = (ln >> 4) * kRowA16 + (ln & 15) * 64;
             char* slot = ring + (c % DEPTH) * C::BUF + (8 * wave + 4 * i) * kRowA16 + ((w ^ ((2 * wave + i) & 3)) << 4);
-            const unsigned codes = gv[i][w];
-            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc[i] >> (8 * (w >> 1))), 0);
+            // an unused token converts to zeros (row 0's bytes, which it read, are not its own)
+            const bool none = (g_bad >> i) & 1;
+            const unsigned codes = none ? 0u : gv[i][w];
+            const float sc = none ? 0.f : __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc[i] >> (8 * (w >> 1))), 0);
             unsigned o[4];
 #define MLA_FP4_PAIR(B_)                                                              \
     {                                                                                 \

@@ -18,8 +18,6 @@ constexpr int kMaxBatchMeta = 16384;
 constexpr int kMaxRows = 4096;       // s_q * h_q limit
 constexpr int kSparseTargetItems = 256;   // work items (one per compute unit) sparse splitting aims for
 constexpr int kMaxSparseSplit = 2048;     // index entries one sparse split may hold
-// largest record pool (bytes) the row-split kernel's gathers address with 32-bit buffer offsets
-constexpr long long kRowsSparseMaxPool = 0xF0000000LL;
 
 // Wave pairs (32 query rows each) per workgroup of the large-row decode kernel, used for
 // s_q*h_q (paged) or h_q (sparse) above 16 rows: one pair (and two token streams) up to 32

@@ -205,8 +205,8 @@ mla_status_t mla_decode_paged_latent512(const void* q, const void* kcache, int64
  *
  * q, sinks, metadata, block table, lengths, causal rule, workspace size
  * (mla_workspace_size) and outputs are as for mla_decode_paged_latent512.
- * Both cache pointers must be 16-byte aligned, and num_blocks * 64 * 256
- * bytes must be at most 3.75 GiB (MLA_ERR_UNSUPPORTED beyond).
+ * Both cache pointers must be 16-byte aligned.  Rows are addressed with
+ * 64-bit offsets: the cache may fill the device.
  */
 mla_status_t mla_decode_paged_fp4(const void* q, const void* kv_codes, const void* kv_scales, int64_t num_blocks,
                                   const int32_t* block_table, int max_blocks,
@@ -229,9 +229,8 @@ mla_status_t mla_decode_paged_fp4(const void* q, const void* kv_codes, const voi
  *            bytes [580,640) unused.  Row value = e4m3(code) * scale.
  *
  * Every other argument, the workspace size and the result are as for
- * mla_decode_paged.  With s_q * h_q > 16 the cache must be at most
- * 3.75 GiB (num_blocks * 64 * 640 bytes); larger caches return
- * MLA_ERR_UNSUPPORTED.
+ * mla_decode_paged.  Records are addressed with 64-bit offsets: the cache
+ * may fill the device.
  */
 mla_status_t mla_decode_paged_fp8(const void* q, const void* kcache, int64_t num_blocks,
                                   const int32_t* block_table, int max_blocks,
@@ -263,7 +262,8 @@ size_t mla_workspace_size_sparse(int batch, int s_q, int h_q, int topk, int spli
  *            scale (little endian), bytes [580,640) unused.  Row value =
  *            e4m3(code) * scale.
  *   indices  [device] int32[batch, s_q, topk]: global token rows in
- *            [0, num_tokens), or -1 to skip.  Each entry is one term
+ *            [0, num_tokens), or -1 to skip.  Records are addressed with
+ *            64-bit offsets: the pool may fill the device.  Each entry is one term
  *            (a repeated row counts repeatedly).  There is no causal flag:
  *            the index lists carry any masking.
  *   splits   0 = mla_sparse_splits(...); otherwise topk is cut into this many

@@ -658,3 +658,84 @@ def test_full_size_sparse_prefill(env, prefill_full, quarter):
     _say("full-size config 9, query tokens %d..%d" % (toks[0], toks[-1]))
     o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale, sets=[(0, t) for t in toks])
     _whole(o[toks], l[toks], o_ref[0, toks], l_ref[0, toks], "config 9 quarter %d" % quarter)
+
+
+# ----------------------------------------------------------------- caches beyond 4 GiB
+# The gathers address records with 64-bit offsets.  Each test places the real pages or records
+# of a small input past the first 4 GiB of a zero-filled device pool (so a 32-bit offset would
+# wrap) and compares with the oracle on the small input.
+def _big_pool(torch, dev, shape, dtype, small, first):
+    """A zero device pool of `shape` with host array `small` copied in at rows first.. ."""
+    pool = torch.zeros(shape, dtype=dtype, device=dev)
+    src = torch.from_numpy(np.ascontiguousarray(small))
+    if dtype == torch.bfloat16:
+        src = src.view(torch.int16).view(torch.bfloat16)
+    pool[first:first + small.shape[0]] = src.to(dev)
+    return pool
+
+
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (32, 2), (64, 1)])
+def test_paged_fp8_cache_beyond_4gib(env, h_q, s_q):
+    import torch
+
+    mla, dev = env
+    _say("fp8 pages beyond 4 GiB", h_q, s_q)
+    inp = make_paged_fp8(2, s_q, h_q, [700, 130], s_q > 1, seed=980 + h_q, poison=True)
+    first = 105000                                   # 105000 pages x 40 KiB = 4.3 GB
+    kc = _big_pool(torch, dev, (first + inp.num_pages + 8, 64, 640), torch.uint8, inp.kcache, first)
+    assert kc.numel() > (1 << 32)
+    q, bt, sl = dev_bf16(inp.q, dev), dev_i32(inp.block_table + first, dev), dev_i32(inp.seqlens, dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, 5)
+    out, lse = mla.decode_paged(q, kc, bt, sl, meta, inp.softmax_scale, inp.causal)
+    torch.cuda.synchronize()
+    o, l = to_host(out, lse)
+    del kc
+    torch.cuda.empty_cache()
+    o_ref, l_ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale,
+                                    inp.causal)
+    check_parity(o, l, o_ref, l_ref, "fp8 pages beyond 4 GiB h_q %d" % h_q)
+
+
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_paged_fp4_cache_beyond_4gib(env, h_q):
+    import torch
+
+    mla, dev = env
+    _say("FP4 pages beyond 4 GiB", h_q)
+    inp = make_paged_fp4(2, 6, h_q, [700, 130], True, seed=985 + h_q, poison=True, sinks=True)
+    first = 262200                                   # 262200 pages x 16 KiB of codes = 4.3 GB
+    n = first + inp.num_pages + 8
+    codes = _big_pool(torch, dev, (n, 64, 256), torch.uint8, inp.kv_codes, first)
+    scales = _big_pool(torch, dev, (n, 64, 32), torch.uint8, inp.kv_scales, first)
+    assert codes.numel() > (1 << 32)
+    q, bt, sl = dev_bf16(inp.q, dev), dev_i32(inp.block_table + first, dev), dev_i32(inp.seqlens, dev)
+    sk = torch.from_numpy(inp.sinks).to(dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, 5)
+    out, lse = mla.decode_paged_fp4(q, codes, scales, bt, sl, meta, inp.softmax_scale, True, sinks=sk)
+    torch.cuda.synchronize()
+    o, l = to_host(out, lse)
+    del codes, scales
+    torch.cuda.empty_cache()
+    o_ref, l_ref = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                                    inp.softmax_scale, True, sinks=inp.sinks)
+    check_parity(o, l, o_ref, l_ref, "FP4 pages beyond 4 GiB h_q %d" % h_q)
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+def test_sparse_pool_beyond_4gib(env, h_q):
+    import torch
+
+    mla, dev = env
+    _say("sparse pool beyond 4 GiB", h_q)
+    inp = make_sparse(2, 2, h_q, 3000, 1500, 0.1, seed=990 + h_q)
+    first = 6800000                                  # 6.8 M records x 640 B = 4.35 GB
+    kv = _big_pool(torch, dev, (first + inp.num_tokens + 8, 640), torch.uint8, inp.kv, first)
+    assert kv.numel() > (1 << 32)
+    idx = np.where(inp.indices >= 0, inp.indices + first, -1).astype(np.int32)
+    out, lse = mla.decode_sparse(dev_bf16(inp.q, dev), kv, dev_i32(idx, dev), inp.softmax_scale)
+    torch.cuda.synchronize()
+    o, l = to_host(out, lse)
+    del kv
+    torch.cuda.empty_cache()
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+    check_parity(o, l, o_ref, l_ref, "sparse pool beyond 4 GiB h_q %d" % h_q)

@@ -103,14 +103,12 @@ def test_paged_noalloc_validation_before_launch(mla):
 
 
 def test_paged_fp8_validation_before_launch(mla):
-    # the same host checks as the bf16 call, plus the 32-bit offset limit of the many-row path
+    # the same host checks as the bf16 call
     assert _paged_call(mla, fp8=True, kc=None) == mla.MLA_ERR_INVALID_ARG
     assert _paged_call(mla, fp8=True, nb=0) == mla.MLA_ERR_INVALID_ARG
     assert _paged_call(mla, fp8=True, scale=float("inf")) == mla.MLA_ERR_INVALID_ARG
     assert _paged_call(mla, fp8=True, wsb=100) == mla.MLA_ERR_WORKSPACE
     assert _paged_call(mla, fp8=True, s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
-    # more than 16 rows over a cache beyond 3.75 GiB (100000 pages x 40 KiB)
-    assert _paged_call(mla, fp8=True, h_q=64, nb=100000) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_paged_latent512_validation_before_launch(mla):
@@ -152,8 +150,6 @@ def test_paged_fp4_validation_before_launch(mla):
     assert call(nb=0) == mla.MLA_ERR_INVALID_ARG
     assert call(s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
     assert call(wsb=100) == mla.MLA_ERR_WORKSPACE
-    # codes beyond 3.75 GiB (245761 pages x 16 KiB)
-    assert call(nb=245761) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_sparse_validation_before_launch(mla):
