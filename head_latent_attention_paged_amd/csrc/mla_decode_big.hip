@@ -39,8 +39,8 @@ constexpr int kPF = MLA_BIG_PF;   // LDS fragment prefetch distance (MFMA steps)
 // The softmax reference of a row is the first finite chunk maximum it sees and never moves
 // inside a pass, so the accumulators are touched only by MFMAs.  p = 2^(s - m) <= 2^kRefSlack
 // keeps bf16 P and the fp32 sums finite; a row whose scores outgrow the reference by more
-// (scores spanning over 44 nats) makes the workgroup restart the segment with the larger
-// reference.
+// (scores spanning over 44 nats) makes the workgroup finish the pass and run it again with each
+// row's maximum over the whole segment as reference: at most two passes.
 constexpr float kRefSlack = 64.f;
 // LDS layouts, chosen by measuring the kernels' read patterns on gfx950 (64 banks): bf16 region A
 // holds dims 0..511 of a row in 1 KB at a 1056-byte row stride, unswizzled, which keeps both the
@@ -164,6 +164,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
     bf16x8 qf[2][18];
     f4 acc[16][2];
     float m_run[2], l_run[2];
+    float m_lane[2];   // largest score this lane has seen in the pass (a restart's reference)
 
     auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
         const int nch = ceil_div(t1 - t0, kChunk);
@@ -364,6 +365,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
                     const float f = SPARSE ? a.scale_log2 * S.tsc[i] : a.scale_log2;
                     S.s[n][i] = valid ? S.s[n][i] * f : -INFINITY;
                     S.outgrown = S.outgrown || (m_run[n] != -INFINITY && S.s[n][i] > cap);
+                    m_lane[n] = fmaxf(m_lane[n], S.s[n][i]);
                 }
             }
         };
@@ -435,10 +437,14 @@ void mla_decode_big_kernel(const AttnArgs a) {
         };
         auto no_side = [](int) {};
 
-        // ---- passes over the segment (a second one only after a restart vote)
-        for (;;) {
+        // ---- passes over the segment (a second one only after a restart vote).  A vote does not
+        // end the pass early: the pass runs to its end (its results are discarded), so m_lane sees
+        // every score of the segment and the second pass, whose reference is that maximum,
+        // cannot vote.
+        for (int pass = 0;; ++pass) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
+                m_lane[n] = -INFINITY;
                 l_run[n] = 0.f;
 #pragma unroll
                 for (int dt = 0; dt < 16; ++dt) acc[dt][n] = f4{0.f, 0.f, 0.f, 0.f};
@@ -491,10 +497,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
                         if (ks == 10) prob_step(5, S, P);
                     });
                     __syncthreads();               // P^T halves and votes of chunk k-1 visible
-                    if (any_vote()) {
-                        restart = true;
-                        break;
-                    }
+                    restart = restart || any_vote();
                     bf16x8 pT[2];
                     p_operands(P, pT);
                     // O^T += V^T P^T (k-1) on the MFMAs while S^T(k) is masked
@@ -503,15 +506,14 @@ void mla_decode_big_kernel(const AttnArgs a) {
                     });
                     if (S.need_max) max_to_lds(S);
                 }
-                if (!restart) {
+                {
                     __syncthreads();               // maxima of the last chunk visible
                     Probs P;
 #pragma unroll
                     for (int step = 0; step < 6; ++step) prob_step(step, S, P);
                     __syncthreads();
-                    if (any_vote()) {
-                        restart = true;
-                    } else {
+                    restart = restart || any_vote();
+                    if (!restart) {
                         bf16x8 pT[2];
                         p_operands(P, pT);
                         pv(nch - 1, pT, no_side);
@@ -544,10 +546,7 @@ void mla_decode_big_kernel(const AttnArgs a) {
 #pragma unroll
                     for (int step = 0; step < 6; ++step) prob_step(step, S, P);
                     __syncthreads();
-                    if (any_vote()) {
-                        restart = true;
-                        break;
-                    }
+                    restart = restart || any_vote();
                     bf16x8 pT[2];
                     p_operands(P, pT);
                     pv(k, pT, no_side);
@@ -555,9 +554,15 @@ void mla_decode_big_kernel(const AttnArgs a) {
             }
             // the copies past the segment's end (or those in flight at a restart) land first
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (!restart) break;
-            // start over with each row's largest maximum so far (S holds the chunk that voted)
-            max_to_lds(S);
+            // (the second pass cannot vote; the bound on the passes is a guard)
+            if (!restart || pass == 1) break;
+            // start over with each row's maximum over the whole pass as reference
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                S.mx[n] = fmaxf(m_lane[n], __shfl_xor(m_lane[n], 16));
+                S.mx[n] = fmaxf(S.mx[n], __shfl_xor(S.mx[n], 32));
+                *(g4 == 0 ? &xch[(wave * 2 + n) * 16 + l16] : my_sink) = S.mx[n];
+            }
             __syncthreads();
             pair_max(S);
 #pragma unroll

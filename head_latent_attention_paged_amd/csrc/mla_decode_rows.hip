@@ -498,7 +498,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // ---- passes over the segment (a second one only after a restart vote).  A vote does not
         // leave the chunk loop early: the pass runs to its end (its results are discarded), so
         // the loop has a single exit and m_lane sees every score of the segment.
-        for (;;) {
+        for (int pass = 0;; ++pass) {
             l_run = 0.f;
             m_lane = -INFINITY;
 #pragma unroll
@@ -598,7 +598,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             }
             // the copies past the segment's end land first
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (!restart) break;
+            // (the second pass, whose reference is the segment maximum, cannot vote; the bound on
+            // the passes is a guard)
+            if (!restart || pass == 1) break;
             // run the pass again with each row's maximum over the segment (both tiles) as reference
             float mx = m_lane;
             mx = fmaxf(mx, __shfl_xor(mx, 16));
