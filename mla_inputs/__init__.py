@@ -11,4 +11,5 @@ from .gen import (  # noqa: F401
     PagedInputs, PagedFp8Inputs, PagedFp4Inputs, SparseInputs,
     bf16_bits_from_f32, bf16_bits_to_f32, quantize_rows_nvfp4,
     make_paged, make_paged_fp8, make_paged_fp4, make_sparse, make_config, config_info, CONFIGS,
+    FusedExtras, make_fused_extras, rope_angles,
 )

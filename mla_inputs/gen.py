@@ -359,6 +359,40 @@ def make_paged_fp4(batch: int, s_q: int, h_q: int,
 
 
 # --------------------------------------------------------------------------
+# Fused-decode inputs (Q-norm weight, RoPE angles) on the V4 geometry
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class FusedExtras:
+    norm_weight: np.ndarray      # fp32 [512]: the query RMS-norm weight, shared by the heads
+    norm_eps: float              # an fp32 value
+    rope_cs: np.ndarray          # fp32 [batch, s_q, 64]: cos(theta_i) for i < 32, then sin(theta_i)
+    positions: np.ndarray        # int64 [batch, s_q]: the query tokens' positions (L - s_q + s)
+
+
+ROPE_BASE = 10000.0
+
+
+def rope_angles(positions: np.ndarray, base: float = ROPE_BASE) -> np.ndarray:
+    """cos/sin [..., 64] (fp32) of the rotary angles pos * base^(-2i/64), i < 32, for integer
+    positions: the per-token angle table a caller hands to the fused decode."""
+    pos = np.asarray(positions, dtype=np.float64)[..., None]
+    inv_freq = base ** (-np.arange(0, 64, 2, dtype=np.float64) / 64.0)
+    ang = pos * inv_freq
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+def make_fused_extras(inp, seed: int, eps: float = 1e-6) -> FusedExtras:
+    """The fused decode's extra inputs for a V4-geometry input set (bf16 or FP4 pages): a norm
+    weight 1 + 0.1 N(0,1) (fp32) and the angles of the query tokens, which are the last s_q
+    tokens of each sequence (position L - s_q + s, at least 0)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = (1.0 + 0.1 * rng.standard_normal(D_V)).astype(np.float32)
+    L = inp.seqlens.astype(np.int64)
+    pos = np.maximum(L[:, None] - inp.s_q + np.arange(inp.s_q)[None, :], 0)
+    return FusedExtras(norm_weight=w, norm_eps=_fp32(eps), rope_cs=rope_angles(pos), positions=pos)
+
+
+# --------------------------------------------------------------------------
 # Sparse fp8 inputs
 # --------------------------------------------------------------------------
 @dataclasses.dataclass
@@ -467,6 +501,10 @@ CONFIGS = {
     # token with its own 2048-entry index list in its causal window
     9: dict(kind="sparse_prefill", name="sparse fp8 prefill: s_q=4096 h_q=128 topk=2048 context=32768",
             batch=1, s_q=4096, h_q=128, tokens_per_seq=32768, topk=2048, p_invalid=0.0),
+    # the fused decode (query RMS norm, RoPE, attention, conjugate RoPE on the output, FP8 cast)
+    # on the V4 geometry, over bf16 pages
+    10: dict(kind="fused_v4", name="fused norm-RoPE-attn-RoPE-FP8 decode: b=64 s_q=6 causal h_q=64 L=4096 d=512 + sinks",
+             batch=64, s_q=6, h_q=64, seqlens=[4096] * 64, causal=True),
 }
 
 
@@ -475,7 +513,7 @@ def config_info(k: int) -> dict:
 
 
 def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
-    """Inputs for workload ``k`` (1..9) with seed 1000 + k unless given."""
+    """Inputs for workload ``k`` (1..10) with seed 1000 + k unless given."""
     c = CONFIGS[k]
     seed = 1000 + k if seed is None else seed
     if c["kind"] == "paged":
@@ -488,4 +526,9 @@ def make_config(k: int, seed: Optional[int] = None, poison: bool = True):
     if c["kind"] == "paged_v4_fp4":
         return make_paged_fp4(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison,
                               sinks=True)
+    if c["kind"] == "fused_v4":
+        inp = make_paged(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["causal"], seed, poison=poison,
+                         d_qk=D_V, sinks=True)
+        inp.fused = make_fused_extras(inp, seed + 500)
+        return inp
     return make_sparse(c["batch"], c["s_q"], c["h_q"], c["tokens_per_seq"], c["topk"], c["p_invalid"], seed)

@@ -324,3 +324,108 @@ def lse_combine(parts_o: np.ndarray, parts_lse: np.ndarray) -> Tuple[np.ndarray,
     o = np.where(tot[:, None] > 0, (w[:, :, None] * parts_o).sum(axis=0) / np.where(tot > 0, tot, 1.0)[:, None], 0.0)
     lse = np.where(tot > 0, safe_mu + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# Fused decode: Q-norm, RoPE, attention, conjugate RoPE on the output, FP8 cast
+# ("deepseek-ai/FlashMLA" project summary, 개요 bullet 3 and 사용 방법 step 5: one kernel merges
+# the query norm, rotary position encoding, the attention, the conjugate rotary encoding on the
+# output side and the final cast to FP8 for the FP8 einsum that follows).  The pages name the
+# stages only; the readings taken here:
+#   * the geometry is the DeepSeek-V4 decode one: a 512-wide latent row per token that is both K
+#     and V, whose last 64 dims carry the rotary encoding of the token's position;
+#   * Q-norm is an RMS norm over each head's 512 query dims with one weight vector shared by the
+#     heads: q * weight / sqrt(mean(q^2) + eps);
+#   * RoPE rotates the interleaved pairs (448 + 2i, 449 + 2i), i < 32, by the query token's angle
+#     theta_i, given as cos/sin per query token; the conjugate RoPE rotates the same pairs of the
+#     attention output by -theta_i of the same token, which turns the cached rows' absolute
+#     rotations into rotations relative to the query;
+#   * the cast writes OCP E4M3FN codes with one fp32 scale per (token, head) row:
+#     scale = max(amax, 2^-126) / 448, code = round-to-nearest-even of x / scale (in fp32).
+# --------------------------------------------------------------------------
+ROPE_DIMS = 64
+ROPE_START = D_V - ROPE_DIMS
+E4M3_MAX = 448.0
+
+
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """x [..., D] float64 -> x * weight / sqrt(mean(x^2) + eps) over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x * np.asarray(weight, dtype=np.float64) / np.sqrt(ms + float(eps))
+
+
+def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, sign: float = 1.0) -> np.ndarray:
+    """Rotate the interleaved pairs (448 + 2i, 449 + 2i) of the last axis of x [..., 512] by the
+    angle whose cosine and sine are cos[..., i], sin[..., i] (i < 32; sign = -1: by minus the
+    angle, the conjugate rotation).  Other dims are unchanged."""
+    x = np.array(x, dtype=np.float64)
+    c = np.asarray(cos, dtype=np.float64)
+    s = sign * np.asarray(sin, dtype=np.float64)
+    a = x[..., ROPE_START::2].copy()
+    b = x[..., ROPE_START + 1::2].copy()
+    x[..., ROPE_START::2] = a * c - b * s
+    x[..., ROPE_START + 1::2] = a * s + b * c
+    return x
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN codes of x (float32 values): round to the nearest finite E4M3 value, ties to
+    the even code, the sign bit kept (negative values that round to zero give -0); magnitudes
+    beyond 448 saturate to 448 (the cast's inputs lie within it)."""
+    x = np.asarray(x, dtype=np.float64)
+    pos = E4M3_TABLE[:0x7F]                          # codes 0x00..0x7E: 0 .. 448, increasing
+    mag = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - pos[lo]
+    d_hi = pos[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def fp8_cast_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row FP8 cast of x [..., 512]: (codes uint8 [..., 512], scale float32 [...]) with
+    scale = fp32(max(amax, 2^-126) / 448) and code = e4m3_encode(fp32(fp32(x) / scale))."""
+    xf = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.abs(xf).max(axis=-1)
+    scale = (np.maximum(amax, np.float32(2.0 ** -126)) / np.float32(E4M3_MAX)).astype(np.float32)
+    y = (xf / scale[..., None]).astype(np.float32)
+    return e4m3_encode(y), scale
+
+
+def fused_decode(q_bits: np.ndarray, norm_weight: np.ndarray, norm_eps: float, rope_cs: np.ndarray,
+                 rows_of, block_table: np.ndarray, seqlens: np.ndarray, softmax_scale: float,
+                 causal: bool, sinks: Optional[np.ndarray] = None):
+    """The fused decode on the DeepSeek-V4 geometry.
+
+    q_bits [B, s_q, h_q, 512] bf16 bits: the query before its norm and rotation;
+    norm_weight [512] fp32; rope_cs [B, s_q, 64] fp32: cos(theta_i) for i < 32, then sin(theta_i),
+    of each query token; rows_of(b, L) -> the float64 [L, 512] rows of sequence b's first L tokens
+    (bf16 or FP4 pages, gathered through the block table); sinks [h_q] or None.
+    Steps: q' = RoPE(RMSNorm(q)); O, LSE = attention of q' over the visible rows (the paged
+    definition, causal rule and sinks included); O' = conjugate RoPE(O); codes, scale = the FP8
+    cast of O'.  Returns (codes uint8 [B, s_q, h_q, 512], scale fp32 [B, s_q, h_q],
+    LSE float64 [B, s_q, h_q], O' float64 [B, s_q, h_q, 512]).
+    """
+    B, s_q, h_q, _ = q_bits.shape
+    sigma = float(np.float32(softmax_scale))
+    w = np.asarray(norm_weight, dtype=np.float32).astype(np.float64)
+    eps = float(np.float32(norm_eps))
+    sk = None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
+    cs = np.asarray(rope_cs, dtype=np.float32).astype(np.float64)
+    O = np.zeros((B, s_q, h_q, D_V))
+    LSE = np.zeros((B, s_q, h_q))
+    for b in range(B):
+        L = int(seqlens[b])
+        rows = rows_of(b, L)
+        for s in range(s_q):
+            n = visible_count(L, s_q, s, causal)
+            cos, sin = cs[b, s, :ROPE_DIMS // 2], cs[b, s, ROPE_DIMS // 2:]
+            q = rope_rotate(rms_norm(bf16_to_f64(q_bits[b, s]), w, eps), cos, sin)
+            o, lse = attend(q, rows[:n], sigma, sk)
+            O[b, s] = rope_rotate(o, cos, sin, sign=-1.0)
+            LSE[b, s] = lse
+    codes, scale = fp8_cast_rows(O)
+    return codes, scale, LSE, O

@@ -72,7 +72,9 @@ def test_sparse_generator_indices():
 
 
 def test_config_table():
-    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7, 8, 9}
+    assert set(CONFIGS) == {1, 2, 3, 4, 5, 6, 7, 8, 9, 10}
+    assert CONFIGS[10]["kind"] == "fused_v4"
+    assert all(CONFIGS[10][k] == CONFIGS[7][k] for k in ("batch", "s_q", "h_q", "seqlens", "causal"))
     assert CONFIGS[9]["kind"] == "sparse_prefill" and CONFIGS[9]["batch"] == 1
     assert CONFIGS[2]["batch"] == 128 and CONFIGS[4]["seqlens"][0] == 65536
     assert CONFIGS[5]["topk"] == 2048

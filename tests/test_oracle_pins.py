@@ -517,3 +517,151 @@ def test_visible_count():
     assert [visible_count(10, 3, s, True) for s in range(3)] == [8, 9, 10]
     assert [visible_count(1, 3, s, True) for s in range(3)] == [0, 0, 1]
     assert visible_count(0, 2, 1, False) == 0
+
+
+# ----------------------------------------------------------------- fused decode: norm, RoPE, FP8 cast
+from mla_inputs import make_fused_extras, rope_angles  # noqa: E402
+from oracle import e4m3_encode, fp8_cast_rows, fused_decode, gather_paged_rows, rms_norm, rope_rotate  # noqa: E402
+
+
+def test_rms_norm_closed_forms():
+    """Unit weight: the output's mean square is ms / (ms + eps); eps = 0 makes it scale-free and
+    of unit RMS; the weight multiplies element by element."""
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((5, 512)) * rng.uniform(0.1, 10.0, size=(5, 1))
+    ms = np.mean(x * x, axis=-1)
+    y = rms_norm(x, np.ones(512), 1e-3)
+    assert np.allclose(np.mean(y * y, axis=-1), ms / (ms + 1e-3), rtol=1e-13)
+    y0 = rms_norm(x, np.ones(512), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y0 * y0, axis=-1)), 1.0, rtol=1e-14)
+    assert np.allclose(rms_norm(7.5 * x, np.ones(512), 0.0), y0, rtol=1e-13)
+    w = rng.standard_normal(512)
+    assert np.allclose(rms_norm(x, w, 1e-3), y * w, rtol=1e-13, atol=1e-15)
+
+
+def test_rope_rotation_conventions():
+    """Angle 0 is the identity; a quarter turn maps each pair (a, b) of dims (448 + 2i, 449 + 2i)
+    to (-b, a) and leaves dims below 448 alone; rotations keep pair norms; the conjugate rotation
+    undoes the rotation."""
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((3, 512))
+    assert np.array_equal(rope_rotate(x, np.ones(32), np.zeros(32)), x)
+    y = rope_rotate(x, np.zeros(32), np.ones(32))
+    assert np.array_equal(y[:, :448], x[:, :448])
+    assert np.array_equal(y[:, 448::2], -x[:, 449::2]) and np.array_equal(y[:, 449::2], x[:, 448::2])
+    th = rng.uniform(-math.pi, math.pi, size=(3, 32))
+    z = rope_rotate(x, np.cos(th), np.sin(th))
+    n0 = x[:, 448::2] ** 2 + x[:, 449::2] ** 2
+    assert np.allclose(z[:, 448::2] ** 2 + z[:, 449::2] ** 2, n0, rtol=1e-13)
+    assert np.allclose(rope_rotate(z, np.cos(th), np.sin(th), sign=-1.0), x, rtol=0, atol=1e-13)
+
+
+def test_rope_angle_table():
+    """The angle table: position 0 is the identity, pair 0 turns by exactly the position (base^0),
+    the last pair by position * base^(-62/64)."""
+    cs = rope_angles(np.array([0, 5]))
+    assert np.array_equal(cs[0, :32], np.ones(32, dtype=np.float32)) and np.all(cs[0, 32:] == 0)
+    assert cs[1, 0] == np.float32(math.cos(5.0)) and cs[1, 32] == np.float32(math.sin(5.0))
+    a31 = 5.0 * 10000.0 ** (-62.0 / 64.0)
+    assert cs[1, 31] == np.float32(math.cos(a31)) and cs[1, 63] == np.float32(math.sin(a31))
+
+
+def test_e4m3_encode_matches_torch_and_rounds_ties_to_even():
+    """Every finite E4M3 value encodes to its own code (library special case: torch's
+    float8_e4m3fn cast); midpoints between neighbours go to the even code; 448 is the largest."""
+    finite = np.array([c for c in range(256) if np.isfinite(E4M3_TABLE[c])])
+    vals = E4M3_TABLE[finite].astype(np.float32)
+    enc = e4m3_encode(vals)
+    zero = vals == 0
+    assert np.array_equal(enc[~zero], finite[~zero].astype(np.uint8))
+    rng = np.random.default_rng(62)
+    x = np.clip(np.concatenate([rng.standard_normal(20000) * 60.0, rng.standard_normal(20000) * 0.02]),
+                -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(e4m3_encode(x), ref)
+    # 1.0625 lies between 1.0 (0x38) and 1.125 (0x39): even 0x38; 1.1875 between 0x39 and 0x3A: 0x3A
+    assert list(e4m3_encode(np.array([1.0625, 1.1875, -1.0625, 448.0], dtype=np.float32))) == [0x38, 0x3A, 0xB8, 0x7E]
+
+
+def test_fp8_row_cast_bounds():
+    """The row's largest magnitude becomes +-448 exactly; every value is within half an E4M3 step
+    of code * scale; an all-zero row gets the smallest scale and zero codes."""
+    rng = np.random.default_rng(63)
+    x = rng.standard_normal((6, 512)) * rng.uniform(1e-3, 1e3, size=(6, 1))
+    x[5] = 0.0
+    codes, scale = fp8_cast_rows(x)
+    deq = E4M3_TABLE[codes] * scale[:, None].astype(np.float64)
+    for r in range(5):
+        j = np.argmax(np.abs(x[r]))
+        assert codes[r, j] & 0x7F == 0x7E
+        y = np.abs(x[r] / scale[r])
+        step = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3), 2.0 ** -9)
+        assert np.all(np.abs(deq[r] - x[r]) <= 0.5 * step * scale[r] * (1 + 1e-6) + 1e-30)
+    assert scale[5] == np.float32(np.float32(2.0 ** -126) / np.float32(448.0)) and np.all(codes[5] == 0)
+
+
+def _fused_paged(inp, fx, sinks=None):
+    rows_of = lambda b, L: gather_paged_rows(inp.kcache, inp.block_table[b], L)  # noqa: E731
+    return fused_decode(inp.q, fx.norm_weight, fx.norm_eps, fx.rope_cs, rows_of, inp.block_table,
+                        inp.seqlens, inp.softmax_scale, inp.causal, sinks=sinks)
+
+
+def test_fused_single_token_is_the_counter_rotated_row():
+    """One cached token: the attention output is that row, so the fused output before the cast is
+    the row turned back by the query's angle, and the LSE is the score of the normed, rotated
+    query (with unit norm weight and angle 0: the plain normed query's score)."""
+    inp = make_paged(1, 1, 16, [1], False, seed=64, d_qk=512)
+    fx = make_fused_extras(inp, 65)
+    codes, scale, lse, O = _fused_paged(inp, fx)
+    row = bf16_to_f64(inp.kcache[inp.block_table[0, 0], 0, 0])
+    cos, sin = fx.rope_cs[0, 0, :32].astype(np.float64), fx.rope_cs[0, 0, 32:].astype(np.float64)
+    assert np.allclose(O[0, 0], rope_rotate(np.tile(row, (16, 1)), cos, sin, sign=-1.0), rtol=0, atol=1e-14)
+    fx.norm_weight[:] = 1.0
+    fx.rope_cs[..., :32] = 1.0
+    fx.rope_cs[..., 32:] = 0.0
+    _, _, lse1, _ = _fused_paged(inp, fx)
+    q = bf16_to_f64(inp.q[0, 0])
+    qn = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + float(np.float32(1e-6)))
+    assert np.allclose(lse1[0, 0], SIGMA_512 * qn @ row, rtol=1e-12, atol=1e-13)
+
+
+SIGMA_512 = float(np.float32(512 ** -0.5))
+
+
+def test_fused_output_depends_only_on_relative_positions():
+    """Cached rows whose last 64 dims are rotated by their token positions and queries rotated by
+    their own positions: moving every position by the same offset leaves the fused output (before
+    the cast) and the LSE unchanged (up to the fp32 rounding of the angle table), while the
+    attention output before the conjugate rotation moves.  A wrong sign or a missing rotation on
+    either side breaks this."""
+    rng = np.random.default_rng(66)
+    T, s_q, h_q = 150, 2, 8
+    base_rows = rng.standard_normal((T, 512))
+    inp = make_paged(1, s_q, h_q, [T], True, seed=67, d_qk=512)
+    fx = make_fused_extras(inp, 68)
+
+    def run(offset):
+        cs_k = rope_angles(offset + np.arange(T)).astype(np.float64)
+        rot = rope_rotate(base_rows, cs_k[:, :32], cs_k[:, 32:])     # exact rows, no bf16 storage
+        fx.rope_cs = rope_angles(offset + T - s_q + np.arange(s_q))[None]
+        _, _, lse, O = fused_decode(inp.q, fx.norm_weight, fx.norm_eps, fx.rope_cs, lambda b, L: rot[:L],
+                                    inp.block_table, inp.seqlens, inp.softmax_scale, True)
+        cs_q = fx.rope_cs.astype(np.float64)[0][:, None, :]
+        plain = rope_rotate(O[0], cs_q[..., :32], cs_q[..., 32:])  # the attention output itself
+        return O, lse, plain
+
+    O0, l0, p0 = run(0)
+    O1, l1, p1 = run(1000)
+    assert np.allclose(O0, O1, rtol=0, atol=1e-6) and np.allclose(l0, l1, rtol=0, atol=1e-6)
+    assert np.abs(p0 - p1)[..., 448:].max() > 1e-2
+
+
+def _one_seq_cache_512(rows_f32):
+    T = rows_f32.shape[0]
+    nblk = max(1, -(-T // 64))
+    kc = np.zeros((nblk, 64, 1, 512), dtype=np.uint16)
+    bits = _bf16(rows_f32)
+    for j in range(nblk):
+        n = min(64, T - 64 * j)
+        kc[j, :n, 0, :] = bits[64 * j:64 * j + n]
+    return kc, np.arange(nblk, dtype=np.int32)
