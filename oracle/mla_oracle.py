@@ -341,7 +341,9 @@ def lse_combine(parts_o: np.ndarray, parts_lse: np.ndarray) -> Tuple[np.ndarray,
 #     attention output by -theta_i of the same token, which turns the cached rows' absolute
 #     rotations into rotations relative to the query;
 #   * the cast writes OCP E4M3FN codes with one fp32 scale per (token, head) row:
-#     scale = max(amax, 2^-126) / 448, code = round-to-nearest-even of x / scale (in fp32).
+#     scale = max(amax, 2^-126) / 448, code = round-to-nearest-even of x / scale (in fp32);
+#   * the attention takes its query as a bf16 operand, as every query the decode calls take: the
+#     normed, rotated query is rounded to bf16 (nearest even) before it scores the rows.
 # --------------------------------------------------------------------------
 ROPE_DIMS = 64
 ROPE_START = D_V - ROPE_DIMS
@@ -395,18 +397,26 @@ def fp8_cast_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return e4m3_encode(y), scale
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to the nearest bf16 value (ties to even), via fp32: a bf16 is the top half of an
+    fp32, so the low 16 bits are rounded away."""
+    bits = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16 << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def fused_decode(q_bits: np.ndarray, norm_weight: np.ndarray, norm_eps: float, rope_cs: np.ndarray,
                  rows_of, block_table: np.ndarray, seqlens: np.ndarray, softmax_scale: float,
-                 causal: bool, sinks: Optional[np.ndarray] = None):
+                 causal: bool, sinks: Optional[np.ndarray] = None, round_query: bool = True):
     """The fused decode on the DeepSeek-V4 geometry.
 
     q_bits [B, s_q, h_q, 512] bf16 bits: the query before its norm and rotation;
     norm_weight [512] fp32; rope_cs [B, s_q, 64] fp32: cos(theta_i) for i < 32, then sin(theta_i),
     of each query token; rows_of(b, L) -> the float64 [L, 512] rows of sequence b's first L tokens
     (bf16 or FP4 pages, gathered through the block table); sinks [h_q] or None.
-    Steps: q' = RoPE(RMSNorm(q)); O, LSE = attention of q' over the visible rows (the paged
-    definition, causal rule and sinks included); O' = conjugate RoPE(O); codes, scale = the FP8
-    cast of O'.  Returns (codes uint8 [B, s_q, h_q, 512], scale fp32 [B, s_q, h_q],
+    Steps: q' = RoPE(RMSNorm(q)), rounded to bf16 (round_query); O, LSE = attention of q' over
+    the visible rows (the paged definition, causal rule and sinks included); O' = conjugate
+    RoPE(O); codes, scale = the FP8 cast of O'.  Returns (codes uint8 [B, s_q, h_q, 512], scale fp32 [B, s_q, h_q],
     LSE float64 [B, s_q, h_q], O' float64 [B, s_q, h_q, 512]).
     """
     B, s_q, h_q, _ = q_bits.shape
@@ -424,6 +434,8 @@ def fused_decode(q_bits: np.ndarray, norm_weight: np.ndarray, norm_eps: float, r
             n = visible_count(L, s_q, s, causal)
             cos, sin = cs[b, s, :ROPE_DIMS // 2], cs[b, s, ROPE_DIMS // 2:]
             q = rope_rotate(rms_norm(bf16_to_f64(q_bits[b, s]), w, eps), cos, sin)
+            if round_query:
+                q = round_bf16(q)
             o, lse = attend(q, rows[:n], sigma, sk)
             O[b, s] = rope_rotate(o, cos, sin, sign=-1.0)
             LSE[b, s] = lse

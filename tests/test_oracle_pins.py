@@ -521,7 +521,19 @@ def test_visible_count():
 
 # ----------------------------------------------------------------- fused decode: norm, RoPE, FP8 cast
 from mla_inputs import make_fused_extras, rope_angles  # noqa: E402
-from oracle import e4m3_encode, fp8_cast_rows, fused_decode, gather_paged_rows, rms_norm, rope_rotate  # noqa: E402
+from oracle import (e4m3_encode, fp8_cast_rows, fused_decode, gather_paged_rows, rms_norm, rope_rotate,  # noqa: E402
+                    round_bf16)
+
+
+def test_round_bf16_matches_torch_and_ties_to_even():
+    """Library special case: torch's float32 -> bfloat16 cast (nearest, ties to even); every bf16
+    value is its own rounding; 1 + 2^-8 (a tie) goes to 1, 1 + 3 * 2^-8 to 1 + 2^-6."""
+    rng = np.random.default_rng(69)
+    x = np.concatenate([rng.standard_normal(50000) * 10.0, rng.standard_normal(50000) * 1e-3]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_bf16(x), ref)
+    assert np.array_equal(round_bf16(ref), ref)
+    assert list(round_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]))) == [1.0, 1 + 2.0 ** -6]
 
 
 def test_rms_norm_closed_forms():
@@ -600,10 +612,10 @@ def test_fp8_row_cast_bounds():
     assert scale[5] == np.float32(np.float32(2.0 ** -126) / np.float32(448.0)) and np.all(codes[5] == 0)
 
 
-def _fused_paged(inp, fx, sinks=None):
+def _fused_paged(inp, fx, sinks=None, round_query=True):
     rows_of = lambda b, L: gather_paged_rows(inp.kcache, inp.block_table[b], L)  # noqa: E731
     return fused_decode(inp.q, fx.norm_weight, fx.norm_eps, fx.rope_cs, rows_of, inp.block_table,
-                        inp.seqlens, inp.softmax_scale, inp.causal, sinks=sinks)
+                        inp.seqlens, inp.softmax_scale, inp.causal, sinks=sinks, round_query=round_query)
 
 
 def test_fused_single_token_is_the_counter_rotated_row():
@@ -619,7 +631,7 @@ def test_fused_single_token_is_the_counter_rotated_row():
     fx.norm_weight[:] = 1.0
     fx.rope_cs[..., :32] = 1.0
     fx.rope_cs[..., 32:] = 0.0
-    _, _, lse1, _ = _fused_paged(inp, fx)
+    _, _, lse1, _ = _fused_paged(inp, fx, round_query=False)
     q = bf16_to_f64(inp.q[0, 0])
     qn = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + float(np.float32(1e-6)))
     assert np.allclose(lse1[0, 0], SIGMA_512 * qn @ row, rtol=1e-12, atol=1e-13)
@@ -645,7 +657,7 @@ def test_fused_output_depends_only_on_relative_positions():
         rot = rope_rotate(base_rows, cs_k[:, :32], cs_k[:, 32:])     # exact rows, no bf16 storage
         fx.rope_cs = rope_angles(offset + T - s_q + np.arange(s_q))[None]
         _, _, lse, O = fused_decode(inp.q, fx.norm_weight, fx.norm_eps, fx.rope_cs, lambda b, L: rot[:L],
-                                    inp.block_table, inp.seqlens, inp.softmax_scale, True)
+                                    inp.block_table, inp.seqlens, inp.softmax_scale, True, round_query=False)
         cs_q = fx.rope_cs.astype(np.float64)[0][:, None, :]
         plain = rope_rotate(O[0], cs_q[..., :32], cs_q[..., 32:])  # the attention output itself
         return O, lse, plain
