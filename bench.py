@@ -33,7 +33,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA datasheet (2.5 PFLOP/s)
 D_QK, D_V = 576, 512
 HEADLINE = 4                   # the long-context workload: the most bytes per call
 # what bounds each workload: the tiny one is latency only
-BOUND = {1: "latency", 2: "hbm", 3: "mfma", 4: "hbm", 5: "hbm", 6: "hbm", 7: "mfma", 8: "mfma", 9: "mfma"}
+BOUND = {1: "latency", 2: "hbm", 3: "mfma", 4: "hbm", 5: "hbm", 6: "hbm", 7: "mfma", 8: "mfma", 9: "mfma",
+         10: "mfma"}
 PAGED_KINDS = ("paged", "paged_fp8", "paged_v4", "paged_v4_fp4")
 
 
@@ -64,6 +65,15 @@ def paged_counts(inp):
         else:
             vis += int(L.sum())
     flops = 2 * (d + D_V) * h_q * vis
+    return byts, flops
+
+
+def fused_counts(inp):
+    """The fused decode: the V4-geometry paged counts with the output as e4m3 codes (1 B per value)
+    plus one fp32 scale per row instead of bf16 O, and the norm weight and angle table read."""
+    byts, flops = paged_counts(inp)
+    rows = inp.batch * inp.s_q * inp.h_q
+    byts += rows * (D_V + 4) - rows * D_V * 2 + D_V * 4 + inp.batch * inp.s_q * 64 * 4
     return byts, flops
 
 
@@ -237,11 +247,37 @@ def setup_prefill(torch, mla, inp, dev):
     return prefill
 
 
+def setup_fused(torch, mla, inp, dev):
+    """The fused decode (mla_decode_fused) over bf16 pages, metadata computed once."""
+    from tests.helpers import dev_bf16, dev_i32
+
+    q = dev_bf16(inp.q, dev)
+    kc = dev_bf16(inp.kcache.reshape(inp.kcache.shape[0], 64, D_V), dev)
+    bt, sl = dev_i32(inp.block_table, dev), dev_i32(inp.seqlens, dev)
+    sk = None if inp.sinks is None else torch.from_numpy(inp.sinks).to(dev)
+    w = torch.from_numpy(inp.fused.norm_weight).to(dev)
+    cs = torch.from_numpy(np.ascontiguousarray(inp.fused.rope_cs)).to(dev)
+    P = mla.num_parts(inp.h_q, inp.s_q)
+    out = torch.empty((inp.batch, inp.s_q, inp.h_q, D_V), dtype=torch.uint8, device=dev)
+    osc = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    ws = torch.zeros((max(mla.workspace_size(inp.batch, inp.s_q, inp.h_q, P), 256),), dtype=torch.uint8, device=dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, P)
+
+    def fused():
+        mla.decode_fused(q, kc, bt, sl, meta, w, inp.fused.norm_eps, cs, inp.softmax_scale, inp.causal, sinks=sk,
+                         out=out, out_scale=osc, lse=lse, workspace=ws)
+
+    return fused
+
+
 def setup_call(torch, mla, k, inp, dev):
     """Workload k's decode call (metadata computed once for paged workloads) and its counts."""
     from mla_inputs import CONFIGS
 
     kind = CONFIGS[k]["kind"]
+    if kind == "fused_v4":
+        return setup_fused(torch, mla, inp, dev), fused_counts(inp)
     if kind in PAGED_KINDS:
         _, fn, _ = setup_paged(torch, mla, inp, dev)
         return fn, paged_counts(inp)
@@ -261,6 +297,7 @@ KERNELS = {
     7: "mla_decode_wide_kernel<0, true, 512> + mla_combine_kernel",
     8: "mla_decode_wide_kernel<3, true, 512> + mla_combine_kernel",
     9: "mla_decode_rows_kernel<1, true, 576> (one split)",
+    10: "mla_decode_wide_kernel<0, true, 512, true> + mla_combine_fused_kernel",
 }
 
 

@@ -25,6 +25,7 @@ EXPORTS = (
     "mla_workspace_size", "mla_decode_paged", "mla_decode_paged_fp8", "mla_decode_paged_latent512",
     "mla_decode_paged_fp4", "mla_sparse_splits",
     "mla_workspace_size_sparse", "mla_decode_sparse", "mla_sparse_prefill", "mla_decode_paged_noalloc",
+    "mla_decode_fused",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20     # MLA_NOALLOC_SCRATCH_BYTES
 
@@ -67,6 +68,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged_fp4.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp,
                                          vp, vp, i32, vp, sz, vp, vp, vp]
     lib.mla_decode_paged_fp4.restype = i32
+    lib.mla_decode_fused.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp,
+                                     vp, f32, vp, vp, vp, i32, vp, sz, vp, vp, vp, vp]
+    lib.mla_decode_fused.restype = i32
     lib.mla_sparse_splits.argtypes = [i32, i32, i32, i32]
     lib.mla_sparse_splits.restype = i32
     lib.mla_workspace_size_sparse.argtypes = [i32, i32, i32, i32, i32]
@@ -317,6 +321,69 @@ def decode_paged_fp4(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.T
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
     return out, lse
+
+
+def decode_fused(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                 cache_seqlens: torch.Tensor, metadata: Tuple[torch.Tensor, torch.Tensor],
+                 norm_weight: torch.Tensor, norm_eps: float, rope_cs: torch.Tensor,
+                 softmax_scale: float = D_V ** -0.5, causal: bool = False,
+                 sinks: Optional[torch.Tensor] = None, kv_scales: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The fused decode (mla_decode_fused): query RMS norm and RoPE, attention over 512-wide latent
+    rows, conjugate RoPE of the output and its FP8 cast.
+
+    q bf16 [b, s_q, h_q, 512]; kcache bf16 [num_blocks, 64, 512], or (with kv_scales uint8
+    [num_blocks, 64, 32]) uint8 [num_blocks, 64, 256] FP4 codes; norm_weight fp32 [512];
+    rope_cs fp32 [b, s_q, 64] (cos then sin of the 32 pair angles of each query token); sinks fp32
+    [h_q] or None.  Returns (codes uint8 [b, s_q, h_q, 512] e4m3, scale fp32 [b, s_q, h_q],
+    lse fp32 [b, s_q, h_q]).
+    """
+    batch, s_q, h_q, d = q.shape
+    if d != D_V:
+        raise ValueError("q must have 512 dims per head")
+    _require(q, "q", torch.bfloat16)
+    nb = kcache.shape[0]
+    if kv_scales is None:
+        _require(kcache, "kcache", torch.bfloat16)
+        if kcache.dim() != 3 or tuple(kcache.shape[1:]) != (PAGE, D_V):
+            raise ValueError("kcache must be [num_blocks, 64, 512] bf16")
+    else:
+        _require(kcache, "kv_codes", torch.uint8)
+        _require(kv_scales, "kv_scales", torch.uint8, (nb, PAGE, 32))
+        if kcache.dim() != 3 or tuple(kcache.shape[1:]) != (PAGE, 256):
+            raise ValueError("FP4 codes must be [num_blocks, 64, 256] uint8")
+    _require(block_table, "block_table", torch.int32)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
+    _require(norm_weight, "norm_weight", torch.float32, (D_V,))
+    _require(rope_cs, "rope_cs", torch.float32, (batch, s_q, 64))
+    if sinks is not None:
+        _require(sinks, "sinks", torch.float32, (h_q,))
+    tile_meta, num_splits = metadata
+    P = tile_meta.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.uint8, device=dev)
+    if out_scale is None:
+        out_scale = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.uint8, (batch, s_q, h_q, D_V))
+    _require(out_scale, "out_scale", torch.float32, (batch, s_q, h_q))
+    _require(lse, "lse", torch.float32, (batch, s_q, h_q))
+    need = workspace_size(batch, s_q, h_q, P)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    _check("mla_decode_fused", lib.mla_decode_fused(
+        q.data_ptr(), kcache.data_ptr(), None if kv_scales is None else kv_scales.data_ptr(), nb,
+        block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(), batch, s_q, h_q,
+        float(softmax_scale), 1 if causal else 0, None if sinks is None else sinks.data_ptr(),
+        norm_weight.data_ptr(), float(norm_eps), rope_cs.data_ptr(),
+        tile_meta.data_ptr(), num_splits.data_ptr(), P,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), out_scale.data_ptr(), lse.data_ptr(), _stream_ptr(dev)))
+    return out, out_scale, lse
 
 
 # --------------------------------------------------------------------------

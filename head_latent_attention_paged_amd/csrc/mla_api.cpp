@@ -43,6 +43,14 @@ int sparse_auto_splits(int batch, int s_q, int h_q, int topk) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// the fused decode's extra arguments
+struct FusedParams {
+    const float* weight;
+    float eps;
+    const float* rope_cs;
+    float* out_scale;
+};
+
 size_t partial_bytes(long long slots, long long rows) {
     return align256((size_t)slots * rows * mla::kDv * sizeof(float)) + align256((size_t)slots * rows * sizeof(float));
 }
@@ -143,7 +151,8 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
                                       void* out, float* lse, void* stream, bool fp8,
                                       int d_qk = mla::kDqk, const float* sinks = nullptr,
                                       const void* kv_scale = nullptr, bool fp4 = false,
-                                      mla::ScratchSource scratch = nullptr) {
+                                      mla::ScratchSource scratch = nullptr,
+                                      const FusedParams* fused = nullptr) {
     if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0 || max_blocks <= 0 || num_blocks <= 0)
@@ -151,6 +160,9 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(kcache) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
     if (fp4 && (!kv_scale || !aligned16(kv_scale))) return MLA_ERR_INVALID_ARG;
+    if (fused && (!fused->weight || !fused->rope_cs || !fused->out_scale || !aligned16(fused->weight) ||
+                  !aligned16(fused->rope_cs) || !std::isfinite(fused->eps) || fused->eps < 0.f))
+        return MLA_ERR_INVALID_ARG;
     if ((long long)s_q * h_q > mla::kMaxRows) return MLA_ERR_UNSUPPORTED;
     if (batch > mla::kMaxBatchMeta) return MLA_ERR_UNSUPPORTED;
     const size_t need = mla_workspace_size(batch, s_q, h_q, num_parts);
@@ -191,10 +203,19 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     a.kv_rows = num_blocks * mla::kPage;
     a.d_qk = d_qk;
     a.sinks = sinks;
+    if (fused) {
+        a.fused = 1;
+        a.qn_weight = fused->weight;
+        a.qn_eps = fused->eps;
+        a.rope_cs = fused->rope_cs;
+        a.out_scale = fused->out_scale;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (mla::launch_decode(a, false, s) != hipSuccess) return MLA_ERR_HIP;
-    if (mla::launch_combine(a.part_o, a.part_lse, num_splits, 0, batch, M, out, lse, s, sinks, h_q) != hipSuccess)
-        return MLA_ERR_HIP;
+    const hipError_t e = fused ? mla::launch_combine_fused(a, s)
+                               : mla::launch_combine(a.part_o, a.part_lse, num_splits, 0, batch, M, out, lse, s,
+                                                     sinks, h_q);
+    if (e != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 
@@ -251,6 +272,20 @@ mla_status_t mla_decode_paged_fp4(const void* q, const void* kv_codes, const voi
     return decode_paged_impl(q, kv_codes, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
                              softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
                              workspace_bytes, out, lse, stream, false, mla::kDv, sinks, kv_scales, true);
+}
+
+mla_status_t mla_decode_fused(const void* q, const void* kv_codes, const void* kv_scales, int64_t num_blocks,
+                              const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                              int batch, int s_q, int h_q, float softmax_scale, int causal, const float* sinks,
+                              const float* norm_weight, float norm_eps, const float* rope_cs,
+                              const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                              void* workspace, size_t workspace_bytes,
+                              void* out_fp8, float* out_scale, float* lse, void* stream) {
+    const FusedParams f{norm_weight, norm_eps, rope_cs, out_scale};
+    return decode_paged_impl(q, kv_codes, num_blocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                             softmax_scale, causal, tile_meta, num_splits, num_parts, workspace,
+                             workspace_bytes, out_fp8, lse, stream, false, mla::kDv, sinks, kv_scales,
+                             kv_scales != nullptr, nullptr, &f);
 }
 
 mla_status_t mla_decode_paged_fp8(const void* q, const void* kcache, int64_t num_blocks,

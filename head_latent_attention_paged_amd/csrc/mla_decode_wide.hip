@@ -103,9 +103,12 @@ struct Cfg {
 
 // D: width of a cached row, 576 (512 latent + 64 RoPE dims) or 512 (the DeepSeek-V4 latent row
 // that is both K and V: bf16 or FP4 pages)
-template <int MODE, bool SHARED, int D>
+// FUSED (512-wide rows): the fused decode, whose query gets its RMS norm and rotation as it is
+// loaded and whose final rows leave as FP8 codes after the conjugate rotation
+template <int MODE, bool SHARED, int D, bool FUSED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_wide_kernel(const AttnArgs a) {
+    static_assert(!FUSED || D == kDv, "the fused decode works on 512-wide rows");
     constexpr bool FP4 = MODE == kPagedFp4;
     constexpr bool GATHER = FP4;
     static_assert(MODE == kPagedBf16 || (FP4 && D == kDv), "FP4 pages hold 512-wide rows");
@@ -204,6 +207,52 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                 uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 32);
                 if (qrw >= a.M) v = make_uint4(0, 0, 0, 0);
                 qf[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+            if constexpr (FUSED) {
+                // the query's RMS norm over its 512 dims (the lane holds dims 16ks + 8qg .. +7,
+                // lane ^ 32 the other half) with the shared weight, then the rotation of the
+                // pairs (448 + 2i, 449 + 2i) by the query token's angles; the result is the bf16
+                // B operand
+                float ss = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float f = (float)qf[ks][e];
+                        ss = __builtin_fmaf(f, f, ss);
+                    }
+                ss += xor32(ss);
+                const float rinv = 1.f / sqrtf(ss * (1.f / kDv) + a.qn_eps);
+                int hq = a.h_q;
+                asm volatile("" : "+s"(hq));
+                const float* cs = a.rope_cs + ((size_t)grp * a.s_q + qr / hq) * 64;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    // (opaque: the sum of squares above does not keep its 256 floats live for this)
+                    asm volatile("" : "+v"(qf[ks]));
+                    const int d0 = 16 * ks + 8 * qg;
+                    const f4 w0 = *reinterpret_cast<const f4*>(a.qn_weight + d0);
+                    const f4 w1 = *reinterpret_cast<const f4*>(a.qn_weight + d0 + 4);
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (float)qf[ks][e] * rinv * (e < 4 ? w0[e] : w1[e - 4]);
+                    if (16 * ks >= kRopeStart) {
+                        const int i0 = (d0 - kRopeStart) >> 1;
+                        const f4 c = *reinterpret_cast<const f4*>(cs + i0);
+                        const f4 sn = *reinterpret_cast<const f4*>(cs + 32 + i0);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float x = v[2 * j], y = v[2 * j + 1];
+                            v[2 * j] = x * c[j] - y * sn[j];
+                            v[2 * j + 1] = x * sn[j] + y * c[j];
+                        }
+                    }
+                    const uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+                    qf[ks] = __builtin_bit_cast(bf16x8, u);
+                    // one fragment at a time: the weight loads are not hoisted ahead of the loop
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         m_run = -INFINITY;
@@ -572,6 +621,71 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         asm volatile("" : "+s"(nrow));
         const int ln = el, er = el & 31, eg = el >> 5;
         __syncthreads();                   // the ring is no longer read: LDS is free
+        if (FUSED && final_out) {
+            // the conjugate rotation of dims 448..511 (tiles 14 and 15) by the query token's
+            // angles, then the FP8 cast with one scale per row (amax / 448): codes through LDS,
+            // out as whole 512-byte rows.  Lane value 4q + r of tile dt is dim 32dt + 8q + 4eg + r.
+            int hq = a.h_q;
+            asm volatile("" : "+s"(hq));
+            const float* cs = a.rope_cs + ((size_t)grp * a.s_q + (orow < a.M ? orow : 0) / hq) * 64;
+            // (the two passes below each rebuild the values from the accumulators: inv is made
+            // opaque per pass, so that no pass keeps 256 products live for the other)
+            auto outval = [&](int dt, int q, float (&x)[4], float iv) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = acc[dt][4 * q + r] * iv;
+                if (32 * dt >= kRopeStart) {
+                    const int i0 = (32 * dt + 8 * q + 4 * eg - kRopeStart) >> 1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float c = cs[i0 + j], sn = cs[32 + i0 + j];
+                        const float u = x[2 * j], w = x[2 * j + 1];
+                        x[2 * j] = u * c + w * sn;
+                        x[2 * j + 1] = w * c - u * sn;
+                    }
+                }
+            };
+            float amax = 0.f;
+            float inv1 = inv;
+            asm volatile("" : "+v"(inv1));
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float x[4];
+                    outval(dt, q, x, inv1);
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            amax = fmaxf(amax, xor32(amax));
+            const float fscale = fmaxf(amax, 1.17549435e-38f) / kE4m3Max;
+            const float finv = 1.f / fscale;
+            float inv2 = inv;
+            asm volatile("" : "+v"(inv2));
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float x[4];
+                    outval(dt, q, x, inv2);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[r] = fminf(fmaxf(x[r] * finv, -kE4m3Max), kE4m3Max);
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+                    *reinterpret_cast<int*>(stg + er * kOutPitch + 32 * dt + 8 * q + 4 * eg) = w;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            if (orow < a.M && el < 32) a.out_scale[(size_t)grp * a.M + orow] = fscale;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own staging writes
+            char* obase = static_cast<char*>(a.out) + ((size_t)grp * a.M + row0) * kDv;
+#pragma unroll 4
+            for (int i = 0; i < kRowsWave / 2; ++i) {
+                const int r = 2 * i + (ln >> 5), cgr = ln & 31;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kOutPitch + cgr * 16);
+                if (r < nrow) *reinterpret_cast<uint4*>(obase + (size_t)r * kDv + cgr * 16) = v;
+            }
+            __syncthreads();               // LDS free for the next segment
+            return;
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -627,10 +741,20 @@ void mla_decode_wide_kernel(const AttnArgs a) {
 hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream) {
     const int R = (a.M + wide::kRowsWg - 1) / wide::kRowsWg;
     const dim3 grid(a.num_parts * R), block(wide::kWaves * 64);
-#define MLA_WIDE_LAUNCH(MODE_, D_)                                                                                 \
-    if (R > 1) hipLaunchKernelGGL((wide::mla_decode_wide_kernel<MODE_, true, D_>), grid, block, 0, stream, a);    \
-    else hipLaunchKernelGGL((wide::mla_decode_wide_kernel<MODE_, false, D_>), grid, block, 0, stream, a);
+#define MLA_WIDE_LAUNCH_F(MODE_, D_, F_)                                                                           \
+    if (R > 1) hipLaunchKernelGGL((wide::mla_decode_wide_kernel<MODE_, true, D_, F_>), grid, block, 0, stream, a); \
+    else hipLaunchKernelGGL((wide::mla_decode_wide_kernel<MODE_, false, D_, F_>), grid, block, 0, stream, a);
+#define MLA_WIDE_LAUNCH(MODE_, D_) MLA_WIDE_LAUNCH_F(MODE_, D_, false)
     if (a.kv_fp8) return hipErrorInvalidValue;      // (the row-split kernel's mode)
+    if (a.fused) {
+        if (a.d_qk != kDv) return hipErrorInvalidValue;
+        if (a.kv_fp4) {
+            MLA_WIDE_LAUNCH_F(wide::kPagedFp4, kDv, true)
+        } else {
+            MLA_WIDE_LAUNCH_F(wide::kPagedBf16, kDv, true)
+        }
+        return hipGetLastError();
+    }
     if (a.kv_fp4) {
         MLA_WIDE_LAUNCH(wide::kPagedFp4, kDv)
     } else if (a.d_qk == kDv) {
@@ -639,6 +763,7 @@ hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream) {
         MLA_WIDE_LAUNCH(wide::kPagedBf16, kDqk)
     }
 #undef MLA_WIDE_LAUNCH
+#undef MLA_WIDE_LAUNCH_F
     return hipGetLastError();
 }
 

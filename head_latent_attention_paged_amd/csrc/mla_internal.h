@@ -62,7 +62,18 @@ struct AttnArgs {
     int d_qk;                   // paged bf16: row width, 576 or 512 (latent row that is K and V)
     const float* sinks;         // per-head attention sinks [h_q] (natural log), or null
     float scale_log2;           // softmax_scale * log2(e)
+    // fused decode (512-wide rows): the query's RMS norm and RoPE before the attention, the
+    // conjugate RoPE and the FP8 cast of the output after it; out then holds e4m3 codes
+    // (uint8 [groups, M, 512]) and out_scale their fp32 scale per row
+    int fused;
+    const float* qn_weight;     // fp32 [512]
+    float qn_eps;
+    const float* rope_cs;       // fp32 [batch, s_q, 64]: cos of the 32 pair angles, then sin
+    float* out_scale;           // fp32 [groups, M]
 };
+// rotary dims of the fused decode: the interleaved pairs (448 + 2i, 449 + 2i) of the 512-wide row
+constexpr int kRopeStart = 448;
+constexpr float kE4m3Max = 448.f;
 
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int overhead,
                            int32_t* tile_meta, int32_t* num_splits, hipStream_t stream);
@@ -93,5 +104,7 @@ mla_status_t decode_paged_scratch(const void* q, const void* kcache, int64_t num
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream, const float* sinks = nullptr, int h_q = 1);
+// the combine of the fused decode: merged rows get the conjugate RoPE and the FP8 cast
+hipError_t launch_combine_fused(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -951,6 +951,8 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const Tiling t = choose_tiling(a.M);
     // bf16 and FP4 pages with more than 64 rows: the one-wave-per-SIMD kernel (576-wide bf16
     // rows need a positive scale, which it applies in the exponent)
+    // the fused decode: the one-wave-per-SIMD kernel, whatever the rows
+    if (!sparse && a.fused) return launch_decode_wide(a, stream);
     if (!sparse && !a.kv_fp8 && a.M > kWideMinRows && (a.kv_fp4 || a.d_qk == kDv || a.scale_log2 > 0.f))
         return launch_decode_wide(a, stream);
     // 512-wide rows (K and V): the row-split kernel, whatever the rows and the scale
@@ -978,6 +980,100 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     MLA_DISPATCH(1, 1)
 #undef MLA_DISPATCH
     return hipErrorInvalidValue;
+}
+
+// The combine of the fused decode: one wave per output row of a split sequence.  The LSE-weighted
+// merge of the row's partials (as mla_combine_kernel), then the conjugate rotation of dims
+// 448..511 by the query token's angles and the FP8 cast with one scale per row (amax / 448).
+// Lane l holds dims 4l..4l+3 and 256 + 4l..+3.
+__global__ __launch_bounds__(256) void mla_combine_fused_kernel(const AttnArgs a) {
+    const int grp = blockIdx.x;
+    const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int rows = a.M;
+    if (r >= rows) return;
+    const int base = a.num_splits[grp];
+    const int n = a.num_splits[grp + 1] - base;
+    if (n == 1) return;   // the decode kernel wrote this row directly
+    const float sk = a.sinks ? a.sinks[r % a.h_q] : -INFINITY;
+    float mu = sk;
+    float wsum = sk != -INFINITY ? 1.f : 0.f;
+    f4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int i0 = 0; i0 < n; i0 += kCombineGroup) {
+        float li[kCombineGroup];
+        f4 v[kCombineGroup][2];
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; ++j) {
+            const int i = base + (i0 + j < n ? i0 + j : n - 1);    // (past n: a repeat, unused)
+            li[j] = a.part_lse[(size_t)i * rows + r];
+            const float* p = a.part_o + ((size_t)i * rows + r) * kDv + 4 * lane;
+            v[j][0] = *reinterpret_cast<const f4*>(p);
+            v[j][1] = *reinterpret_cast<const f4*>(p + 256);
+        }
+        float mg = mu;
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; ++j)
+            if (i0 + j < n) mg = fmaxf(mg, li[j]);
+        if (mg == -INFINITY) continue;                          // nothing finite so far
+        const float sc = mu == -INFINITY ? 0.f : expf(mu - mg);  // mu <= mg
+        wsum *= sc;
+        o[0] *= sc;
+        o[1] *= sc;
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; ++j) {
+            if (i0 + j < n && li[j] != -INFINITY) {
+                const float w = expf(li[j] - mg);
+                wsum += w;
+                o[0] += v[j][0] * w;
+                o[1] += v[j][1] * w;
+            }
+        }
+        mu = mg;
+    }
+    if (mu != -INFINITY) {
+        const float iw = 1.f / wsum;
+        o[0] *= iw;
+        o[1] *= iw;
+    }
+    if (4 * lane + 256 >= kRopeStart) {
+        const float* cs = a.rope_cs + ((size_t)grp * a.s_q + r / a.h_q) * 64;
+        const int i0 = (4 * lane + 256 - kRopeStart) >> 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float c = cs[i0 + j], sn = cs[32 + i0 + j];
+            const float u = o[1][2 * j], w = o[1][2 * j + 1];
+            o[1][2 * j] = u * c + w * sn;
+            o[1][2 * j + 1] = w * c - u * sn;
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[h][e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float fscale = fmaxf(amax, 1.17549435e-38f) / kE4m3Max;
+    const float finv = 1.f / fscale;
+    unsigned char* orow = static_cast<unsigned char*>(a.out) + ((size_t)grp * rows + r) * kDv;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(o[h][e] * finv, -kE4m3Max), kE4m3Max);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+        *reinterpret_cast<int*>(orow + 256 * h + 4 * lane) = w;
+    }
+    if (lane == 0) {
+        a.out_scale[(size_t)grp * rows + r] = fscale;
+        a.lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
+    }
+}
+
+hipError_t launch_combine_fused(const AttnArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(mla_combine_fused_kernel, dim3(a.batch, (a.M + 3) / 4), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* prefix,

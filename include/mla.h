@@ -217,6 +217,44 @@ mla_status_t mla_decode_paged_fp4(const void* q, const void* kv_codes, const voi
                                   void* out, float* lse, void* stream);
 
 /*
+ * The fused decode ("deepseek-ai/FlashMLA" project summary, section 개요 bullet 3: one
+ * kernel launch merges the query norm, RoPE, the attention, the conjugate RoPE on the output
+ * side and the final cast to FP8; section 사용 방법 step 5: its FP8 output feeds the FP8 einsum
+ * that follows), here on the DeepSeek-V4 decode geometry of mla_decode_paged_latent512 /
+ * mla_decode_paged_fp4.  Per query row (token s of sequence b, head h):
+ *
+ *   q'  = RoPE(q * norm_weight / sqrt(mean(q^2) + norm_eps))      (RMS norm over 512 dims)
+ *   O   = the paged decode of q' (causal rule, sinks: mla_decode_paged_latent512)
+ *   O'  = conjugate RoPE(O)
+ *   out = e4m3 codes of O' / scale, scale = max(max|O'|, 2^-126) / 448 (one fp32 per row)
+ *
+ * RoPE turns the interleaved pairs of dims (448 + 2i, 449 + 2i), i < 32, by the query token's
+ * angle theta_i; the conjugate RoPE turns the same pairs of O by -theta_i.  (The cached rows'
+ * last 64 dims carry their own tokens' rotations, written when the cache was filled.)  The
+ * codes are OCP E4M3FN, rounded to nearest even from fp32 x * (1 / scale).
+ *
+ *   q           [device] bf16 [batch, s_q, h_q, 512]: the query before its norm and RoPE
+ *   kv_codes    [device] bf16 [num_blocks, 64, 512] when kv_scales is NULL; otherwise
+ *               uint8 [num_blocks, 64, 256] FP4 codes (as mla_decode_paged_fp4)
+ *   kv_scales   [device] uint8 [num_blocks, 64, 32] UE4M3 block scales, or NULL (bf16 pages)
+ *   norm_weight [device] fp32 [512], shared by the heads; norm_eps >= 0
+ *   rope_cs     [device] fp32 [batch, s_q, 64]: cos(theta_i), i < 32, then sin(theta_i), of
+ *               each query token
+ *   out_fp8     [device] uint8 [batch, s_q, h_q, 512] e4m3 codes (written)
+ *   out_scale   [device] fp32 [batch, s_q, h_q] (written); lse as for mla_decode_paged
+ *
+ * Block table, lengths, causal rule, sinks, metadata and workspace (mla_workspace_size) are as
+ * for mla_decode_paged_latent512.  norm_weight and rope_cs must be 16-byte aligned.
+ */
+mla_status_t mla_decode_fused(const void* q, const void* kv_codes, const void* kv_scales, int64_t num_blocks,
+                              const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                              int batch, int s_q, int h_q, float softmax_scale, int causal, const float* sinks,
+                              const float* norm_weight, float norm_eps, const float* rope_cs,
+                              const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
+                              void* workspace, size_t workspace_bytes,
+                              void* out_fp8, float* out_scale, float* lse, void* stream);
+
+/*
  * Paged MLA decode over an fp8 cache: the same call as mla_decode_paged with
  * the cache in the fp8 layout of the decode path ("deepseek-ai/FlashMLA"
  * project summary, section 사용 방법 step 3: flash_mla_with_kvcache on the

@@ -12,7 +12,8 @@ import pytest
 
 from mla_inputs import make_config, make_paged, make_paged_fp4, make_paged_fp8, make_sparse
 from mla_inputs.gen import bf16_bits_from_f32, bf16_bits_to_f32, quantize_rows_e4m3
-from oracle import paged_decode, paged_decode_fp4, paged_decode_fp8, sparse_decode
+from oracle import (E4M3_TABLE, fused_decode, gather_paged_fp4, gather_paged_rows, paged_decode, paged_decode_fp4,
+                    paged_decode_fp8, sparse_decode)
 from tests.helpers import check_parity, dev_bf16, dev_i32, dev_u8, record_parity, to_host
 
 pytestmark = pytest.mark.gpu
@@ -739,3 +740,122 @@ def test_sparse_pool_beyond_4gib(env, h_q):
     torch.cuda.empty_cache()
     o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
     check_parity(o, l, o_ref, l_ref, "sparse pool beyond 4 GiB h_q %d" % h_q)
+
+
+# ----------------------------------------------------------------- fused decode (norm, RoPE, attn, RoPE, FP8)
+def run_fused(env, inp, num_parts=None):
+    """mla_decode_fused over bf16 pages (PagedInputs with 512-wide rows) or FP4 pages."""
+    import torch
+
+    mla, dev = env
+    fx = inp.fused
+    q = dev_bf16(inp.q, dev)
+    if hasattr(inp, "kv_codes"):
+        kc, ks = dev_u8(inp.kv_codes, dev), dev_u8(inp.kv_scales, dev)
+    else:
+        kc, ks = dev_bf16(inp.kcache.reshape(inp.num_pages, 64, 512), dev), None
+    bt, sl = dev_i32(inp.block_table, dev), dev_i32(inp.seqlens, dev)
+    sk = None if inp.sinks is None else torch.from_numpy(inp.sinks).to(dev)
+    w = torch.from_numpy(fx.norm_weight).to(dev)
+    cs = torch.from_numpy(np.ascontiguousarray(fx.rope_cs)).to(dev)
+    meta = mla.get_metadata(sl, inp.h_q, inp.s_q, num_parts)
+    codes, scale, lse = mla.decode_fused(q, kc, bt, sl, meta, w, fx.norm_eps, cs, inp.softmax_scale, inp.causal,
+                                         sinks=sk, kv_scales=ks)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scale.cpu().numpy(), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_fused(inp):
+    fx = inp.fused
+    if hasattr(inp, "kv_codes"):
+        rows_of = lambda b, L: gather_paged_fp4(inp.kv_codes, inp.kv_scales, inp.block_table[b], L)  # noqa: E731
+    else:
+        rows_of = lambda b, L: gather_paged_rows(inp.kcache, inp.block_table[b], L)  # noqa: E731
+    return fused_decode(inp.q, fx.norm_weight, fx.norm_eps, fx.rope_cs, rows_of, inp.block_table, inp.seqlens,
+                        inp.softmax_scale, inp.causal, sinks=inp.sinks)
+
+
+def check_fused(got, ref, what, softmax_scale=512 ** -0.5):
+    """The FP8 output against the exact (float64) fused result.  LSE: the attention bar, scaled
+    with the softmax scale above the default 512^-0.5 (the kernel's fp32 norm and the oracle's
+    float64 norm round the query to bf16 the same way except within fp32 error of a rounding
+    boundary, where one element moves by one bf16 step; the score moves by softmax_scale times
+    that, so the bar grows with the scale).  Scale:
+    the row maxima may differ by the O bar, so the scales by that over 448.  Values: the
+    dequantised code lies within the O bar plus one E4M3 step (at the reference's magnitude plus
+    the bar) of the exact value: the kernel's own fp32 value, within the bar, may round to either
+    neighbour."""
+    codes, scale, lse = got
+    codes_r, scale_r, lse_r, O_r = ref
+    assert codes.shape == codes_r.shape and scale.shape == scale_r.shape
+    fin = np.isfinite(lse_r)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_r)), "%s: -inf rows differ" % what
+    if fin.any():
+        lerr = np.abs(lse[fin] - lse_r[fin]).max()
+        ltol = 1e-3 * max(1.0, abs(softmax_scale) / 512 ** -0.5)
+        assert lerr <= ltol, "%s: max|LSE-LSE_ref| = %.3g > %.3g" % (what, lerr, ltol)
+    assert not np.any((codes & 0x7F) == 0x7F), "%s: NaN codes" % what
+    tol = 1e-2 * np.abs(O_r).max() + 2e-3
+    assert np.all(np.abs(scale.astype(np.float64) - scale_r) <= tol / 448.0 + 1e-7 * scale_r), "%s: scales" % what
+    sk = scale.astype(np.float64)[..., None]
+    deq = E4M3_TABLE[codes] * sk
+    y = (np.abs(O_r) + tol) / sk
+    step = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3), 2.0 ** -9) * sk
+    err = np.abs(deq - O_r)
+    bad = err > tol + step
+    assert not bad.any(), "%s: %d values beyond the bar (worst excess %.3g)" % (what, bad.sum(), (err - tol - step).max())
+    same = float(np.mean(codes == codes_r))
+    return float(np.abs(deq - O_r).max()), same
+
+
+FUSED_CASES = [
+    # batch, s_q, h_q, seqlens, causal, sinks, num_parts
+    (2, 6, 64, [300, 70], True, True, None),
+    (2, 6, 64, [300, 70], True, False, 3),
+    (3, 1, 16, [1, 64, 65], False, True, None),
+    (3, 2, 32, [500, 0, 3], True, True, 3),
+    (1, 6, 64, [2000], True, True, 16),
+    (1, 6, 128, [700], True, True, None),
+    (4, 6, 8, [5, 6, 7, 129], True, True, 2),
+    (2, 3, 32, [300, 77], True, True, None),
+    (2, 1, 64, [3000, 2500], False, False, 8),
+    (1, 6, 64, [322], True, True, 8),
+]
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[str(i) for i in range(len(FUSED_CASES))])
+def test_fused_decode_cases(env, case, fp4):
+    from mla_inputs import make_fused_extras
+
+    batch, s_q, h_q, L, causal, sinks, P = case
+    _say("fused case", case, "fp4" if fp4 else "bf16")
+    if fp4:
+        inp = make_paged_fp4(batch, s_q, h_q, L, causal, seed=1100 + sum(L) + h_q, poison=True, sinks=sinks)
+    else:
+        inp = make_paged(batch, s_q, h_q, L, causal, seed=1000 + sum(L) + h_q, poison=True, d_qk=512, sinks=sinks)
+    inp.fused = make_fused_extras(inp, 1200 + h_q)
+    got = run_fused(env, inp, P)
+    err, same = check_fused(got, oracle_fused(inp), "fused " + str(case))
+    _say("fused", case, "max err %.3g, codes equal to the oracle's: %.4f" % (err, same))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05, 2.5])
+def test_fused_decode_softmax_scales(env, scale):
+    from mla_inputs import make_fused_extras
+
+    _say("fused scale", scale)
+    inp = make_paged(2, 6, 64, [900, 300], True, seed=1300, poison=True, softmax_scale=scale, d_qk=512, sinks=True)
+    inp.fused = make_fused_extras(inp, 1301)
+    check_fused(run_fused(env, inp), oracle_fused(inp), "fused scale %g" % scale, inp.softmax_scale)
+
+
+def test_full_size_fused_decode(env):
+    _say("full-size config 10")
+    inp = make_config(10, poison=False)
+    got = run_fused(env, inp)
+    ref = oracle_fused(inp)
+    err, same = check_fused(got, ref, "config 10")
+    rec = record_parity("config 10 (dequantised FP8 vs exact)", E4M3_TABLE[got[0]] * got[1].astype(np.float64)[..., None],
+                        got[2], ref[3], ref[2])
+    _say("config 10 max err %.3g rmse %.3g, codes equal to the oracle's %.4f" % (err, rec["rmse"], same))

@@ -152,6 +152,30 @@ def test_paged_fp4_validation_before_launch(mla):
     assert call(wsb=100) == mla.MLA_ERR_WORKSPACE
 
 
+def test_fused_validation_before_launch(mla):
+    f = mla.lib.mla_decode_fused
+    ok = dict(q=16, kc=16, ks=None, nb=4, bt=16, maxb=1, sl=16, batch=1, s_q=6, h_q=64, scale=0.04, causal=1,
+              sinks=None, w=16, eps=1e-6, cs=16, meta=16, ns=16, P=8, ws=16, wsb=1 << 30, out=16, osc=16, lse=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["kc"], a["ks"], a["nb"], a["bt"], a["maxb"], a["sl"], a["batch"], a["s_q"], a["h_q"],
+                 a["scale"], a["causal"], a["sinks"], a["w"], a["eps"], a["cs"], a["meta"], a["ns"], a["P"],
+                 a["ws"], a["wsb"], a["out"], a["osc"], a["lse"], None)
+
+    assert call(w=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(cs=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(osc=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(w=20) == mla.MLA_ERR_INVALID_ARG                   # misaligned weight
+    assert call(cs=24) == mla.MLA_ERR_INVALID_ARG                  # misaligned angle table
+    assert call(eps=-1.0) == mla.MLA_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert call(ks=20) == mla.MLA_ERR_INVALID_ARG                  # misaligned FP4 scales
+    assert call(s_q=64, h_q=128) == mla.MLA_ERR_UNSUPPORTED
+    assert call(wsb=100) == mla.MLA_ERR_WORKSPACE
+
+
 def test_sparse_validation_before_launch(mla):
     f = mla.lib.mla_decode_sparse
     ok = dict(q=16, kv=16, nt=10, idx=16, topk=64, batch=1, s_q=1, h_q=16, scale=0.04, splits=0,
