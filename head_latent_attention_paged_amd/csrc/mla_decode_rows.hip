@@ -39,6 +39,8 @@
 // paged chunk layout.
 #include "mla_device.h"
 
+#include <type_traits>
+
 namespace mla {
 
 namespace rows {
@@ -67,11 +69,14 @@ constexpr int kChunk16 = kRegionB16 + kChunk * 128;
 __device__ __forceinline__ int swzB(int r) { return (r >> 1) & 7; }
 
 // Sparse gathers: a chunk's 32 records are 32 x 36 granules of 16 codes plus 32 scale granules;
-// a wave loads 4 records = 148 granules with 3 loads of 64 lanes (slots 148..191 repeat slots
-// 84..127: same data to the same place).  Index entries become record numbers once per segment;
+// a wave loads 4 records as 296 half-granules of 8 bytes with 5 loads of 64 lanes (slots
+// 296..319 repeat slots 232..255: same data to the same place).  Consecutive lanes hold
+// consecutive half-granules, so their 16-byte bf16 conversions land side by side in LDS (whole
+// granules per lane wrote 32-byte-strided halves, and a fifth of the kernel's LDS cycles were
+// bank conflicts).  Index entries become record numbers once per segment;
 // an unused entry (or one past the list) becomes -1, which reads record 0 and is marked unused.
 // Loads take 64-bit addresses, so the record pool has no size limit.
-constexpr int kGather = 3;
+constexpr int kGather = 5;
 // output staging: a wave's 16 rows x 256 values (fp32 1 KB, bf16 512 B per row) at this row pitch
 constexpr int kOutPitch = 1040;
 
@@ -182,9 +187,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     // (+16 for the second half of the tokens), dims 16*dt + 8*((l16&3)>>1) + 4*(l16&1)
     const int vaddr = (4 * g4 + (l16 >> 2)) * kRowA16 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8 + 32 * 16 * h;
 
-    // ---- sparse gathers: load i of this lane fetches granule g_off/16 of record g_tok/4 of the
-    // chunk and stores it at g_dst of the ring slot: codes as 16 bf16 (32 B, the second half at
-    // g_dst ^ 16), a scale granule as its raw first dword
+    // ---- sparse gathers: load i of this lane fetches the 8 bytes at g_off of record g_tok/4 of
+    // the chunk and stores them at g_dst of the ring slot: codes as 8 bf16 (16 B), the first half
+    // of the scale granule as its raw first dword
     int g_tok[GATHER ? NG : 1], g_off[GATHER ? NG : 1], g_dst[GATHER ? NG : 1];
     if constexpr (FP4) {
         // lane: code granule lane & 15 (dims 32*(lane & 15) .. +31) of record lane >> 4
@@ -196,14 +201,15 @@ void mla_decode_rows_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kGather; ++i) {
             int sl = 64 * i + lane;
-            if (sl >= 4 * 37) sl -= 64;
-            const int tok = 4 * wave + sl / 37;
-            const int gran = sl % 37;
+            if (sl >= 8 * 37) sl -= 64;
+            const int tok = 4 * wave + sl / 74;
+            const int hg = sl % 74;
+            const int gran = hg >> 1, half = hg & 1;
             g_tok[i] = tok * 4;
-            g_off[i] = gran * 16;
-            g_dst[i] = gran == 36 ? kChunk16 + tok * 32
-                     : gran < 32  ? tok * kRowA16 + gran * 32
-                                  : kRegionB16 + tok * 128 + (((2 * (gran - 32)) ^ swzB(tok)) << 4);
+            g_off[i] = gran * 16 + half * 8;
+            g_dst[i] = gran == 36 ? kChunk16 + tok * 32 + half * 16
+                     : gran < 32  ? tok * kRowA16 + gran * 32 + half * 16
+                                  : kRegionB16 + tok * 128 + (((2 * (gran - 32) + half) ^ swzB(tok)) << 4);
         }
     }
     // gathered records (FP4: code rows) and the FP4 scale rows, addressed with 64-bit offsets
@@ -295,7 +301,9 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         // ---- sparse: load i of chunk c into registers; conversion of those registers into chunk
         // c's ring slot.  Chunks past the segment's end gather its last chunk again (unused slot).
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 gv[GATHER ? NG : 1];
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        using GV = std::conditional_t<FP4, u32x4, u32x2>;
+        GV gv[GATHER ? NG : 1];
         int g_rec[GATHER ? NG : 1];       // record of load i, -1: none (reads record 0)
         unsigned short g_sc = 0;      // FP4: the two scale bytes of this lane's 32 values
         // paged gathers of the current chunk (wave-uniform): record of its first token, and how
@@ -322,7 +330,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             }
             g_rec[i] = rec;
             const size_t rr = rec >= 0 ? (size_t)rec : 0;
-            const u32x4* gp = reinterpret_cast<const u32x4*>(pool + rr * REC + g_off[i]);
+            const GV* gp = reinterpret_cast<const GV*>(pool + rr * REC + g_off[i]);
             if constexpr (SHARED) gv[i] = *gp;
             else gv[i] = __builtin_nontemporal_load(gp);
             if constexpr (FP4)
@@ -357,14 +365,12 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         auto convert = [&](int c, int i) {
             char* slot = ring + (c % DEPTH) * C::BUF;
             // an unused entry converts to zeros (record 0's bytes, which it read, are not its own)
-            const u32x4 r = g_rec[i] < 0 ? u32x4{0u, 0u, 0u, 0u} : gv[i];
+            const GV r = g_rec[i] < 0 ? GV{} : gv[i];
             uint4 lo = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.x, r.y));
-            const uint4 hi = __builtin_bit_cast(uint4, fp8x8_to_bf16(r.z, r.w));
             // scale granule: the raw fp32 scale, NaN for an unused entry (masked off)
             const unsigned sc = g_rec[i] < 0 ? 0x7fc00000u : r.x;
             lo.x = g_off[i] == 36 * 16 ? sc : lo.x;
             *reinterpret_cast<uint4*>(slot + g_dst[i]) = lo;
-            *reinterpret_cast<uint4*>(slot + (g_dst[i] ^ 16)) = hi;
         };
 
         // ---- LDS fragments
