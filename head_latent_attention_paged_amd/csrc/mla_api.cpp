@@ -214,7 +214,7 @@ static mla_status_t decode_paged_impl(const void* q, const void* kcache, int64_t
     if (mla::launch_decode(a, false, s) != hipSuccess) return MLA_ERR_HIP;
     const hipError_t e = fused ? mla::launch_combine_fused(a, s)
                                : mla::launch_combine(a.part_o, a.part_lse, num_splits, 0, batch, M, out, lse, s,
-                                                     sinks, h_q);
+                                                     sinks, h_q, mla::decode_uses_wide(a, false));
     if (e != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }

@@ -698,22 +698,17 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own staging writes
-            if (final_out) {
-                char* obase = static_cast<char*>(a.out) + ((size_t)grp * a.M + row0) * (kDv * 2) + 512 * hf;
+            // bf16 rows: the output, or a split's partial (O of the split, normalised by its own
+            // sum), whose LSE stays fp32 (the partials of 128-row groups are large: bf16 halves
+            // the bytes the combine moves)
+            char* obase = final_out ? static_cast<char*>(a.out) + ((size_t)grp * a.M + row0) * (kDv * 2) + 512 * hf
+                                    : reinterpret_cast<char*>(a.part_o) + ((size_t)slot * a.M + row0) * (kDv * 2) + 512 * hf;
 #pragma unroll 4
-                for (int r = 0; r < kRowsWave; ++r) {
-                    const f4 v = *reinterpret_cast<const f4*>(stg + r * kOutPitch + ln * 16);
-                    if (r < nrow)
-                        *reinterpret_cast<uint2*>(obase + (size_t)r * (kDv * 2) + ln * 8) =
-                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-            } else {
-                char* pbase = reinterpret_cast<char*>(a.part_o) + ((size_t)slot * a.M + row0) * (kDv * 4) + 1024 * hf;
-#pragma unroll 4
-                for (int r = 0; r < kRowsWave; ++r) {
-                    const f4 v = *reinterpret_cast<const f4*>(stg + r * kOutPitch + ln * 16);
-                    if (r < nrow) *reinterpret_cast<f4*>(pbase + (size_t)r * (kDv * 4) + ln * 16) = v;
-                }
+            for (int r = 0; r < kRowsWave; ++r) {
+                const f4 v = *reinterpret_cast<const f4*>(stg + r * kOutPitch + ln * 16);
+                if (r < nrow)
+                    *reinterpret_cast<uint2*>(obase + (size_t)r * (kDv * 2) + ln * 8) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read back before the next half
         }

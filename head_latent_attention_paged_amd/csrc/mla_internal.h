@@ -101,9 +101,12 @@ mla_status_t decode_paged_scratch(const void* q, const void* kcache, int64_t num
                                   float softmax_scale, int causal,
                                   const int32_t* tile_meta, const int32_t* num_splits, int num_parts,
                                   void* out, float* lse, void* stream, ScratchSource scratch);
+// whether launch_decode runs the one-wave-per-SIMD kernel, whose partials are bf16
+bool decode_uses_wide(const AttnArgs& a, bool sparse);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* num_splits_prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
-                          hipStream_t stream, const float* sinks = nullptr, int h_q = 1);
+                          hipStream_t stream, const float* sinks = nullptr, int h_q = 1,
+                          bool bf16_parts = false);
 // the combine of the fused decode: merged rows get the conjugate RoPE and the FP8 cast
 hipError_t launch_combine_fused(const AttnArgs& a, hipStream_t stream);
 

@@ -736,6 +736,19 @@ void mla_decode_m16_kernel(const AttnArgs a) {
 // K2: combine split-KV partials (one 128-thread half-block per output row)
 // --------------------------------------------------------------------------
 constexpr int kCombineGroup = 4;
+// partial O rows: fp32, or bf16 (BF16: the one-wave-per-SIMD kernel's 128-row groups)
+template <bool BF16>
+__device__ __forceinline__ f4 load_part4(const float* part_o, size_t row, int d) {
+    if constexpr (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(part_o) + (row * kDv + d) * 2);
+        return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+        return *reinterpret_cast<const f4*>(part_o + row * kDv + d);
+    }
+}
+
+template <bool BF16>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ prefix,
@@ -771,7 +784,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
         for (int j = 0; j < kCombineGroup; ++j) {
             const int i = base + (i0 + j < n ? i0 + j : n - 1);    // (past n: a repeat, unused)
             li[j] = part_lse[(size_t)i * rows + r];
-            v[j] = *reinterpret_cast<const f4*>(part_o + ((size_t)i * rows + r) * kDv + d4 * 4);
+            v[j] = load_part4<BF16>(part_o, (size_t)i * rows + r, d4 * 4);
         }
         float mg = mu;
 #pragma unroll
@@ -947,14 +960,16 @@ static hipError_t launch_decode_t(const AttnArgs& a, int items, int R, hipStream
     return hipGetLastError();
 }
 
+bool decode_uses_wide(const AttnArgs& a, bool sparse) {
+    // the fused decode, whatever the rows; bf16 and FP4 pages with more than 64 rows (576-wide
+    // bf16 rows need a positive scale, which the kernel applies in the exponent)
+    if (sparse || a.kv_fp8) return false;
+    return a.fused || (a.M > kWideMinRows && (a.kv_fp4 || a.d_qk == kDv || a.scale_log2 > 0.f));
+}
+
 hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
     const Tiling t = choose_tiling(a.M);
-    // bf16 and FP4 pages with more than 64 rows: the one-wave-per-SIMD kernel (576-wide bf16
-    // rows need a positive scale, which it applies in the exponent)
-    // the fused decode: the one-wave-per-SIMD kernel, whatever the rows
-    if (!sparse && a.fused) return launch_decode_wide(a, stream);
-    if (!sparse && !a.kv_fp8 && a.M > kWideMinRows && (a.kv_fp4 || a.d_qk == kDv || a.scale_log2 > 0.f))
-        return launch_decode_wide(a, stream);
+    if (decode_uses_wide(a, sparse)) return launch_decode_wide(a, stream);
     // 512-wide rows (K and V): the row-split kernel, whatever the rows and the scale
     if (!sparse && a.d_qk == kDv) return launch_decode_rows(a, false, stream);
     if (!sparse && a.kv_fp8) {
@@ -1006,9 +1021,9 @@ __global__ __launch_bounds__(256) void mla_combine_fused_kernel(const AttnArgs a
         for (int j = 0; j < kCombineGroup; ++j) {
             const int i = base + (i0 + j < n ? i0 + j : n - 1);    // (past n: a repeat, unused)
             li[j] = a.part_lse[(size_t)i * rows + r];
-            const float* p = a.part_o + ((size_t)i * rows + r) * kDv + 4 * lane;
-            v[j][0] = *reinterpret_cast<const f4*>(p);
-            v[j][1] = *reinterpret_cast<const f4*>(p + 256);
+            // (the fused decode runs on the one-wave-per-SIMD kernel: bf16 partials)
+            v[j][0] = load_part4<true>(a.part_o, (size_t)i * rows + r, 4 * lane);
+            v[j][1] = load_part4<true>(a.part_o, (size_t)i * rows + r, 256 + 4 * lane);
         }
         float mg = mu;
 #pragma unroll
@@ -1078,10 +1093,15 @@ hipError_t launch_combine_fused(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* prefix,
                           int uniform_splits, int groups, int rows, void* out, float* lse,
-                          hipStream_t stream, const float* sinks, int h_q) {
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
-                       part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
-                       sinks, h_q);
+                          hipStream_t stream, const float* sinks, int h_q, bool bf16_parts) {
+    if (bf16_parts)
+        hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
+                           part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
+                           sinks, h_q);
+    else
+        hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
+                           part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
+                           sinks, h_q);
     return hipGetLastError();
 }
 
