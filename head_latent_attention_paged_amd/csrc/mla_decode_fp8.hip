@@ -22,6 +22,9 @@ constexpr int kChunk8 = 32;                    // tokens per chunk: half a page
 constexpr int kBuf = kChunk8 * kRec;           // 20 KB of records
 constexpr int kOps = kBuf / 1024;              // 20 copies of 64 lanes x 16 B per chunk
 constexpr int kStreams = 4;
+// LDS read prefetch distances (MFMA steps) of the K and V^T fragments
+constexpr int kPfK = 6;
+constexpr int kPfV = 6;
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_m16_fp8_kernel(const AttnArgs a) {
@@ -53,14 +56,12 @@ void mla_decode_m16_fp8_kernel(const AttnArgs a) {
         for (int e = 0; e < 8; ++e) vaddr[e] = vr * kRec + ((e ^ swz8(vr)) << 4) + (l16 & 1) * 8;
     }
     // copies: op j, lane: LDS byte 1024*j + 16*lane = record row rr, slot s, filled from granule
-    // s ^ swz8(rr) of the row
-    int c_row[kOps], c_gran[kOps];
+    // s ^ swz8(rr) of the row; c_off is that source offset in a whole chunk
+    auto copy_row = [&](int j) { return (64 * j + lane) / 40; };
+    auto copy_gran = [&](int j) { const int gg = 64 * j + lane; return ((gg % 40) ^ swz8(gg / 40)) << 4; };
+    unsigned c_off[kOps];
 #pragma unroll
-    for (int j = 0; j < kOps; ++j) {
-        const int gg = 64 * j + lane;
-        c_row[j] = gg / 40;
-        c_gran[j] = ((gg % 40) ^ swz8(gg / 40)) << 4;
-    }
+    for (int j = 0; j < kOps; ++j) c_off[j] = (unsigned)(copy_row(j) * kRec + copy_gran(j));
 
     bf16x8 qf[18];
     f4 acc[32];
@@ -86,6 +87,9 @@ void mla_decode_m16_fp8_kernel(const AttnArgs a) {
 
         // Wave ts handles chunks c = ts + 4k: half c & 1 of page (c >> 1) of the segment.  The
         // page numbers come 64 at a time into one register of the wave (lane i: page base + i).
+        // The window's load is waited for inside the reload branch (the empty asm reads it), so
+        // the common path carries no pending load: a wait there would be on the whole
+        // vector-memory counter, in-flight KV copies included.
         const int lo_page = t0 >> 6;
         int bt_base = -1000000, win = 0;
         auto page_of = [&](int p) {
@@ -93,6 +97,7 @@ void mla_decode_m16_fp8_kernel(const AttnArgs a) {
                 bt_base = p;
                 const int np = ceil_div(t1, kPage) - lo_page;
                 win = (lane < np - p) ? a.block_table[(size_t)grp * a.max_blocks + lo_page + p + lane] : 0;
+                asm volatile("" ::"v"(win));
             }
             return __builtin_amdgcn_readlane(win, p - bt_base);
         };
@@ -105,10 +110,15 @@ void mla_decode_m16_fp8_kernel(const AttnArgs a) {
             const int page = page_of(c >> 1);
             const char* base = static_cast<const char*>(a.kv) + ((size_t)page * kPage + (tb & 63)) * kRec;
             char* dst = bufs + b * kBuf;
+            if (nrows == kChunk8) {
 #pragma unroll
-            for (int j = 0; j < kOps; ++j) {
-                const int rr = min(c_row[j], nrows - 1);
-                dma16_s(base, (unsigned)(rr * kRec + c_gran[j]), dst + 1024 * j);
+                for (int j = 0; j < kOps; ++j) dma16_s(base, c_off[j], dst + 1024 * j);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kOps; ++j) {
+                    const int rr = min(copy_row(j), nrows - 1);
+                    dma16_s(base, (unsigned)(rr * kRec + copy_gran(j)), dst + 1024 * j);
+                }
             }
         };
 
@@ -124,18 +134,38 @@ void mla_decode_m16_fp8_kernel(const AttnArgs a) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             const int tb = t0 + c * kChunk8;
-            // S^T of the two tiles over 576 dims: four independent chains
+            // S^T of the two tiles over 576 dims: four independent chains.  Step i = 2*ks + t; the
+            // K fragment of step i + kPfK is read while step i converts and multiplies, and the
+            // schedule interleaves (read, 4 conversions, MFMA) per step so that one wave per SIMD
+            // keeps LDS reads in flight behind its MFMAs.
             f4 s2[2][2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) s2[t][0] = s2[t][1] = f4{0.f, 0.f, 0.f, 0.f};
+            auto kread = [&](int i) {
+                const int ks = i >> 1, t = i & 1;
+                return *reinterpret_cast<const uint2*>(buf + kaddr[t][ks & 3] + 128 * (ks >> 2));
+            };
+            uint2 kw[36];
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
+            for (int i = 0; i < kPfK; ++i) kw[i] = kread(i);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint2 w = *reinterpret_cast<const uint2*>(buf + kaddr[t][ks & 3] + 128 * (ks >> 2));
-                    s2[t][ks & 1] = mfma16(fp8x8_to_bf16(w.x, w.y), qf[ks], s2[t][ks & 1]);
-                }
+            for (int i = 0; i < 36; ++i) {
+                if (i + kPfK < 36) kw[i + kPfK] = kread(i + kPfK);
+                const int ks = i >> 1, t = i & 1;
+                s2[t][ks & 1] = mfma16(fp8x8_to_bf16(kw[i].x, kw[i].y), qf[ks], s2[t][ks & 1]);
+                if (i + kPfK < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
+            // the first V^T fragments, read before the softmax needs the scores
+            typedef int v2i __attribute__((ext_vector_type(2)));
+            auto vread = [&](int dt) {
+                return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(buf + vaddr[dt & 7] + 128 * (dt >> 3)));
+            };
+            v2i vw[32];
+#pragma unroll
+            for (int dt = 0; dt < kPfV; ++dt) vw[dt] = vread(dt);
             // mask and scale: token scale * softmax scale (log2 units)
             float x[2][4], tsc[2][4];
             float mx = -INFINITY;
@@ -178,12 +208,13 @@ void mla_decode_m16_fp8_kernel(const AttnArgs a) {
                 pk[2 * t + 1] = pack_bf16x2(p[2], p[3]);
             }
             const bf16x8 pT = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            typedef int v2i __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int dt = 0; dt < 32; ++dt) {
-                const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(buf + vaddr[dt & 7] + 128 * (dt >> 3)));
-                acc[dt] = mfma16(fp8x8_to_bf16((unsigned)w[0], (unsigned)w[1]), pT, acc[dt]);
+                if (dt + kPfV < 32) vw[dt + kPfV] = vread(dt + kPfV);
+                acc[dt] = mfma16(fp8x8_to_bf16((unsigned)vw[dt][0], (unsigned)vw[dt][1]), pT, acc[dt]);
+                if (dt + kPfV < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             }
         }
 
