@@ -612,14 +612,30 @@ void mla_decode_m16_kernel(const AttnArgs a) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             const int tb = t0 + c * kMChunk;
-            // S^T[token][row] over 576 dims: two accumulators (even / odd k steps) break the chain
+            // S^T[token][row] over 576 dims: two accumulators (even / odd k steps) break the chain.
+            // K fragments are read four MFMA steps ahead and V^T fragments six, with the schedule
+            // pinned to (read, MFMA) pairs so that the one wave per SIMD keeps LDS reads in flight.
             f4 sacc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+            auto kread = [&](int ks) {
+                const int off = ks < 16 ? kA[ks & 1] + 128 * (ks >> 1) : kB[ks & 1];
+                return *reinterpret_cast<const bf16x8*>(buf + off);
+            };
+            bf16x8 kw[18];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kw[i] = kread(i);
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                const int off = ks < 16 ? kA[ks & 1] + 128 * (ks >> 1) : kB[ks & 1];
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + off);
-                sacc[ks & 1] = mfma16(kf, qf[ks], sacc[ks & 1]);
+                if (ks + 4 < 18) kw[ks + 4] = kread(ks + 4);
+                sacc[ks & 1] = mfma16(kw[ks], qf[ks], sacc[ks & 1]);
+                if (ks + 4 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
+            auto vread = [&](int dt) {
+                return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(buf + vb[dt & 3] + 128 * (dt >> 2)));
+            };
+            short4v vw[32];
+#pragma unroll
+            for (int dt = 0; dt < 6; ++dt) vw[dt] = vread(dt);
             const f4 sv = sacc[0] + sacc[1];
             float x[4];
             float mx = -INFINITY;
@@ -650,9 +666,10 @@ void mla_decode_m16_kernel(const AttnArgs a) {
             const short4v pT = __builtin_bit_cast(short4v, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
 #pragma unroll
             for (int dt = 0; dt < 32; ++dt) {
-                const short4v vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4v*)(buf + vb[dt & 3] + 128 * (dt >> 2)));
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pT, acc[dt], 0, 0, 0);
+                if (dt + 6 < 32) vw[dt + 6] = vread(dt + 6);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vw[dt], pT, acc[dt], 0, 0, 0);
+                if (dt + 6 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             }
         }
 
