@@ -750,18 +750,79 @@ void mla_decode_m16_kernel(const AttnArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// K2: combine split-KV partials (one 128-thread half-block per output row)
+// K2: combine split-KV partials (one wave per output row, 8 dims per lane)
 // --------------------------------------------------------------------------
-constexpr int kCombineGroup = 4;
-// partial O rows: fp32, or bf16 (BF16: the one-wave-per-SIMD kernel's 128-row groups)
+// splits loaded together per round trip: 4 for the bf16 partials (at most a few splits per row),
+// 8 for the fp32 ones (the 16-row kernel splits long sequences into many parts)
 template <bool BF16>
-__device__ __forceinline__ f4 load_part4(const float* part_o, size_t row, int d) {
+constexpr int combine_group() { return BF16 ? 4 : 8; }
+// dims d .. d+7 of a partial O row: fp32 (two 16-byte loads), or bf16 (one 16-byte load; BF16:
+// the one-wave-per-SIMD kernel's 128-row groups)
+template <bool BF16>
+__device__ __forceinline__ void load_part8(const float* part_o, size_t row, int d, f4& lo, f4& hi) {
     if constexpr (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(part_o) + (row * kDv + d) * 2);
-        return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(part_o) + (row * kDv + d) * 2);
+        lo = f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        hi = f4{__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
+                __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)};
     } else {
-        return *reinterpret_cast<const f4*>(part_o + row * kDv + d);
+        lo = *reinterpret_cast<const f4*>(part_o + row * kDv + d);
+        hi = *reinterpret_cast<const f4*>(part_o + row * kDv + d + 4);
+    }
+}
+
+// The LSE-weighted merge of one row's n partials (slots base .. base+n-1) for the lane's dims
+// d .. d+7: o[0..1] = sum_i exp(lse_i - mu) O_i / wsum, with an attention sink sk as one more
+// term of the denominator (LSE = the sink, no value).  The splits go in groups of G whose LSEs
+// and values are loaded together (one memory round trip per group); mu is the running
+// maximum, and a group that raises it rescales what the earlier groups summed.
+template <bool BF16>
+__device__ __forceinline__ void merge_row(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                          int base, int n, int rows, int r, int d, float sk,
+                                          f4 (&o)[2], float& mu, float& wsum) {
+    mu = sk;
+    wsum = sk != -INFINITY ? 1.f : 0.f;
+    o[0] = o[1] = f4{0.f, 0.f, 0.f, 0.f};
+    constexpr int G = combine_group<BF16>();
+    for (int i0 = 0; i0 < n; i0 += G) {
+        float li[G];
+        f4 v[G][2];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            // (n is the same for the whole wave: the branch does not diverge)
+            li[j] = -INFINITY;
+            v[j][0] = v[j][1] = f4{0.f, 0.f, 0.f, 0.f};
+            if (i0 + j < n) {
+                const size_t i = (size_t)(base + i0 + j) * rows + r;
+                li[j] = part_lse[i];
+                load_part8<BF16>(part_o, i, d, v[j][0], v[j][1]);
+            }
+        }
+        float mg = mu;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (i0 + j < n) mg = fmaxf(mg, li[j]);
+        if (mg == -INFINITY) continue;                          // nothing finite so far
+        const float sc = mu == -INFINITY ? 0.f : expf(mu - mg);  // mu <= mg
+        wsum *= sc;
+        o[0] *= sc;
+        o[1] *= sc;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (i0 + j < n && li[j] != -INFINITY) {
+                const float w = expf(li[j] - mg);
+                wsum += w;
+                o[0] += v[j][0] * w;
+                o[1] += v[j][1] * w;
+            }
+        }
+        mu = mg;
+    }
+    if (mu != -INFINITY) {
+        const float iw = 1.f / wsum;
+        o[0] *= iw;
+        o[1] *= iw;
     }
 }
 
@@ -773,8 +834,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
                                                           __bf16* __restrict__ out, float* __restrict__ lse,
                                                           const float* __restrict__ sinks, int h_q) {
     const int grp = blockIdx.x;
-    const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
-    const int d4 = threadIdx.x & 127;
+    const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (r >= rows) return;
     int base, n;
     if (prefix) {
@@ -785,46 +846,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
         n = uniform_splits;
     }
     if (n == 1) return;   // the decode kernel wrote this row directly
-    __bf16* orow = out + ((size_t)grp * rows + r) * kDv + d4 * 4;
-    // an attention sink is one more term of the denominator, with LSE = the sink and no value
     const float sk = sinks ? sinks[r % h_q] : -INFINITY;
-    // The splits go in groups of kCombineGroup whose LSEs and values are loaded together (one
-    // memory round trip per group, not one for the maximum and one for the sum).  mu is the
-    // running maximum; a group that raises it rescales what the earlier groups summed.
-    float mu = sk;
-    float wsum = sk != -INFINITY ? 1.f : 0.f;
-    f4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < n; i0 += kCombineGroup) {
-        float li[kCombineGroup];
-        f4 v[kCombineGroup];
-#pragma unroll
-        for (int j = 0; j < kCombineGroup; ++j) {
-            const int i = base + (i0 + j < n ? i0 + j : n - 1);    // (past n: a repeat, unused)
-            li[j] = part_lse[(size_t)i * rows + r];
-            v[j] = load_part4<BF16>(part_o, (size_t)i * rows + r, d4 * 4);
-        }
-        float mg = mu;
-#pragma unroll
-        for (int j = 0; j < kCombineGroup; ++j)
-            if (i0 + j < n) mg = fmaxf(mg, li[j]);
-        if (mg == -INFINITY) continue;                          // nothing finite so far
-        const float sc = mu == -INFINITY ? 0.f : expf(mu - mg);  // mu <= mg
-        wsum *= sc;
-        o *= sc;
-#pragma unroll
-        for (int j = 0; j < kCombineGroup; ++j) {
-            if (i0 + j < n && li[j] != -INFINITY) {
-                const float w = expf(li[j] - mg);
-                wsum += w;
-                o += v[j] * w;
-            }
-        }
-        mu = mg;
-    }
-    if (mu != -INFINITY) o *= 1.f / wsum;
-    const uint2 pk = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    *reinterpret_cast<uint2*>(orow) = pk;
-    if (d4 == 0) lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
+    f4 o[2];
+    float mu, wsum;
+    merge_row<BF16>(part_o, part_lse, base, n, rows, r, 8 * lane, sk, o, mu, wsum);
+    const uint4 pk = make_uint4(pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]),
+                                pack_bf16x2(o[1][0], o[1][1]), pack_bf16x2(o[1][2], o[1][3]));
+    *reinterpret_cast<uint4*>(out + ((size_t)grp * rows + r) * kDv + 8 * lane) = pk;
+    if (lane == 0) lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
 }
 
 // --------------------------------------------------------------------------
@@ -1017,7 +1046,7 @@ hipError_t launch_decode(const AttnArgs& a, bool sparse, hipStream_t stream) {
 // The combine of the fused decode: one wave per output row of a split sequence.  The LSE-weighted
 // merge of the row's partials (as mla_combine_kernel), then the conjugate rotation of dims
 // 448..511 by the query token's angles and the FP8 cast with one scale per row (amax / 448).
-// Lane l holds dims 4l..4l+3 and 256 + 4l..+3.
+// Lane l holds dims 8l .. 8l+7.
 __global__ __launch_bounds__(256) void mla_combine_fused_kernel(const AttnArgs a) {
     const int grp = blockIdx.x;
     const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -1028,54 +1057,19 @@ __global__ __launch_bounds__(256) void mla_combine_fused_kernel(const AttnArgs a
     const int n = a.num_splits[grp + 1] - base;
     if (n == 1) return;   // the decode kernel wrote this row directly
     const float sk = a.sinks ? a.sinks[r % a.h_q] : -INFINITY;
-    float mu = sk;
-    float wsum = sk != -INFINITY ? 1.f : 0.f;
-    f4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int i0 = 0; i0 < n; i0 += kCombineGroup) {
-        float li[kCombineGroup];
-        f4 v[kCombineGroup][2];
-#pragma unroll
-        for (int j = 0; j < kCombineGroup; ++j) {
-            const int i = base + (i0 + j < n ? i0 + j : n - 1);    // (past n: a repeat, unused)
-            li[j] = a.part_lse[(size_t)i * rows + r];
-            // (the fused decode runs on the one-wave-per-SIMD kernel: bf16 partials)
-            v[j][0] = load_part4<true>(a.part_o, (size_t)i * rows + r, 4 * lane);
-            v[j][1] = load_part4<true>(a.part_o, (size_t)i * rows + r, 256 + 4 * lane);
-        }
-        float mg = mu;
-#pragma unroll
-        for (int j = 0; j < kCombineGroup; ++j)
-            if (i0 + j < n) mg = fmaxf(mg, li[j]);
-        if (mg == -INFINITY) continue;                          // nothing finite so far
-        const float sc = mu == -INFINITY ? 0.f : expf(mu - mg);  // mu <= mg
-        wsum *= sc;
-        o[0] *= sc;
-        o[1] *= sc;
-#pragma unroll
-        for (int j = 0; j < kCombineGroup; ++j) {
-            if (i0 + j < n && li[j] != -INFINITY) {
-                const float w = expf(li[j] - mg);
-                wsum += w;
-                o[0] += v[j][0] * w;
-                o[1] += v[j][1] * w;
-            }
-        }
-        mu = mg;
-    }
-    if (mu != -INFINITY) {
-        const float iw = 1.f / wsum;
-        o[0] *= iw;
-        o[1] *= iw;
-    }
-    if (4 * lane + 256 >= kRopeStart) {
+    f4 o[2];
+    float mu, wsum;
+    // (the fused decode runs on the one-wave-per-SIMD kernel: bf16 partials)
+    merge_row<true>(a.part_o, a.part_lse, base, n, rows, r, 8 * lane, sk, o, mu, wsum);
+    if (8 * lane >= kRopeStart) {
         const float* cs = a.rope_cs + ((size_t)grp * a.s_q + r / a.h_q) * 64;
-        const int i0 = (4 * lane + 256 - kRopeStart) >> 1;
+        const int i0 = (8 * lane - kRopeStart) >> 1;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const float c = cs[i0 + j], sn = cs[32 + i0 + j];
-            const float u = o[1][2 * j], w = o[1][2 * j + 1];
-            o[1][2 * j] = u * c + w * sn;
-            o[1][2 * j + 1] = w * c - u * sn;
+            const float u = o[j >> 1][2 * (j & 1)], w = o[j >> 1][2 * (j & 1) + 1];
+            o[j >> 1][2 * (j & 1)] = u * c + w * sn;
+            o[j >> 1][2 * (j & 1) + 1] = w * c - u * sn;
         }
     }
     float amax = 0.f;
@@ -1088,15 +1082,16 @@ __global__ __launch_bounds__(256) void mla_combine_fused_kernel(const AttnArgs a
     const float fscale = fmaxf(amax, 1.17549435e-38f) / kE4m3Max;
     const float finv = 1.f / fscale;
     unsigned char* orow = static_cast<unsigned char*>(a.out) + ((size_t)grp * rows + r) * kDv;
+    int wv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(o[h][e] * finv, -kE4m3Max), kE4m3Max);
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
-        *reinterpret_cast<int*>(orow + 256 * h + 4 * lane) = w;
+        wv[h] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
     }
+    *reinterpret_cast<uint2*>(orow + 8 * lane) = make_uint2((unsigned)wv[0], (unsigned)wv[1]);
     if (lane == 0) {
         a.out_scale[(size_t)grp * rows + r] = fscale;
         a.lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
@@ -1112,11 +1107,11 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, const int3
                           int uniform_splits, int groups, int rows, void* out, float* lse,
                           hipStream_t stream, const float* sinks, int h_q, bool bf16_parts) {
     if (bf16_parts)
-        hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
+        hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(groups, (rows + 3) / 4), dim3(256), 0, stream,
                            part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
                            sinks, h_q);
     else
-        hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
+        hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(groups, (rows + 3) / 4), dim3(256), 0, stream,
                            part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
                            sinks, h_q);
     return hipGetLastError();
