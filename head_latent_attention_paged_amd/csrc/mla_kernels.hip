@@ -507,15 +507,19 @@ void mla_decode_kernel(const AttnArgs a) {
 // Four independent token streams per block (one per wave, one wave per SIMD).  Each stream
 // double-buffers 16-token chunks (18 KB) that go HBM -> LDS by direct copies, so one chunk is
 // always in flight while the previous one is multiplied; the streams merge at the end.
+// Region A (dims 0..511) keeps a token's 1 KB unswizzled at a 1056-byte stride: the 16 tokens x
+// 64 B of a K read and the transposing V^T reads fall on distinct banks (the 1024-byte stride
+// with the chunk kernels' XOR swizzle left 47% of this kernel's LDS cycles in bank conflicts).
 // --------------------------------------------------------------------------
 constexpr int kMChunk = 16;
-constexpr int kMBuf = kMChunk * kRowA + kMChunk * 128;      // 18 KB: region A then region B
-constexpr int kMRegionB = kMChunk * kRowA;
+constexpr int kMRowA = 1056;                                 // region A row stride (1 KB + 32 B)
+constexpr int kMBuf = kMChunk * kMRowA + kMChunk * 128;     // region A then region B
+constexpr int kMRegionB = kMChunk * kMRowA;
 constexpr int kMDmaOps = kMChunk + 2;                        // copy instructions per chunk and wave
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_m16_kernel(const AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[4 * 2 * kMBuf];   // 144 KB
+    __shared__ __attribute__((aligned(16))) char smem[4 * 2 * kMBuf];   // 148 KB
     __shared__ int s_pages[4][64];                                       // per-wave page window
     const int lane = threadIdx.x & 63;
     const int ts = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // stream = wave
@@ -527,7 +531,7 @@ void mla_decode_m16_kernel(const AttnArgs a) {
     int kA[2], kB[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-        kA[par] = l16 * kRowA + (((4 * par + g4) ^ swz(l16)) << 4);
+        kA[par] = l16 * kMRowA + ((4 * par + g4) << 4);
         kB[par] = kMRegionB + l16 * 128 + (((4 * par + g4) ^ swz(l16)) << 4);
     }
     // V^T fragment (A operand of O^T, 16x16x16): tokens 4*g4..+3, dims 16*dt + l16 via one
@@ -536,7 +540,7 @@ void mla_decode_m16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
         const int row = 4 * g4 + (l16 >> 2);
-        vb[d4] = lds_a(row, 2 * d4 + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+        vb[d4] = row * kMRowA + ((2 * d4 + ((l16 & 3) >> 1)) << 4) + (l16 & 1) * 8;
     }
 
     bf16x8 qf[18];
@@ -587,7 +591,7 @@ void mla_decode_m16_kernel(const AttnArgs a) {
 #pragma unroll
             for (int row = 0; row < kMChunk; ++row) {
                 const int rr = min(row, nrows - 1);   // rows past the end repeat the last row (weight 0)
-                dma16(base + rr * kRowBytes + ((lane ^ swz(row)) << 4), dst + row * kRowA);
+                dma16(base + rr * kRowBytes + (lane << 4), dst + row * kMRowA);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
