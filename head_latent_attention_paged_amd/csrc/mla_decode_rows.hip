@@ -238,11 +238,19 @@ void mla_decode_rows_kernel(const AttnArgs a) {
 
         // sparse: the split's index list (at most kMaxSparseSplit entries) goes to LDS once, as
         // record numbers (-1 for unused entries and up to the end of the last chunk)
+        // (all of a thread's loads are issued before any is waited for: one memory round trip)
         if constexpr (SPARSE) {
-            for (int e = threadIdx.x; e < nch * kChunk; e += kWaves * 64) {
-                long long v = -1;
-                if (e < t1 - t0) v = a.indices[(size_t)grp * a.topk + t0 + e];
-                lidx[e] = (v >= 0 && v < a.kv_rows) ? (int)v : -1;
+            constexpr int kPer = kMaxSparseSplit / (kWaves * 64);
+            int v[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int e = threadIdx.x + j * kWaves * 64;
+                v[j] = e < t1 - t0 ? a.indices[(size_t)grp * a.topk + t0 + e] : -1;
+            }
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int e = threadIdx.x + j * kWaves * 64;
+                if (e < nch * kChunk) lidx[e] = (v[j] >= 0 && v[j] < a.kv_rows) ? v[j] : -1;
             }
             __syncthreads();
         }
