@@ -12,9 +12,12 @@
 // from LDS feeds a 32-row MFMA, twice the work per LDS byte of a 16-row tile, and the 512 O^T
 // accumulators of a wave's rows live in the accumulation registers.
 //
-// Chunk loop, iteration k: Q.K^T(k) with the copies of chunk k+2 spread over its MFMAs, then
-// P.V(k-1) with the masking and probabilities of chunk k spread over its MFMAs.  One workgroup
-// barrier per chunk guards the ring of KV chunks, which all four waves fill.
+// Chunk loop, iteration k: Q.K^T(k) with the copies of chunk k+3 spread over its MFMAs, the
+// masking and the first token step's probabilities of chunk k, then P.V(k) with the second
+// step's probabilities and the lane's maximum computed between its MFMAs.  A chunk's slot frees
+// as soon as its own P.V is done, so three chunks are in flight while one is used (timing copies
+// without the HBM copies ran the compute-bound shapes 17-19% faster: the kernel waits on its
+// copies).  One workgroup barrier per chunk guards the ring, which all four waves fill.
 //
 // Softmax reference: a row's reference is the maximum of its first chunk and never moves inside
 // a pass, so the accumulators are touched only by MFMAs; p = 2^(s - m) <= 2^kRefSlack keeps bf16
@@ -89,10 +92,10 @@ struct Cfg {
     static constexpr int OPS = D == kDqk ? 9 : 8;          // 1 KB copies per wave per chunk
     // a ring slot: a bf16 chunk, and for gathered records their 32 token scales (fp32)
     static constexpr int BUF = kChunk16 + (GATHER ? kChunk * 4 : 0);
-    // ring: chunk k-1 (P.V), chunk k (Q.K^T) and, copied, two in flight; gathered, chunk k+1
-    // (converted while chunk k+2 is loaded into registers)
+    // ring: chunk k (Q.K^T, then P.V) and, copied, three in flight; gathered, chunk k+1
+    // (converted while chunk k+2 is loaded into registers) and a spare slot
     static constexpr int DEPTH = GATHER ? 3 : 4;
-    static constexpr int AHEAD = DEPTH - 2;
+    static constexpr int AHEAD = DEPTH - 1;
     static constexpr int RING = DEPTH * BUF;
     static constexpr int PAGES = kWaves * 64 * 4;          // per-wave page windows
     static constexpr int VOTES = kWaves * 4;
@@ -119,6 +122,9 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     constexpr bool RAWMAX = !GATHER && D == kDqk;
     using C = Cfg<GATHER, D>;
     constexpr int DEPTH = C::DEPTH, AHEAD = C::AHEAD;
+    // P.V of a chunk right after its own Q.K^T (see the chunk loop), except for the fused decode
+    // over FP4 pages
+    constexpr bool kEarlyPV = !(GATHER && FUSED);
     // FP4 gathers per lane per chunk: a wave loads 8 rows of 16 code granules (plus 2 scale
     // bytes per granule), 128 granules in 2 loads of 64 lanes
     constexpr int NG = 2;
@@ -421,7 +427,7 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         };
         // O^T += V^T P^T over chunk c: token step s (16 tokens) for all 16 dim tiles, s = 0, 1
         // (the two steps of a tile are 16 MFMAs apart); side(i) runs between the MFMAs
-        auto pv = [&](int c, const bf16x8 (&pb)[2], auto&& side) {
+        auto pv = [&](int c, bf16x8 (&pb)[2], auto&& side) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
             bf16x8 vf[VPF];
             auto vidx = [](int n) { return 2 * (n & 15) + (n >> 4); };     // MFMA n: tile n&15, step n>>4
@@ -436,7 +442,9 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         };
 
         // ---- masking of chunk c: lane value v is token 8*(v>>2) + 4*g + (v&3) of this lane's row
-        auto mask = [&](int c, f16v& s, float& mx) {
+        // (ROWMAX: also the row's largest masked score over both lanes, for chunk 0's reference)
+        auto mask = [&](int c, f16v& s, float& mx, auto rowmax_c) {
+            constexpr bool ROWMAX = decltype(rowmax_c)::value;
             const int tb = t0 + c * kChunk;
             const int bnd = vis_end - tb;                             // valid: 8*(v>>2) + (v&3) < bnd
             float m = -INFINITY;
@@ -478,18 +486,22 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                     m = fmaxf(m, s[v]);
                 }
             }
-            if constexpr (RAWMAX) m *= a.scale_log2;   // a positive scale commutes with the max
-            m = fmaxf(m, xor32(m));
-            mx = m;
+            if constexpr (ROWMAX) {
+                if constexpr (RAWMAX) m *= a.scale_log2;   // a positive scale commutes with the max
+                m = fmaxf(m, xor32(m));
+                mx = m;
+            }
         };
         // probabilities under the row's reference of token step h2 (lane values 8*h2 .. +7): the
         // bf16 B operand of that step of P.V
-        auto probs = [&](int c, const f16v& s, int h2) -> bf16x8 {
+        // (mx: the running maximum of the masked scores taken)
+        auto probs = [&](int c, const f16v& s, int h2, float& mx) -> bf16x8 {
             const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = s[8 * h2 + e];
+                mx = fmaxf(mx, x);
                 if constexpr (RAWMAX) p[e] = exp2_fast(__builtin_fmaf(x, a.scale_log2, -m_use));
                 else p[e] = exp2_fast(x - m_use);
                 l_run += p[e];
@@ -507,7 +519,6 @@ void mla_decode_wide_kernel(const AttnArgs a) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) acc[t] = f16v{};
             bool outgrown = false;
-            bf16x8 pb[2];
             if constexpr (!GATHER) {
 #pragma unroll
                 for (int c = 0; c < AHEAD; ++c) {
@@ -524,54 +535,97 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                 for (int i = 0; i < NG; ++i) gather(1, i);
             }
             __syncthreads();
-            // chunk 0: Q.K^T with the copies of chunk 2 (gathered: the conversion of chunk 1 and
-            // the loads of chunk 2) spread over it, reference, probabilities
-            {
-                f16v s;
-                if constexpr (!GATHER) {
-                    const Plan p = plan_for(AHEAD);
-                    qk(0, s, [&](int ks) {
-                        if ((ks & 3) == 1 && ks / 4 < C::OPS) copy_op(p, ks / 4);
-                    });
-                } else {
-                    qk(0, s, [&](int ks) { gather_side(1, ks); });
-                }
-                float mx;
-                mask(0, s, mx);
-                m_lane = fmaxf(m_lane, mx);
-                if (m_run == -INFINITY) m_run = mx;     // a restart pass keeps its reference
-                pb[0] = probs(0, s, 0);
-                pb[1] = probs(0, s, 1);
-            }
-            for (int k = 1; k < nch; ++k) {
-                if constexpr (!GATHER) wait_chunk();
-                // chunk k in LDS for every wave; slot (k-2) % DEPTH free (gathered: slot (k+1) %
-                // DEPTH, whose chunk k-2 was last read by P.V in the previous iteration)
-                __syncthreads();
-                f16v s;
-                if constexpr (!GATHER) {
-                    const Plan p = plan_for(k + AHEAD);
-                    qk(k, s, [&](int ks) {
-                        if ((ks & 3) == 1 && ks / 4 < C::OPS) copy_op(p, ks / 4);
-                    });
-                } else {
-                    qk(k, s, [&](int ks) { gather_side(k + 1, ks); });
-                }
-                // O^T += V^T P^T (k-1) while S^T(k) is masked and turned into probabilities (step
-                // 0's operand once the MFMAs of step 0 are issued, step 1's after the last)
+            // one chunk after its Q.K^T: masking, the probabilities of token step 0, then P.V of
+            // the chunk with step 1's probabilities and the lane's largest masked score computed
+            // between its MFMAs.  The row's reference comes from chunk 0 (a restart pass keeps
+            // its own), so a later chunk's probabilities need no maximum of their own; its lane
+            // maximum feeds the restart vote and reference (the row's is taken at the restart).
+            auto finish = [&](int c, f16v& s, auto first_c) {
+                constexpr bool FIRST = decltype(first_c)::value;
                 float mx = 0.f;
-                pv(k - 1, pb, [&](int n) {
-                    if (n == 3) {
-                        mask(k, s, mx);
-                        m_lane = fmaxf(m_lane, mx);
-                        // also true for a finite score in a row without a reference
-                        outgrown = outgrown | (mx > m_run + kRefSlack);
-                    }
-                    if (n == 16) pb[0] = probs(k, s, 0);
+                mask(c, s, mx, std::integral_constant<bool, FIRST>{});
+                if constexpr (FIRST) {
+                    m_lane = fmaxf(m_lane, mx);
+                    if (m_run == -INFINITY) m_run = mx;
+                }
+                bf16x8 pb[2];
+                float ml = -INFINITY;
+                pb[0] = probs(c, s, 0, ml);
+                pv(c, pb, [&](int n) {
+                    if (n == 2) pb[1] = probs(c, s, 1, ml);
                 });
-                pb[1] = probs(k, s, 1);
+                if constexpr (!FIRST) {
+                    if constexpr (RAWMAX) ml *= a.scale_log2;   // a positive scale commutes with the max
+                    m_lane = fmaxf(m_lane, ml);
+                    // also true for a finite score in a row without a reference
+                    outgrown = outgrown | (ml > m_run + kRefSlack);
+                }
+            };
+            if constexpr (kEarlyPV) {
+                // chunk 0: Q.K^T with the copies of chunk AHEAD (gathered: the conversion of chunk 1
+                // and the loads of chunk 2) spread over it, then its reference, probabilities and P.V
+                {
+                    f16v s;
+                    if constexpr (!GATHER) {
+                        const Plan p = plan_for(AHEAD);
+                        qk(0, s, [&](int ks) {
+                            if ((ks & 3) == 1 && ks / 4 < C::OPS) copy_op(p, ks / 4);
+                        });
+                    } else {
+                        qk(0, s, [&](int ks) { gather_side(1, ks); });
+                    }
+                    finish(0, s, std::true_type{});
+                }
+                for (int k = 1; k < nch; ++k) {
+                    if constexpr (!GATHER) wait_chunk();
+                    // chunk k in LDS for every wave; the slot of chunk k-1, whose P.V every wave has
+                    // done, free for the copies of chunk k+AHEAD (gathered: slot (k+1) % DEPTH, for the
+                    // conversion of chunk k+1)
+                    __syncthreads();
+                    f16v s;
+                    if constexpr (!GATHER) {
+                        const Plan p = plan_for(k + AHEAD);
+                        qk(k, s, [&](int ks) {
+                            if ((ks & 3) == 1 && ks / 4 < C::OPS) copy_op(p, ks / 4);
+                        });
+                    } else {
+                        qk(k, s, [&](int ks) { gather_side(k + 1, ks); });
+                    }
+                    finish(k, s, std::false_type{});
+                }
+            } else {
+                // (the fused decode over FP4 pages, whose registers do not fit the order above:
+                // P.V(k-1) runs after Q.K^T(k), with chunk k's masking and probabilities spread
+                // over its MFMAs)
+                bf16x8 pb[2];
+                {
+                    f16v s;
+                    qk(0, s, [&](int ks) { gather_side(1, ks); });
+                    float mx, ml = -INFINITY;
+                    mask(0, s, mx, std::true_type{});
+                    m_lane = fmaxf(m_lane, mx);
+                    if (m_run == -INFINITY) m_run = mx;
+                    pb[0] = probs(0, s, 0, ml);
+                    pb[1] = probs(0, s, 1, ml);
+                }
+                for (int k = 1; k < nch; ++k) {
+                    __syncthreads();
+                    f16v s;
+                    qk(k, s, [&](int ks) { gather_side(k + 1, ks); });
+                    float mx = 0.f, ml = -INFINITY;
+                    pv(k - 1, pb, [&](int n) {
+                        if (n == 3) {
+                            mask(k, s, mx, std::true_type{});
+                            m_lane = fmaxf(m_lane, mx);
+                            // also true for a finite score in a row without a reference
+                            outgrown = outgrown | (mx > m_run + kRefSlack);
+                        }
+                        if (n == 16) pb[0] = probs(k, s, 0, ml);
+                    });
+                    pb[1] = probs(k, s, 1, ml);
+                }
+                pv(nch - 1, pb, no_side);
             }
-            pv(nch - 1, pb, no_side);
             // the copies past the segment's end land; every wave's vote visible
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             // (the ballot runs on the whole wave: inside the lane-0 branch it would see one row)
