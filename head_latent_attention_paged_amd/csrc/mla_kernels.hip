@@ -547,17 +547,25 @@ void mla_decode_m16_kernel(const AttnArgs a) {
     f4 acc[32];
     float m_run, l_run;
 
-    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
-        const int r = l16;
-        {
-            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (r < a.M ? r : 0)) * (kDqk * 2);
+    // Q of a segment: the workgroup copies its 16 rows (18 KB, rows past M repeat row 0) into
+    // wave 0's second buffer, each wave a quarter; every wave then reads its fragments from there
+    char* const qs = smem + kMBuf;
+    auto copy_q = [&](int grp) {
+        const char* qg = static_cast<const char*>(a.q) + (size_t)grp * a.M * (kDqk * 2);
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
-                uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
-                if (r >= a.M) v = make_uint4(0, 0, 0, 0);
-                qf[ks] = __builtin_bit_cast(bf16x8, v);
+        for (int i = 0; i < 5; ++i) {
+            const int j = ts + 4 * i;
+            if (j < 18) {
+                const unsigned e = 1024 * j + 16 * lane;
+                const unsigned row = e / (kDqk * 2), col = e % (kDqk * 2);
+                dma16_s_shared(qg, ((int)row < a.M ? row : 0) * (kDqk * 2) + col, qs + 1024 * j);
             }
         }
+    };
+
+    // win0: lane i holds the block-table entry of page t0/64 + i (loaded by the caller)
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot, int win0) {
+        const int r = l16;
         m_run = -INFINITY;
         l_run = 0.f;
 #pragma unroll
@@ -566,10 +574,12 @@ void mla_decode_m16_kernel(const AttnArgs a) {
         const int nch = ceil_div(t1 - t0, kMChunk);
 
         // Wave ts handles chunks c = ts + 4k: rows 16*ts..16*ts+15 of page lo + k.  The page
-        // numbers come 64 at a time into a per-wave LDS window, so looking one up never waits
-        // on the vector-memory counter (which also counts the in-flight KV copies).
+        // numbers come 64 at a time into a per-wave LDS window (the first from the caller), so
+        // looking one up never waits on the vector-memory counter (which also counts the
+        // in-flight KV copies).
         const int lo_page = t0 >> 6;
-        int bt_base = -1000000;
+        int bt_base = 0;
+        s_pages[ts][lane] = win0;
         auto page_of = [&](int k) {
             if (k - bt_base >= 64 || k < bt_base) {
                 bt_base = k;
@@ -605,6 +615,17 @@ void mla_decode_m16_kernel(const AttnArgs a) {
         if (ts < nch) {
             issue(0, 0);
         }
+        // Q: the caller waited for this wave's copies; the barrier covers the other waves', the
+        // second one every wave's reads before wave 0 refills the buffer
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+            uint4 v = *reinterpret_cast<const uint4*>(qs + r * (kDqk * 2) + (ks * 32 + g4 * 8) * 2);
+            if (r >= a.M) v = make_uint4(0, 0, 0, 0);
+            qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
         int k = 0;
         for (int c = ts; c < nch; c += 4, ++k) {
             const char* buf = bufs + (k & 1) * kMBuf;
@@ -677,28 +698,27 @@ void mla_decode_m16_kernel(const AttnArgs a) {
             }
         }
 
-        // row sums, merge the 4 streams (stream 0 keeps the result), write
+        // row sums, then the 4 streams merge through LDS: every wave stores its accumulators,
+        // and wave ts merges and writes value tiles 8*ts..8*ts+7 of all four
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
-        f4* macc = reinterpret_cast<f4*>(smem);
-        float* mml = reinterpret_cast<float*>(smem + 3 * 32 * 64 * 16);
+        f4* macc = reinterpret_cast<f4*>(smem);                                 // [stream][tile][lane]
+        float* mml = reinterpret_cast<float*>(smem + 4 * 32 * 64 * 16);        // [stream][lane][m, l]
         __syncthreads();
-        if (ts > 0) {
 #pragma unroll
-            for (int dt = 0; dt < 32; ++dt) macc[((ts - 1) * 32 + dt) * 64 + lane] = acc[dt];
-            mml[((ts - 1) * 64 + lane) * 2 + 0] = m_run;
-            mml[((ts - 1) * 64 + lane) * 2 + 1] = l_run;
-        }
+        for (int dt = 0; dt < 32; ++dt) macc[(ts * 32 + dt) * 64 + lane] = acc[dt];
+        mml[(ts * 64 + lane) * 2 + 0] = m_run;
+        mml[(ts * 64 + lane) * 2 + 1] = l_run;
         __syncthreads();
-        if (ts == 0) {
+        {
             float mk[4], lk[4];
-            mk[0] = m_run;
-            lk[0] = l_run;
-            float m_new = m_run;
+            mk[0] = mml[lane * 2 + 0];
+            lk[0] = mml[lane * 2 + 1];
+            float m_new = mk[0];
 #pragma unroll
             for (int w = 1; w < 4; ++w) {
-                mk[w] = mml[((w - 1) * 64 + lane) * 2 + 0];
-                lk[w] = mml[((w - 1) * 64 + lane) * 2 + 1];
+                mk[w] = mml[(w * 64 + lane) * 2 + 0];
+                lk[w] = mml[(w * 64 + lane) * 2 + 1];
                 m_new = fmaxf(m_new, mk[w]);
             }
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -714,25 +734,27 @@ void mla_decode_m16_kernel(const AttnArgs a) {
                 if (final_out) {
                     __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)grp * a.M + r) * kDv + 4 * g4;
 #pragma unroll
-                    for (int dt = 0; dt < 32; ++dt) {
-                        f4 v = acc[dt] * al[0];
+                    for (int j = 0; j < 8; ++j) {
+                        const int dt = 8 * ts + j;
+                        f4 v = macc[dt * 64 + lane] * al[0];
 #pragma unroll
-                        for (int w = 1; w < 4; ++w) v += macc[((w - 1) * 32 + dt) * 64 + lane] * al[w];
+                        for (int w = 1; w < 4; ++w) v += macc[(w * 32 + dt) * 64 + lane] * al[w];
                         v *= inv;
                         *reinterpret_cast<uint2*>(orow + dt * 16) =
                             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                     }
-                    if (g4 == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
+                    if (ts == 0 && g4 == 0) a.lse[(size_t)grp * a.M + r] = lse_v;
                 } else {
                     float* prow = a.part_o + ((size_t)slot * a.M + r) * kDv + 4 * g4;
 #pragma unroll
-                    for (int dt = 0; dt < 32; ++dt) {
-                        f4 v = acc[dt] * al[0];
+                    for (int j = 0; j < 8; ++j) {
+                        const int dt = 8 * ts + j;
+                        f4 v = macc[dt * 64 + lane] * al[0];
 #pragma unroll
-                        for (int w = 1; w < 4; ++w) v += macc[((w - 1) * 32 + dt) * 64 + lane] * al[w];
+                        for (int w = 1; w < 4; ++w) v += macc[(w * 32 + dt) * 64 + lane] * al[w];
                         *reinterpret_cast<f4*>(prow + dt * 16) = v * inv;
                     }
-                    if (g4 == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
+                    if (ts == 0 && g4 == 0) a.part_lse[(size_t)slot * a.M + r] = lse_v;
                 }
             }
         }
@@ -742,14 +764,22 @@ void mla_decode_m16_kernel(const AttnArgs a) {
     const int* meta = a.tile_meta + (size_t)item * kMetaInts;
     const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
     for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
-        const int L = a.seqlens[bb];
-        const int nb = ceil_div(L, kPage);
+        // A segment's first loads go out together, one memory round trip before its first KV
+        // copy: the copy of Q, the first 64 entries of its block-table row from page lo (in
+        // bounds of the row; entries past the sequence are never used), its length and split
+        // count.  All of them are waited for (the empty asm reads the window) before the KV
+        // copies start, so no load the compiler tracks is pending behind a copy.  (The copy of Q
+        // goes first: the compiler's waits on the later loads then cover it.)
+        copy_q(bb);
         const int lo = (bb == b0) ? blk0 : 0;
-        const int hi = (bb == b1) ? blk1 : nb;
+        const int win0 = (lane < a.max_blocks - lo) ? a.block_table[(size_t)bb * a.max_blocks + lo + lane] : 0;
+        const int L = a.seqlens[bb];
+        const int ns0 = a.num_splits[bb], ns1 = a.num_splits[bb + 1];
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("" ::"v"(win0));
+        const int hi = (bb == b1) ? blk1 : ceil_div(L, kPage);
         if (lo >= hi) continue;
-        const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
-        const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
-        run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+        run_segment(bb, lo * kPage, min(hi * kPage, L), L, ns1 - ns0 == 1, (bb == b0) ? slot0 : ns0, win0);
     }
 }
 
