@@ -221,43 +221,77 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     float m_run, l_run;
     float m_lane;     // largest score this lane has seen in the pass (for a restart's reference)
 
-    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot) {
-        const int nch = ceil_div(t1 - t0, kChunk);
-        // ---- Q fragments (B operand of S^T): dims 32*ks + 8*g4 .. +7 of this lane's row
-        {
-            const char* qrow = static_cast<const char*>(a.q) + ((size_t)grp * a.M + (row_ok ? row : 0)) * ROWB;
+    // ---- segment start.  Q (64 rows) and, sparse, the split's index list come by direct copies
+    // into LDS: Q into the ring's last two slots, which the pipeline's first chunks leave free,
+    // each wave an eighth; the fragments are read from there just before the first Q.K^T.
+    constexpr int QOPS = ROWB / 128;                 // 1 KB copies of Q per wave (64 rows / 8 waves)
+    char* const qs = ring + (DEPTH - 2) * C::BUF;
+    auto copy_q = [&](int grp) {
+        const char* qg = static_cast<const char*>(a.q) + (size_t)grp * a.M * ROWB;
+        // (an opaque lane id: the per-lane offsets are not hoisted out of the segment loop)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
-                if (!row_ok) v = make_uint4(0, 0, 0, 0);
-                qf[ks] = __builtin_bit_cast(bf16x8, v);
+        for (int i = 0; i < QOPS; ++i) {
+            const int j = wave + kWaves * i;
+            const unsigned e = 1024 * j + 16 * ln;
+            const int r = rg * kRowsWg + (int)(e / ROWB);     // rows past M read row 0
+            dma16_s(qg, (unsigned)((r < a.M ? r : 0) * ROWB) + e % ROWB, qs + 1024 * j);
+        }
+    };
+    // sparse: the split's entries [t0, t1) as raw index values, 64 per copy (entries past t1
+    // read entry t0 and are marked unused later)
+    auto copy_idx = [&](int grp, int t0, int t1) {
+        const int nch = ceil_div(t1 - t0, kChunk);
+        const int* ig = a.indices + (size_t)grp * a.topk + t0;
+#pragma unroll
+        for (int i = 0; i < kMaxSparseSplit / (64 * kWaves); ++i) {
+            const int j = wave + kWaves * i;
+            if (64 * j < nch * kChunk) {
+                const int e = 64 * j + lane;
+                dma4(ig + (e < t1 - t0 ? e : 0), lidx + 64 * j);
             }
         }
+    };
+    // Q fragments (B operand of S^T): dims 32*ks + 8*g4 .. +7 of this lane's row, from the copy
+    // (every wave's copies have landed: the caller waited for this wave's, a barrier for the rest)
+    auto read_q = [&]() {
+        const char* qrow = qs + (16 * rb + l16) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 v = *reinterpret_cast<const uint4*>(qrow + (ks * 32 + g4 * 8) * 2);
+            if (!row_ok) v = make_uint4(0, 0, 0, 0);
+            qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    };
+
+    // win0 (paged): lane i holds the block-table entry of page t0/64 + i
+    auto run_segment = [&](int grp, int t0, int t1, int L, bool final_out, int slot, int win0) {
+        const int nch = ceil_div(t1 - t0, kChunk);
         m_run = -INFINITY;
         const int limit = a.causal ? (L - a.s_q + row / a.h_q) : (L - 1);
 
-        // sparse: the split's index list (at most kMaxSparseSplit entries) goes to LDS once, as
-        // record numbers (-1 for unused entries and up to the end of the last chunk)
-        // (all of a thread's loads are issued before any is waited for: one memory round trip)
+        // sparse: the copied index values become record numbers in place (-1 for unused entries
+        // and up to the end of the last chunk)
         if constexpr (SPARSE) {
+            __syncthreads();                 // every wave's index copies have landed
             constexpr int kPer = kMaxSparseSplit / (kWaves * 64);
-            int v[kPer];
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int e = threadIdx.x + j * kWaves * 64;
-                v[j] = e < t1 - t0 ? a.indices[(size_t)grp * a.topk + t0 + e] : -1;
-            }
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int e = threadIdx.x + j * kWaves * 64;
-                if (e < nch * kChunk) lidx[e] = (v[j] >= 0 && v[j] < a.kv_rows) ? v[j] : -1;
+                if (e < nch * kChunk) {
+                    const int v = lidx[e];
+                    lidx[e] = (e < t1 - t0 && v >= 0 && v < a.kv_rows) ? v : -1;
+                }
             }
             __syncthreads();
         }
 
         // paged: page numbers of the segment, 64 at a time into a per-wave LDS window (a lookup
-        // then never waits on the vector-memory counter, which also counts the KV copies)
-        int bt_base = -1000000;
+        // then never waits on the vector-memory counter, which also counts the KV copies); the
+        // first window from the caller
+        int bt_base = 0;
+        if constexpr (!SPARSE) lpages[wave * 64 + lane] = win0;
         auto page_of = [&](int p) {
             int* win = lpages + wave * 64;
             if (p - bt_base >= 64 || p < bt_base) {
@@ -544,6 +578,12 @@ void mla_decode_rows_kernel(const AttnArgs a) {
             // chunk AHEAD, or the conversion of chunk 1 and the gathers of chunk 2, spread over
             // it), reference, probabilities of the own tile
             __syncthreads();
+            if (pass == 0) {
+                // Q from its copy; every wave has read it before the slots are refilled
+                read_q();
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
             {
                 const Plan p = plan_for(AHEAD);
                 auto side0 = [&](int ks) {
@@ -689,21 +729,35 @@ void mla_decode_rows_kernel(const AttnArgs a) {
         const int* meta = a.tile_meta + (size_t)item * kMetaInts;
         const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
         for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
-            const int L = a.seqlens[bb];
-            const int nb = ceil_div(L, kPage);
+            // A segment's first loads go out together, one memory round trip before its first KV
+            // copy: the copy of Q, the first 64 block-table entries from page lo (in bounds of
+            // the row; entries past the sequence are never used), its length and split count.
+            // All are waited for (the empty asm reads the window) before the KV copies start, so
+            // no load the compiler tracks is pending behind a copy.  (The copy of Q goes first:
+            // the compiler's waits on the later loads then cover it.)
+            copy_q(bb);
             const int lo = (bb == b0) ? blk0 : 0;
-            const int hi = (bb == b1) ? blk1 : nb;
+            const int win0 = (lane < a.max_blocks - lo) ? a.block_table[(size_t)bb * a.max_blocks + lo + lane] : 0;
+            const int L = a.seqlens[bb];
+            const int ns0 = a.num_splits[bb], ns1 = a.num_splits[bb + 1];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("" ::"v"(win0));
+            const int hi = (bb == b1) ? blk1 : ceil_div(L, kPage);
             if (lo >= hi) continue;
-            const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
-            const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
-            run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+            run_segment(bb, lo * kPage, min(hi * kPage, L), L, ns1 - ns0 == 1, (bb == b0) ? slot0 : ns0, win0);
         }
     } else {
         const int grp = item / a.num_parts;
         const int split = item % a.num_parts;
         const int e0 = split * a.split_len;
         const int e1 = min(e0 + a.split_len, a.topk);
-        if (e0 < e1) run_segment(grp, e0, e1, 0, a.num_parts == 1, grp * a.num_parts + split);
+        if (e0 < e1) {
+            // the index list first, then Q: the first gathers wait only for the list
+            copy_idx(grp, e0, e1);
+            copy_q(grp);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QOPS) : "memory");
+            run_segment(grp, e0, e1, 0, a.num_parts == 1, grp * a.num_parts + split, 0);
+        }
     }
 }
 

@@ -773,14 +773,14 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         const int* meta = a.tile_meta + (size_t)item * kMetaInts;
         const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
         for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
+            // the length and the split count in one memory round trip
             const int L = a.seqlens[bb];
+            const int ns0 = a.num_splits[bb], ns1 = a.num_splits[bb + 1];
             const int nb = ceil_div(L, kPage);
             const int lo = (bb == b0) ? blk0 : 0;
             const int hi = (bb == b1) ? blk1 : nb;
             if (lo >= hi) continue;
-            const int nsp = a.num_splits[bb + 1] - a.num_splits[bb];
-            const int slot = (bb == b0) ? slot0 : a.num_splits[bb];
-            run_segment(bb, lo * kPage, min(hi * kPage, L), L, nsp == 1, slot);
+            run_segment(bb, lo * kPage, min(hi * kPage, L), L, ns1 - ns0 == 1, (bb == b0) ? slot0 : ns0);
         }
     }
 }

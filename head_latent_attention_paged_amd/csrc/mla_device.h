@@ -80,6 +80,12 @@ __device__ __forceinline__ void dma16_s_shared(const void* sbase, unsigned voff,
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
+// 4-byte copy of each lane's global address into LDS (lane i writes at m0 + 4 * i).
+__device__ __forceinline__ void dma4(const void* gptr, const void* lds_ptr) {
+    const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_ptr;
+    asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+}
+
 // Nontemporal 16-byte load of streamed KV data into registers.
 __device__ __forceinline__ uint4 load_nt(const void* p) {
     typedef unsigned u4v __attribute__((ext_vector_type(4)));
