@@ -1,7 +1,6 @@
 // gfx950 (CDNA4) kernels for paged and sparse MLA decode.
 //
-// K0  mla_metadata_kernel   tile-scheduler metadata from device sequence lengths (one wave up
-//                           to 1024 sequences: mla_metadata_wave_kernel)
+// K0  mla_metadata_kernel   tile-scheduler metadata from device sequence lengths
 // K1  mla_decode_kernel     gather -> Q.K^T (576) -> online softmax -> P.V (512) -> final or partial
 //                           (paged bf16 cache, or sparse fp8 records through an index list)
 // K2  mla_combine_kernel    LSE-weighted merge of split-KV partials
@@ -1008,108 +1007,6 @@ __global__ __launch_bounds__(kMetaThreads) void mla_metadata_kernel(const int32_
     }
 }
 
-// The same partition from one wave, for up to 1024 sequences (16 consecutive ones per lane):
-// every length is loaded in one memory round trip and the scans are wave shuffles, so the
-// launch is a load, two scans and the parts' searches, with no workgroup barrier on the path.
-constexpr int kMetaWaveMax = 1024;
-constexpr int kMetaWavePer = kMetaWaveMax / 64;
-
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-__global__ __launch_bounds__(64) void mla_metadata_wave_kernel(const int32_t* __restrict__ seqlens, int batch,
-                                                               int num_parts, int ovh,
-                                                               int32_t* __restrict__ tile_meta,
-                                                               int32_t* __restrict__ num_splits) {
-    __shared__ int cpre[kMetaWaveMax + 1];   // cost prefix C_b
-    __shared__ int spre[kMetaWaveMax + 1];   // split prefix
-    const int lane = threadIdx.x;
-    const int per = (batch + 63) / 64;
-    const int bl = lane * per;               // this lane's first sequence
-    int cost[kMetaWavePer];
-#pragma unroll
-    for (int i = 0; i < kMetaWavePer; ++i) {
-        const int b = bl + i;
-        const int L = (i < per && b < batch) ? seqlens[b] : 0;
-        const int nb = L > 0 ? (L + kPage - 1) / kPage : 0;
-        cost[i] = nb > 0 ? nb + ovh : 0;
-    }
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < kMetaWavePer; ++i) c += cost[i];
-    const int cin = wave_incl_scan(c);
-    const int total = __shfl(cin, 63);
-    const int payload = total > 0 ? (total + num_parts - 1) / num_parts : 1;
-    int run = cin - c, sp = 0;
-    int spl[kMetaWavePer];
-#pragma unroll
-    for (int i = 0; i < kMetaWavePer; ++i) {
-        const int b = bl + i;
-        if (i < per && b < batch) cpre[b] = run;
-        spl[i] = 0;
-        const int nb = cost[i] > 0 ? cost[i] - ovh : 0;
-        if (nb > 0) {
-            const int u0 = run + ovh;
-            spl[i] = (u0 + nb - 1) / payload - u0 / payload + 1;
-        }
-        sp += spl[i];
-        run += cost[i];
-    }
-    const int sin = wave_incl_scan(sp);
-    int srun = sin - sp;
-#pragma unroll
-    for (int i = 0; i < kMetaWavePer; ++i) {
-        const int b = bl + i;
-        if (i < per && b < batch) {
-            spre[b] = srun;
-            num_splits[b] = srun;
-        }
-        srun += spl[i];
-    }
-    const int stot = __shfl(sin, 63);
-    if (lane == 0) {
-        cpre[batch] = total;
-        spre[batch] = stot;
-        num_splits[batch] = stot;
-    }
-    __syncthreads();
-    for (int p = lane; p < num_parts; p += 64) {
-        int bb[2], blk[2];
-        for (int e = 0; e < 2; ++e) {
-            const long long u = (long long)(p + e) * payload;
-            if (u >= total) {
-                bb[e] = batch;
-                blk[e] = 0;
-                continue;
-            }
-            int lo = 0, hi = batch;   // first b with cpre[b+1] > u
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (cpre[mid + 1] <= u) lo = mid + 1; else hi = mid;
-            }
-            bb[e] = lo;
-            const int off = (int)(u - cpre[lo]) - ovh;
-            blk[e] = off > 0 ? off : 0;
-        }
-        int slot = 0;
-        if (bb[0] < batch) {
-            const int first = (cpre[bb[0]] + ovh) / payload;
-            slot = spre[bb[0]] + (p - first);
-            if (p < first) slot = 0;
-        }
-        int32_t* m = tile_meta + (size_t)p * kMetaInts;
-        m[0] = bb[0]; m[1] = blk[0]; m[2] = bb[1]; m[3] = blk[1]; m[4] = slot;
-        m[5] = 0; m[6] = 0; m[7] = 0;
-    }
-}
-
 // --------------------------------------------------------------------------
 // Launchers
 // --------------------------------------------------------------------------
@@ -1132,12 +1029,8 @@ Tiling choose_tiling(int rows) {
 
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int overhead,
                            int32_t* tile_meta, int32_t* num_splits, hipStream_t stream) {
-    if (batch <= kMetaWaveMax)
-        hipLaunchKernelGGL(mla_metadata_wave_kernel, dim3(1), dim3(64), 0, stream,
-                           seqlens, batch, num_parts, overhead, tile_meta, num_splits);
-    else
-        hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(kMetaThreads), 0, stream,
-                           seqlens, batch, num_parts, overhead, tile_meta, num_splits);
+    hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(kMetaThreads), 0, stream,
+                       seqlens, batch, num_parts, overhead, tile_meta, num_splits);
     return hipGetLastError();
 }
 

@@ -111,7 +111,8 @@ def run_sparse(env, inp, splits=0):
     ([37, 130], 256), ([4096] * 128, 256), ([65536] * 16, 256), ([1, 64, 65, 0, 128, 3000], 7),
     ([0, 0, 5], 4), ([100] * 9, 1), (list(range(0, 3000, 37)), 64),
     (list(np.random.default_rng(1).integers(0, 9000, size=3000)), 128),
-    # the one-wave launch (up to 1024 sequences, up to 16 per lane) and the first size past it
+    # batches of more than one pass over the 256 threads, 65 (one wave and one lane), and more
+    # parts than sequences
     (list(np.random.default_rng(2).integers(0, 9000, size=1024)), 256),
     (list(np.random.default_rng(3).integers(0, 9000, size=1025)), 256),
     (list(np.random.default_rng(4).integers(0, 200, size=65)), 100), ([7] * 64, 300),
