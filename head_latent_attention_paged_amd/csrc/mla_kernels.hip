@@ -811,26 +811,30 @@ __device__ __forceinline__ void load_part8(const float* part_o, size_t row, int 
 // term of the denominator (LSE = the sink, no value).  The splits go in groups of G whose LSEs
 // and values are loaded together (one memory round trip per group); mu is the running
 // maximum, and a group that raises it rescales what the earlier groups summed.
-template <bool BF16>
+template <bool BF16, int NV = 2>
 __device__ __forceinline__ void merge_row(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                           int base, int n, int rows, int r, int d, float sk,
-                                          f4 (&o)[2], float& mu, float& wsum) {
+                                          f4 (&o)[NV], float& mu, float& wsum) {
+    static_assert(NV == 2 || !BF16, "bf16 partials: 8 dims per lane");
     mu = sk;
     wsum = sk != -INFINITY ? 1.f : 0.f;
-    o[0] = o[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NV; ++q) o[q] = f4{0.f, 0.f, 0.f, 0.f};
     constexpr int G = combine_group<BF16>();
     for (int i0 = 0; i0 < n; i0 += G) {
         float li[G];
-        f4 v[G][2];
+        f4 v[G][NV];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             // (n is the same for the whole wave: the branch does not diverge)
             li[j] = -INFINITY;
-            v[j][0] = v[j][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NV; ++q) v[j][q] = f4{0.f, 0.f, 0.f, 0.f};
             if (i0 + j < n) {
                 const size_t i = (size_t)(base + i0 + j) * rows + r;
                 li[j] = part_lse[i];
-                load_part8<BF16>(part_o, i, d, v[j][0], v[j][1]);
+                if constexpr (NV == 2) load_part8<BF16>(part_o, i, d, v[j][0], v[j][1]);
+                else v[j][0] = *reinterpret_cast<const f4*>(part_o + i * kDv + d);
             }
         }
         float mg = mu;
@@ -840,26 +844,28 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o, cons
         if (mg == -INFINITY) continue;                          // nothing finite so far
         const float sc = mu == -INFINITY ? 0.f : expf(mu - mg);  // mu <= mg
         wsum *= sc;
-        o[0] *= sc;
-        o[1] *= sc;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) o[q] *= sc;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             if (i0 + j < n && li[j] != -INFINITY) {
                 const float w = expf(li[j] - mg);
                 wsum += w;
-                o[0] += v[j][0] * w;
-                o[1] += v[j][1] * w;
+#pragma unroll
+                for (int q = 0; q < NV; ++q) o[q] += v[j][q] * w;
             }
         }
         mu = mg;
     }
     if (mu != -INFINITY) {
         const float iw = 1.f / wsum;
-        o[0] *= iw;
-        o[1] *= iw;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) o[q] *= iw;
     }
 }
 
+// BF16 partials: one wave per row, 8 dims per lane; fp32 partials: two waves per row (the
+// value halves), 4 dims per lane, so that a row with many splits has twice the loads in flight
 template <bool BF16>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
@@ -867,8 +873,11 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
                                                           int uniform_splits, int rows,
                                                           __bf16* __restrict__ out, float* __restrict__ lse,
                                                           const float* __restrict__ sinks, int h_q) {
+    constexpr int WPR = BF16 ? 1 : 2;                 // waves per row
     const int grp = blockIdx.x;
-    const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int w = threadIdx.x >> 6;
+    const int r = blockIdx.y * (4 / WPR) + w / WPR;
+    const int half = w % WPR;
     const int lane = threadIdx.x & 63;
     if (r >= rows) return;
     int base, n;
@@ -881,13 +890,21 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
     }
     if (n == 1) return;   // the decode kernel wrote this row directly
     const float sk = sinks ? sinks[r % h_q] : -INFINITY;
-    f4 o[2];
     float mu, wsum;
-    merge_row<BF16>(part_o, part_lse, base, n, rows, r, 8 * lane, sk, o, mu, wsum);
-    const uint4 pk = make_uint4(pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]),
-                                pack_bf16x2(o[1][0], o[1][1]), pack_bf16x2(o[1][2], o[1][3]));
-    *reinterpret_cast<uint4*>(out + ((size_t)grp * rows + r) * kDv + 8 * lane) = pk;
-    if (lane == 0) lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
+    if constexpr (BF16) {
+        f4 o[2];
+        merge_row<BF16>(part_o, part_lse, base, n, rows, r, 8 * lane, sk, o, mu, wsum);
+        const uint4 pk = make_uint4(pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]),
+                                    pack_bf16x2(o[1][0], o[1][1]), pack_bf16x2(o[1][2], o[1][3]));
+        *reinterpret_cast<uint4*>(out + ((size_t)grp * rows + r) * kDv + 8 * lane) = pk;
+    } else {
+        f4 o[1];
+        const int d = (kDv / 2) * half + 4 * lane;
+        merge_row<BF16, 1>(part_o, part_lse, base, n, rows, r, d, sk, o, mu, wsum);
+        *reinterpret_cast<uint2*>(out + ((size_t)grp * rows + r) * kDv + d) =
+            make_uint2(pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]));
+    }
+    if (lane == 0 && half == 0) lse[(size_t)grp * rows + r] = (mu == -INFINITY) ? -INFINITY : mu + logf(wsum);
 }
 
 // --------------------------------------------------------------------------
@@ -1145,7 +1162,7 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, const int3
                            part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
                            sinks, h_q);
     else
-        hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(groups, (rows + 3) / 4), dim3(256), 0, stream,
+        hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(groups, (rows + 1) / 2), dim3(256), 0, stream,
                            part_o, part_lse, prefix, uniform_splits, rows, static_cast<__bf16*>(out), lse,
                            sinks, h_q);
     return hipGetLastError();
