@@ -427,18 +427,26 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         };
         // O^T += V^T P^T over chunk c: token step s (16 tokens) for all 16 dim tiles, s = 0, 1
         // (the two steps of a tile are 16 MFMAs apart); side(i) runs between the MFMAs
-        auto pv = [&](int c, bf16x8 (&pb)[2], auto&& side) {
+        auto vidx = [](int n) { return 2 * (n & 15) + (n >> 4); };     // MFMA n: tile n&15, step n>>4
+        // the first VPF-1 V^T fragments of chunk c's P.V (issued ahead of it)
+        auto pv_head = [&](int c, bf16x8 (&vf)[VPF]) {
             const char* buf = ring + (c % DEPTH) * C::BUF;
-            bf16x8 vf[VPF];
-            auto vidx = [](int n) { return 2 * (n & 15) + (n >> 4); };     // MFMA n: tile n&15, step n>>4
 #pragma unroll
             for (int i = 0; i < VPF - 1; ++i) vf[i] = vfrag(buf, vidx(i));
+        };
+        auto pv_body = [&](int c, bf16x8 (&vf)[VPF], bf16x8 (&pb)[2], auto&& side) {
+            const char* buf = ring + (c % DEPTH) * C::BUF;
 #pragma unroll
             for (int n = 0; n < 32; ++n) {
                 if (n + VPF - 1 < 32) vf[(n + VPF - 1) % VPF] = vfrag(buf, vidx(n + VPF - 1));
                 acc[n & 15] = mfma32(vf[n % VPF], pb[n >> 4], acc[n & 15]);
                 side(n);
             }
+        };
+        auto pv = [&](int c, bf16x8 (&pb)[2], auto&& side) {
+            bf16x8 vf[VPF];
+            pv_head(c, vf);
+            pv_body(c, vf, pb, side);
         };
 
         // ---- masking of chunk c: lane value v is token 8*(v>>2) + 4*g + (v&3) of this lane's row
@@ -542,6 +550,11 @@ void mla_decode_wide_kernel(const AttnArgs a) {
             // maximum feeds the restart vote and reference (the row's is taken at the restart).
             auto finish = [&](int c, f16v& s, auto first_c) {
                 constexpr bool FIRST = decltype(first_c)::value;
+                // bf16 pages: the first V^T reads of the chunk's P.V go out before the masking and
+                // the probabilities, whose VALU work then covers their latency (FP4 pages measured
+                // slower that way: their conversion work sits between the same MFMAs)
+                bf16x8 vf[VPF];
+                if constexpr (!GATHER) pv_head(c, vf);
                 float mx = 0.f;
                 mask(c, s, mx, std::integral_constant<bool, FIRST>{});
                 if constexpr (FIRST) {
@@ -551,7 +564,8 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                 bf16x8 pb[2];
                 float ml = -INFINITY;
                 pb[0] = probs(c, s, 0, ml);
-                pv(c, pb, [&](int n) {
+                if constexpr (GATHER) pv_head(c, vf);
+                pv_body(c, vf, pb, [&](int n) {
                     if (n == 2) pb[1] = probs(c, s, 1, ml);
                 });
                 if constexpr (!FIRST) {
