@@ -132,6 +132,9 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     constexpr int PF = MLA_WIDE_KPF;               // K fragment prefetch distance (MFMA steps)
     constexpr int VPF = MLA_WIDE_VPF;              // V^T fragment prefetch distance
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    // fused decode: the query-norm weight, staged once per workgroup (the prologue of every
+    // segment reads it fragment by fragment)
+    __shared__ __attribute__((aligned(16))) float s_qw[FUSED ? kDv : 4];
     char* ring = smem;
     int* lpages = reinterpret_cast<int*>(smem + C::RING);
     int* votes = reinterpret_cast<int*>(smem + C::RING + C::PAGES);
@@ -237,8 +240,8 @@ void mla_decode_wide_kernel(const AttnArgs a) {
                     // (opaque: the sum of squares above does not keep its 256 floats live for this)
                     asm volatile("" : "+v"(qf[ks]));
                     const int d0 = 16 * ks + 8 * qg;
-                    const f4 w0 = *reinterpret_cast<const f4*>(a.qn_weight + d0);
-                    const f4 w1 = *reinterpret_cast<const f4*>(a.qn_weight + d0 + 4);
+                    const f4 w0 = *reinterpret_cast<const f4*>(s_qw + d0);
+                    const f4 w1 = *reinterpret_cast<const f4*>(s_qw + d0 + 4);
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = (float)qf[ks][e] * rinv * (e < 4 ? w0[e] : w1[e - 4]);
@@ -784,6 +787,10 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     };
 
     {
+        if constexpr (FUSED) {
+            for (int i = threadIdx.x; i < kDv; i += kWaves * 64) s_qw[i] = a.qn_weight[i];
+            __syncthreads();
+        }
         const int* meta = a.tile_meta + (size_t)item * kMetaInts;
         const int b0 = meta[0], blk0 = meta[1], b1 = meta[2], blk1 = meta[3], slot0 = meta[4];
         for (int bb = b0; bb <= b1 && bb < a.batch; ++bb) {
