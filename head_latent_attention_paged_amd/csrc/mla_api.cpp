@@ -85,9 +85,13 @@ int mla_num_parts(int num_cus, int h_q, int s_q) {
     // one-wave-per-SIMD kernel's 128-row groups): one round, because every extra split of a
     // sequence writes and reads back fp32 partials of all its rows (measured on the 256- and
     // 384-row workloads: one round with fewer splits is 10-20% faster than two).
-    const int row_groups = rows > mla::kWideMinRows ? (int)((rows + mla::kWideRows - 1) / mla::kWideRows) : t.row_groups;
-    int p = (rows > mla::kWideMinRows ? 1 : rows > 32 ? 2 : 1) * num_cus / row_groups;
-    if (p >= 8) p -= p % 8;
+    // The row-split and 16-row kernels take a multiple of 8 parts (each XCD then holds whole
+    // parts); the one-wave-per-SIMD kernel places the parts beyond the last multiple of 8 on the
+    // compute units left over (384 rows: 85 parts in 255 workgroups instead of 80 in 240).
+    const bool wide = rows > mla::kWideMinRows;
+    const int row_groups = wide ? (int)((rows + mla::kWideRows - 1) / mla::kWideRows) : t.row_groups;
+    int p = (wide ? 1 : rows > 32 ? 2 : 1) * num_cus / row_groups;
+    if (p >= 8 && !wide) p -= p % 8;
     return p >= 1 ? p : 1;
 }
 

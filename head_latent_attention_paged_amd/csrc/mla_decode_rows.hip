@@ -152,17 +152,7 @@ void mla_decode_rows_kernel(const AttnArgs a) {
     const int R = ceil_div(a.M, kRowsWg);
     const int n_items = SPARSE ? a.batch * a.num_parts : a.num_parts;
     int item, rg;
-    {
-        const int bid = blockIdx.x;
-        if ((n_items & 7) == 0) {
-            const int xcd = bid & 7, k = bid >> 3;
-            item = (k / R) * 8 + xcd;
-            rg = k % R;
-        } else {
-            item = bid / R;
-            rg = bid % R;
-        }
-    }
+    xcd_item(blockIdx.x, n_items, R, item, rg);
     const int row = rg * kRowsWg + 16 * rb + l16;     // this lane's query row (B / C column)
     const bool row_ok = row < a.M;
     // row groups that re-read the same KV keep it in L2 (default policy); a single reader

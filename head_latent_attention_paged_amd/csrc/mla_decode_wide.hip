@@ -145,21 +145,12 @@ void mla_decode_wide_kernel(const AttnArgs a) {
     const int g = lane >> 5;           // k half of the operands
     const int j16 = lane & 15, ih = (lane >> 4) & 1;
 
-    // ---- work item -> (part, row group); row groups of one part share an XCD
+    // ---- work item -> (part, row group); row groups of one part share an XCD (all but the
+    // parts beyond the last multiple of 8)
     const int R = ceil_div(a.M, kRowsWg);
     const int n_items = a.num_parts;
     int item, rg;
-    {
-        const int bid = blockIdx.x;
-        if ((n_items & 7) == 0) {
-            const int xcd = bid & 7, k = bid >> 3;
-            item = (k / R) * 8 + xcd;
-            rg = k % R;
-        } else {
-            item = bid / R;
-            rg = bid % R;
-        }
-    }
+    xcd_item(blockIdx.x, n_items, R, item, rg);
 
     auto copy_s = [&](const void* sbase, unsigned voff, const void* l) {
         if constexpr (SHARED) dma16_s_shared(sbase, voff, l);

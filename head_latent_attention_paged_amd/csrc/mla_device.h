@@ -45,6 +45,23 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 
 __device__ __forceinline__ int lds_a(int r, int c) { return r * kRowA + ((c ^ swz(r)) << 4); }
 __device__ __forceinline__ int lds_b(int r, int c) { return kRegionB + r * 128 + ((c ^ swz(r)) << 4); }
 
+// Work item and row group of workgroup `bid` when each of n_items work items takes R workgroups.
+// Workgroups go to the 8 XCDs round robin by block index: the R row groups of each of the first
+// n_items & ~7 items land on one XCD, back to back, so that the later readers of a KV chunk hit
+// that XCD's L2; the items beyond those take the remaining workgroups in order.
+__device__ __forceinline__ void xcd_item(int bid, int n_items, int R, int& item, int& rg) {
+    const int full = n_items & ~7;
+    if (bid < full * R) {
+        const int xcd = bid & 7, k = bid >> 3;
+        item = (k / R) * 8 + xcd;
+        rg = k % R;
+    } else {
+        const int t = bid - full * R;
+        item = full + t / R;
+        rg = t % R;
+    }
+}
+
 __device__ __forceinline__ f4 mfma16(bf16x8 a, bf16x8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -88,9 +88,10 @@ hipError_t launch_decode_wide(const AttnArgs& a, hipStream_t stream);
 constexpr int kWideRows = 128;
 constexpr int kWideMinRows = 64;
 // Per-sequence fixed cost in the tile scheduler's partition, in 64-token blocks: none up to 64
-// rows (equal sequences then split into equal parts with one segment each), two above, where a
-// segment start (Q, the first chunks, the epilogue of 128-row workgroups) costs more.
-inline int meta_overhead_blocks(long long rows) { return rows > kWideMinRows ? 2 : 0; }
+// rows (equal sequences then split into equal parts with one segment each), four above, where a
+// segment start (Q, the first chunks, the epilogue of 128-row workgroups) costs about as much as
+// that many blocks of the chunk loop.
+inline int meta_overhead_blocks(long long rows) { return rows > kWideMinRows ? 4 : 0; }
 // Supplies the workspace of a call that brings none: given the bytes the call needs, sets the
 // pointer and size of the library's own array, or returns an error status.
 typedef mla_status_t (*ScratchSource)(size_t need, void** ptr, size_t* bytes);

@@ -67,19 +67,7 @@ void mla_decode_kernel(const AttnArgs a) {
     const int R = ceil_div(a.M, C::ROWS_WG);
     const int n_items = (SPARSE ? a.batch * a.num_parts : a.num_parts);
     int item, rg;
-    {
-        const int bid = blockIdx.x;
-        if ((n_items & 7) == 0) {
-            // blocks are dispatched round-robin over the 8 XCDs: keep the R row groups of one
-            // work item on one XCD, launched back to back, so they share its L2 copy of the KV.
-            const int xcd = bid & 7, k = bid >> 3;
-            item = (k / R) * 8 + xcd;
-            rg = k % R;
-        } else {
-            item = bid / R;
-            rg = bid % R;
-        }
-    }
+    xcd_item(blockIdx.x, n_items, R, item, rg);
     const int rbase = rg * C::ROWS_WG + rw * C::ROWS_WAVE;   // first row of this wave
 
     // LDS byte offsets that do not depend on the chunk.

@@ -61,9 +61,11 @@ const char* mla_status_string(mla_status_t status);
  * one workgroup per compute unit once the row groups of a sequence are
  * counted (64-row groups up to 64 rows, 128-row groups beyond), two per
  * compute unit when 32 < s_q*h_q <= 64.  num_cus <= 0 queries the current
- * device.  Returns >= 1, a multiple of 8 when num_cus is (so the part -> XCD
- * mapping is exact).  Any value >= 1 is valid for the calls below; larger
- * values force more KV splits.
+ * device.  Returns >= 1; up to 64 rows a multiple of 8 when num_cus is (each
+ * XCD then holds whole parts), above 64 rows num_cus / (128-row groups)
+ * (the parts beyond the last multiple of 8 fill the compute units left over).
+ * Any value >= 1 is valid for the calls below; larger values force more KV
+ * splits.
  */
 int mla_num_parts(int num_cus, int h_q, int s_q);
 
@@ -79,7 +81,7 @@ int mla_num_parts(int num_cus, int h_q, int s_q);
  *   num_splits    [device] int32[batch + 1]                  (out)
  *
  * Work is counted in 64-token blocks, plus a fixed cost per non-empty
- * sequence (none for s_q*h_q <= 64 rows, two blocks above), and cut into
+ * sequence (none for s_q*h_q <= 64 rows, four blocks above), and cut into
  * num_parts contiguous, equally sized ranges of the flattened (sequence,
  * block) order; a sequence crossing a range edge is split.
  * num_splits is the exclusive prefix sum of the number of parts touching

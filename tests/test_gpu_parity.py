@@ -165,6 +165,8 @@ PAGED_CASES = [
     (2, 2, 64, [0, 0], True, None),
     (1, 6, 16, [322], True, 8),
     (24, 1, 128, [2012, 2415, 67, 2423, 1406, 1545, 1890, 857, 2938, 161, 833, 1150, 1713, 1225, 393, 135, 3, 146, 446, 2997, 572, 1957, 2250, 703], False, None),
+    # 11 parts of 2 row groups: 8 parts placed XCD by XCD, the other 3 in order after them
+    (2, 2, 128, [1500, 700], True, 11),
 ]
 
 
@@ -283,6 +285,8 @@ V4_CASES = [
     # last block alone (3 parts), and in the combine's second group of splits (8 parts)
     (1, 6, 64, [130], True, True, 3),
     (1, 6, 64, [322], True, True, 8),
+    # 13 parts of 3 row groups: 8 parts placed XCD by XCD, the other 5 in order after them
+    (2, 6, 64, [900, 333], True, True, 13),
 ]
 
 

@@ -40,9 +40,12 @@ def test_status_strings(mla):
 def test_num_parts_and_workspace(mla):
     assert mla.num_parts(16, 1, num_cus=256) == 256
     assert mla.num_parts(128, 2, num_cus=256) % 8 == 0
-    # more than 64 rows: one round of 128-row workgroups (256 rows -> 2 groups, 384 -> 3)
+    # more than 64 rows: one round of 128-row workgroups (256 rows -> 2 groups, 384 -> 3), with
+    # no rounding to a multiple of 8 parts (384 rows: 85 parts, 255 of the 256 compute units)
     assert mla.num_parts(128, 2, num_cus=256) == 128
-    assert mla.num_parts(64, 6, num_cus=256) == 80
+    assert mla.num_parts(64, 6, num_cus=256) == 85
+    # up to 64 rows the part count stays a multiple of 8
+    assert mla.num_parts(32, 2, num_cus=250) % 8 == 0
     assert mla.num_parts(32, 2, num_cus=256) == 512
     assert mla.num_parts(16, 1, num_cus=3) >= 1
     ws = mla.workspace_size(128, 1, 16, 256)
@@ -261,9 +264,9 @@ def test_host_metadata_partition(mla, L, P, h_q):
     _check_partition(L, P, meta, ns)
 
 
-@pytest.mark.parametrize("h_q,overhead", [(16, 0), (64, 0), (128, 2)])
+@pytest.mark.parametrize("h_q,overhead", [(16, 0), (64, 0), (128, 4)])
 def test_host_metadata_balance(mla, h_q, overhead):
-    """Equal shares of blocks plus a fixed cost per sequence: none up to 64 rows, two blocks above."""
+    """Equal shares of blocks plus a fixed cost per sequence: none up to 64 rows, four blocks above."""
     rng = np.random.default_rng(0)
     L = rng.integers(1024, 8193, size=128)
     P = 128
