@@ -222,6 +222,8 @@ FP8_PAGED_CASES = [
     # one part holding more tokens than a sparse split's index list (many-row gathers)
     (1, 2, 64, [5000], True, 1),
     (2, 1, 32, [3000, 2500], False, 2),
+    # 128 rows in two 64-row groups over 11 parts: 8 parts placed XCD by XCD, 3 after them
+    (2, 2, 64, [3000, 1700], True, 11),
 ]
 
 
@@ -392,6 +394,9 @@ SPARSE_CASES = [
     # top-k beyond one split's 2048 entries (at least three splits)
     (1, 2, 128, 6000, 5000, 0.1, 0),
     (2, 1, 16, 9000, 4500, 0.0, 0),
+    # 10 work items (5 query tokens x 2 splits) of two 64-row groups: 8 items placed XCD by XCD,
+    # 2 after them
+    (1, 5, 128, 3000, 1500, 0.1, 2),
 ]
 
 
