@@ -675,6 +675,62 @@ def test_full_size_sparse_prefill(env, prefill_full, quarter):
     _whole(o[toks], l[toks], o_ref[0, toks], l_ref[0, toks], "config 9 quarter %d" % quarter)
 
 
+# ----------------------------------------------------------------- the largest row count, one head
+def _run_kind(env, kind, batch, s_q, h_q, L, causal, seed):
+    """One paged call of the given cache kind against its oracle (poisoned pools, sinks on the
+    512-wide kinds)."""
+    if kind == "bf16":
+        inp = make_paged(batch, s_q, h_q, L, causal, seed=seed, poison=True)
+        o, l = run_paged(env, inp)
+        ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
+    elif kind == "latent512":
+        inp = make_paged(batch, s_q, h_q, L, causal, seed=seed, poison=True, d_qk=512, sinks=True)
+        o, l = run_paged_v4(env, inp)
+        ref = paged_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal,
+                           sinks=inp.sinks)
+    elif kind == "fp8":
+        inp = make_paged_fp8(batch, s_q, h_q, L, causal, seed=seed, poison=True)
+        o, l = run_paged_fp8(env, inp)
+        ref = paged_decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.softmax_scale, causal)
+    else:
+        inp = make_paged_fp4(batch, s_q, h_q, L, causal, seed=seed, poison=True, sinks=True)
+        o, l = run_paged_fp4(env, inp)
+        ref = paged_decode_fp4(inp.q, inp.kv_codes, inp.kv_scales, inp.block_table, inp.seqlens,
+                               inp.softmax_scale, causal, sinks=inp.sinks)
+    return o, l, ref
+
+
+@pytest.mark.parametrize("kind,s_q,h_q", [("bf16", 32, 128), ("latent512", 64, 64), ("fp8", 32, 128),
+                                          ("fp4", 64, 64)])
+def test_maximum_rows(env, kind, s_q, h_q):
+    """s_q * h_q = 4096 query rows per sequence, the largest count the calls accept (32 groups of
+    128 rows on the one-wave-per-SIMD kernel, 64 groups of 64 on the row-split kernel for fp8
+    pages), causal; the second sequence is shorter than s_q, so its first query tokens see no
+    token at all (O = 0, LSE = -inf)."""
+    _say("maximum rows", kind, s_q, h_q)
+    o, l, (o_ref, l_ref) = _run_kind(env, kind, 2, s_q, h_q, [300, 20], True, seed=1200 + s_q + h_q)
+    check_parity(o, l, o_ref, l_ref, "maximum rows %s" % kind)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "latent512", "fp8", "fp4"])
+@pytest.mark.parametrize("s_q", [1, 3])
+def test_single_head(env, kind, s_q):
+    """One query head (h_q = 1): one or three rows in a 16-row tile or a 64-row group, the rest
+    of the tile masked."""
+    _say("single head", kind, s_q)
+    o, l, (o_ref, l_ref) = _run_kind(env, kind, 2, s_q, 1, [200, 70], s_q > 1, seed=1300 + s_q)
+    check_parity(o, l, o_ref, l_ref, "single head %s s_q %d" % (kind, s_q))
+
+
+@pytest.mark.parametrize("splits", [0, 2])
+def test_sparse_single_head(env, splits):
+    _say("sparse single head", splits)
+    inp = make_sparse(2, 3, 1, 500, 200, 0.1, seed=1400 + splits)
+    o, l = run_sparse(env, inp, splits)
+    o_ref, l_ref = sparse_decode(inp.q, inp.kv, inp.indices, inp.softmax_scale)
+    check_parity(o, l, o_ref, l_ref, "sparse single head splits %d" % splits)
+
+
 # ----------------------------------------------------------------- caches beyond 4 GiB
 # The gathers address records with 64-bit offsets.  Each test places the real pages or records
 # of a small input past the first 4 GiB of a zero-filled device pool (so a 32-bit offset would
@@ -834,6 +890,10 @@ FUSED_CASES = [
     (2, 3, 32, [300, 77], True, True, None),
     (2, 1, 64, [3000, 2500], False, False, 8),
     (1, 6, 64, [322], True, True, 8),
+    # the largest row count (4096 per sequence; the first query tokens of the 20-token sequence
+    # see nothing) and a single head
+    (2, 64, 64, [300, 20], True, True, None),
+    (2, 3, 1, [200, 70], True, True, None),
 ]
 
 
