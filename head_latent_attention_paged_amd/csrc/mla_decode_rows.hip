@@ -27,9 +27,9 @@
 // Sparse fp8: a chunk is 32 gathered records ("deepseek-ai/FlashMLA" project summary, section
 // 기술적 세부 사항: fp8 values plus a per-token scale, -1 = unused index).  The workgroup loads
 // each record once into registers (64-bit record addresses; an unused entry reads record 0 and
-// converts to zeros), converts the e4m3 codes exactly to bf16 and stores them in the same LDS layout as a paged
-// chunk, so the Q.K^T / P.V core is the paged one; the token scale multiplies the score and the
-// probability before P.V.
+// converts to zeros), converts the e4m3 codes exactly to bf16 and stores them in the same LDS
+// layout as a paged chunk, so the Q.K^T / P.V core is the paged one; the token scale multiplies
+// the score and the probability before P.V.
 //
 // FP4 pages (DeepSeek-V4 geometry, "[flashinfer] FlashInfer, NVFP4를 활용한 DeepSeek-V4 디코딩
 // 성능 최적화", README tensor table): a token's 512-wide latent row is 256 bytes of E2M1 codes
