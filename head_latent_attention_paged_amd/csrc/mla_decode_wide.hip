@@ -353,12 +353,15 @@ void mla_decode_wide_kernel(const AttnArgs a) {
         // the token entry is 1, or NaN for an unused one
         auto convert_fp4 = [&](int c, int i, int w) {
             const int ln = lane_now();
-            const int cbase = (ln >> 4) * kRowA16 + (ln & 15) * 64;
+            // (a 24-bit multiply: full rate, where a 32-bit one issues at a quarter)
+            const int cbase = (int)__umul24((unsigned)(ln >> 4), (unsigned)kRowA16) + (ln & 15) * 64;
             char* slot = ring + (c % DEPTH) * C::BUF + (8 * wave + 4 * i) * kRowA16 + ((w ^ ((2 * wave + i) & 3)) << 4);
-            // an unused token converts to zeros (row 0's bytes, which it read, are not its own)
+            // an unused token converts to zeros (row 0's bytes, which it read, are not its own);
+            // the scale is converted in every lane and then masked, without a branch
             const bool none = (g_bad >> i) & 1;
             const unsigned codes = none ? 0u : gv[i][w];
-            const float sc = none ? 0.f : __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc[i] >> (8 * (w >> 1))), 0);
+            const float sc_all = __builtin_amdgcn_cvt_f32_fp8((int)((unsigned)g_sc[i] >> (8 * (w >> 1))), 0);
+            const float sc = __uint_as_float(__float_as_uint(sc_all) & (none ? 0u : ~0u));
             unsigned o[4];
 #define MLA_FP4_PAIR(B_)                                                              \
     {                                                                                 \
